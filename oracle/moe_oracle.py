@@ -1,0 +1,288 @@
+"""Float64 CPU oracle for the sparse MoE expert layer with W4 g128 experts.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the test-suite, the smoke check
+and the CPU-baseline leg of the benchmark may import this module.  It shares
+no code with the HIP library: it is a plain, slow, obviously correct
+restatement of what the layer computes, in float64, so that every GPU result
+can be compared element by element against it.
+
+Sources (web pages; cited by site, page section and the object on it):
+
+  [P1] xdnf.cn/news/329730 "千亿MoE模型在RTX 3090上突破100 tok/s：全链路推理优化实战"
+  [P2] lpnh.cn/news/2730718 (125B MoE on one RTX 3090, full-path tuning)
+  [P3] zwxr.cn/news/276292 (Strata engine on RTX 3090 + Xeon E5-2699 v4)
+  [P5] haowenji.com/articles/x-2109226022155796480
+       "把 96.5GB 的 GLM-5.3-Flash 塞进单张 4090 48GB ..."
+
+Each function names the passage it follows.  Readings taken where the pages
+are silent or garbled are stated in the docstrings; the same list, with the
+reasons, is kept in the design notes at the repository root.
+
+Packed int4 storage (a format of this library, not of the pages, which keep
+int8 codes): row-major [out, in/2] bytes; byte j of a row holds column 2j in
+bits 0-3 and column 2j+1 in bits 4-7, each stored as the unsigned nibble
+u = q + 8 (offset binary, 0..15).  Scales are fp16, row-major [out, in/128].
+"""
+from __future__ import annotations
+
+import numpy as np
+
+GROUP = 128          # [P2] §2.1: 128 weights per group along in_features
+QMAX = 7             # [P2] §2.1: 2**(bits-1) - 1 with bits = 4
+QMIN, QHI = -8, 7    # [P2] §2.1: clamp range of the rounded codes
+
+
+# ---------------------------------------------------------------------------
+# fp16 rounding
+# ---------------------------------------------------------------------------
+def rn16(a) -> np.ndarray:
+    """Round float64 values to the nearest fp16 (ties to even), back as float64.
+
+    numpy converts float64 to float16 directly with round-to-nearest-even;
+    the tests pin this against a brute-force nearest-neighbour search over
+    every finite fp16 value.
+    """
+    return np.asarray(a, dtype=np.float64).astype(np.float16).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# a0: symmetric group quantization  ([P2] §2.1 group-quantization pseudo-code;
+#     applied offline to every module whose name contains "expert", [P2] §3.2)
+# ---------------------------------------------------------------------------
+def group_quantize(w16: np.ndarray, group: int = GROUP):
+    """Quantize an fp16 weight [out, in] to int4 codes and fp16 group scales.
+
+    [P2] §2.1: the weight is viewed as [out, in/group, group]; each group's
+    scale is its largest magnitude divided by 2**(bits-1)-1 = 7; the codes are
+    round(w / scale) clamped to [-8, 7].  The page runs this on a model loaded
+    in fp16 ([P2] §3.2), so every operation rounds to fp16:
+
+        s = RN16(max|w| / 7),   q = clamp(RNE(RN16(w / s)), -8, 7).
+
+    Each quotient is formed in float64 and then rounded once to fp16; since
+    53 >= 2*11 + 2 this equals the correctly rounded fp16 quotient.  A group
+    of zeros (0/0 on the page) gets s = 0 and q = 0 (reading: the page is
+    silent).  in_features must be a multiple of the group size (reading: the
+    page's reshape would drop a tail silently; here it is refused).
+
+    Returns (q int8 [out, in], s float16 [out, in/group]).
+    """
+    w16 = np.asarray(w16)
+    if w16.dtype != np.float16:
+        raise TypeError("group_quantize expects fp16 weights")
+    out_dim, in_dim = w16.shape
+    if in_dim % group:
+        raise ValueError("in_features must be a multiple of the group size")
+    w = w16.astype(np.float64).reshape(out_dim, in_dim // group, group)
+    m = np.abs(w).max(axis=-1, keepdims=True)
+    s = rn16(m / QMAX)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = rn16(np.where(s > 0, w / np.where(s > 0, s, 1.0), 0.0))
+    q = np.clip(np.rint(r), QMIN, QHI)          # np.rint rounds half to even
+    q = np.where(s > 0, q, 0.0)
+    return (q.astype(np.int8).reshape(out_dim, in_dim),
+            s.reshape(out_dim, in_dim // group).astype(np.float16))
+
+
+def pack_w4(q: np.ndarray) -> np.ndarray:
+    """int8 codes [out, in] in [-8, 7] -> packed bytes [out, in/2] (offset binary)."""
+    q = np.asarray(q)
+    if q.min(initial=0) < QMIN or q.max(initial=0) > QHI:
+        raise ValueError("codes outside [-8, 7]")
+    u = (q.astype(np.int16) + 8).astype(np.uint8)
+    return (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_w4(packed: np.ndarray) -> np.ndarray:
+    """Packed bytes [out, in/2] -> int8 codes [out, in]."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty((p.shape[0], p.shape[1] * 2), dtype=np.int8)
+    out[:, 0::2] = (p & 0x0F).astype(np.int8) - 8
+    out[:, 1::2] = (p >> 4).astype(np.int8) - 8
+    return out
+
+
+def dequant(packed: np.ndarray, s: np.ndarray, group: int = GROUP) -> np.ndarray:
+    """W[n, c] = q[n, c] * s[n, c // group], in float64 (exact: an int4 code
+    times an fp16 scale needs at most 4 + 11 significant bits)."""
+    q = unpack_w4(packed).astype(np.float64)
+    s64 = np.asarray(s, dtype=np.float64)
+    return q * np.repeat(s64, group, axis=1)
+
+
+# ---------------------------------------------------------------------------
+# a1 + a2: router logits, softmax, top-k
+#   [P2] §2.3 (softmax and top-k fused in one kernel), [P3] §3.2 (softmax over
+#   the expert logits, then a descending partial sort for the first k).
+# ---------------------------------------------------------------------------
+def router_logits(x16, wr16, bias=None) -> np.ndarray:
+    """l[t, e] = sum_h x[t, h] * Wr[e, h] + b[e]   (float64)."""
+    l = np.asarray(x16, dtype=np.float64) @ np.asarray(wr16, dtype=np.float64).T
+    if bias is not None:
+        l = l + np.asarray(bias, dtype=np.float64)[None, :]
+    return l
+
+
+def softmax(l: np.ndarray) -> np.ndarray:
+    """Row softmax with the row maximum subtracted first."""
+    z = l - l.max(axis=-1, keepdims=True)
+    e = np.exp(z)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def topk_order(l: np.ndarray, k: int) -> np.ndarray:
+    """First k experts of each row ordered by (-logit, expert index).
+
+    Reading: ties go to the lower expert index, both in selection and in the
+    output order (the page's partial sort is unstable and leaves ties open).
+    Top-k of the probabilities equals top-k of the logits: softmax is monotone.
+    """
+    T, E = l.shape
+    eidx = np.broadcast_to(np.arange(E), (T, E))
+    order = np.lexsort((eidx, -l), axis=-1)   # last key primary: -logit, then index
+    return order[:, :k].astype(np.int32)
+
+
+def route(x16, wr16, bias, k: int):
+    """Returns (topk_idx int32 [T,k], topk_w float64 [T,k], logits float64 [T,E]).
+
+    The combine weights are the softmax probabilities of the chosen experts,
+    not renormalised over the k chosen (reading taken for every workload).
+    """
+    l = router_logits(x16, wr16, bias)
+    p = softmax(l)
+    idx = topk_order(l, k)
+    w = np.take_along_axis(p, idx.astype(np.int64), axis=1)
+    return idx, w, l
+
+
+# ---------------------------------------------------------------------------
+# a3 + a4: token permutation by expert  ([P1] §3.2 and [P2] §2.3: tokens that
+#   chose the same expert are gathered so that each expert runs one GEMM)
+# ---------------------------------------------------------------------------
+def permute(topk_idx: np.ndarray, num_experts: int):
+    """Histogram, exclusive scan and stable scatter of the flat (token, slot) pairs.
+
+    Flat index f = t*k + j.  Segment e holds the f with idx_flat[f] = e in
+    increasing f (stable; reading taken so the permutation is unique).
+    Returns (offsets int32 [E+1], perm_src int32 [T*k], inv_pos int32 [T*k]):
+    perm_src[r] = f of the r-th permuted row, inv_pos[f] = r.
+    """
+    flat = np.asarray(topk_idx, dtype=np.int64).reshape(-1)
+    cnt = np.bincount(flat, minlength=num_experts)
+    off = np.concatenate([[0], np.cumsum(cnt)]).astype(np.int32)
+    perm_src = np.argsort(flat, kind="stable").astype(np.int32)
+    inv_pos = np.empty_like(perm_src)
+    inv_pos[perm_src] = np.arange(flat.size, dtype=np.int32)
+    return off, perm_src, inv_pos
+
+
+def gather_rows(x16: np.ndarray, perm_src: np.ndarray, k: int) -> np.ndarray:
+    """x_perm[r] = x[perm_src[r] // k] (a bitwise copy of fp16 rows)."""
+    return np.asarray(x16)[np.asarray(perm_src, dtype=np.int64) // k]
+
+
+# ---------------------------------------------------------------------------
+# a5 + a6 + a7: SwiGLU expert FFN  ([P3] §4.3 and [P5] §01: each expert holds
+#   gate / up / down matrices, Mixtral-style w1 / w3 / w2)
+# ---------------------------------------------------------------------------
+def silu(z: np.ndarray) -> np.ndarray:
+    """silu(z) = z / (1 + exp(-z))."""
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def swiglu_ffn(X: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray) -> np.ndarray:
+    """Y = (silu(X Wg^T) * (X Wu^T)) Wd^T, all float64.
+
+    Wg, Wu are [F, H] (in_features = H), Wd is [H, F] (in_features = F).
+    """
+    X = np.asarray(X, dtype=np.float64)
+    g = X @ np.asarray(Wg, dtype=np.float64).T
+    u = X @ np.asarray(Wu, dtype=np.float64).T
+    h = silu(g) * u
+    return h @ np.asarray(Wd, dtype=np.float64).T
+
+
+def expert_ffn_w4(X, gate_q, gate_s, up_q, up_s, down_q, down_s) -> np.ndarray:
+    """One routed expert: dequantize its three int4 matrices, then SwiGLU."""
+    return swiglu_ffn(X, dequant(gate_q, gate_s), dequant(up_q, up_s),
+                      dequant(down_q, down_s))
+
+
+# ---------------------------------------------------------------------------
+# a8: weighted combine + shared expert, and the RMS normalisation that links
+#   stacked layers
+# ---------------------------------------------------------------------------
+def combine(y_perm, ys, inv_pos, topk_w, T: int, k: int) -> np.ndarray:
+    """out[t] = ys[t] + sum_j w[t, j] * y_perm[inv_pos[t*k + j]]  (float64).
+
+    The shared expert enters with weight 1 and no gate ([P5] §01 "8 routed +
+    1 shared"; reading: the shared expert is always on, unweighted).
+    """
+    y_perm = np.asarray(y_perm, dtype=np.float64)
+    H = y_perm.shape[1] if y_perm.ndim == 2 and y_perm.shape[0] else (
+        np.asarray(ys).shape[1] if ys is not None else 0)
+    out = np.zeros((T, H)) if ys is None else np.asarray(ys, dtype=np.float64).copy()
+    w = np.asarray(topk_w, dtype=np.float64).reshape(T, k)
+    inv = np.asarray(inv_pos, dtype=np.int64).reshape(T, k)
+    for j in range(k):
+        out += w[:, j:j + 1] * y_perm[inv[:, j]]
+    return out
+
+
+def rmsnorm(y: np.ndarray, eps: float = 1e-6) -> np.ndarray:
+    """y / sqrt(mean(y^2) + eps) per row; no learned gain, no residual.
+
+    Reading: the stacked decode workload only says that a layer's output feeds
+    the next layer after RMS normalisation.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    return y / np.sqrt(np.mean(y * y, axis=-1, keepdims=True) + eps)
+
+
+# ---------------------------------------------------------------------------
+# whole layer
+# ---------------------------------------------------------------------------
+def moe_layer(x16, router_w16, router_b, experts, k: int, shared=None):
+    """One MoE layer forward in float64, keeping every intermediate.
+
+    experts: indexable by expert id, returning
+             (gate_q, gate_s, up_q, up_s, down_q, down_s) for that expert
+             (packed int4 bytes and fp16 scales).  Only the experts that
+             receive tokens are fetched, so a lazy provider may regenerate
+             them on demand.
+    shared:  None or (Wg16 [Fs,H], Wu16 [Fs,H], Wd16 [H,Fs]) fp16.
+    """
+    x16 = np.asarray(x16)
+    T = x16.shape[0]
+    E = np.asarray(router_w16).shape[0]
+    idx, w, logits = route(x16, router_w16, router_b, k)
+    off, perm_src, inv_pos = permute(idx, E)
+    x_perm = gather_rows(x16, perm_src, k)
+    H = x16.shape[1]
+    y_perm = np.zeros((T * k, H))
+    for e in range(E):
+        a, b = int(off[e]), int(off[e + 1])
+        if b > a:
+            y_perm[a:b] = expert_ffn_w4(x_perm[a:b], *experts[e])
+    ys = swiglu_ffn(x16, *shared) if shared is not None else None
+    out = combine(y_perm, ys, inv_pos, w, T, k)
+    return dict(idx=idx, w=w, logits=logits, offsets=off, perm_src=perm_src,
+                inv_pos=inv_pos, x_perm=x_perm, y_perm=y_perm, ys=ys, out=out)
+
+
+def near_ties(logits: np.ndarray, k: int, gap: float = 1e-6):
+    """Tokens whose ordered top-k list is not separated by more than `gap`.
+
+    Returns a boolean [T] mask: True when, among the first k+1 logits in
+    (-logit, index) order, two neighbours differ by <= gap.  A GPU/oracle
+    disagreement in the top-k order of such a token is reported, not failed.
+    """
+    T, E = logits.shape
+    kk = min(k + 1, E)
+    order = topk_order(logits, kk).astype(np.int64)
+    v = np.take_along_axis(logits, order, axis=1)
+    if kk < 2:
+        return np.zeros(T, dtype=bool)
+    return (np.abs(np.diff(v, axis=1)) <= gap).any(axis=1)

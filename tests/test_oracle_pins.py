@@ -1,0 +1,325 @@
+"""Pins of the float64 oracle against facts fixed outside it.
+
+Each test checks the oracle against something it does not compute itself:
+values derived by hand (tests/golden), exact rational arithmetic, brute force
+on tiny inputs, closed forms and invariants.  None of these needs a GPU.
+"""
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+from workloads import get_config
+from workloads import gen as G
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+# every finite fp16 value, ascending, as exact Fractions (for brute force)
+_F16_BITS = np.arange(0, 0x7C00, dtype=np.uint16)                 # +0 .. max finite
+_F16_POS = _F16_BITS.view(np.float16).astype(np.float64)
+
+
+def nearest_f16(v: Fraction) -> Fraction:
+    """Round a rational to fp16 by searching all finite fp16 values
+    (ties to the value with an even bit pattern)."""
+    sign = -1 if v < 0 else 1
+    a = abs(v)
+    i = int(np.searchsorted(_F16_POS, float(a)))
+    cands = set()
+    for j in (i - 2, i - 1, i, i + 1):
+        if 0 <= j < _F16_POS.size:
+            cands.add(j)
+    best = min(cands, key=lambda j: (abs(Fraction(_F16_POS[j]) - a), int(_F16_BITS[j]) & 1))
+    return sign * Fraction(_F16_POS[best])
+
+
+# ---------------------------------------------------------------- fp16 rounding
+def test_rn16_matches_bruteforce_nearest():
+    g = np.random.default_rng(1)
+    vals = np.concatenate([
+        g.standard_normal(300) * 0.02, g.standard_normal(300) * 7,
+        # exact midpoints between neighbouring fp16 values (tie cases)
+        (_F16_POS[1000:1100] + _F16_POS[1001:1101]) / 2,
+        (_F16_POS[20000:20100] + _F16_POS[20001:20101]) / 2,
+    ])
+    got = O.rn16(vals)
+    for v, r in zip(vals, got):
+        assert Fraction(r) == nearest_f16(Fraction(v)), v
+
+
+# ---------------------------------------------------------------- quantizer
+def test_quantizer_golden_example():
+    fx = json.load(open(os.path.join(GOLDEN, "quantize_example.json")))
+    w = np.zeros(fx["shape"], dtype=np.float16)
+    for c, v in fx["weights_nonzero"].items():
+        w[0, int(c)] = v
+        assert float(np.float16(v)) == v          # fixture values are exact fp16
+    q, s = O.group_quantize(w, fx["group_size"])
+    assert s.dtype == np.float16 and q.dtype == np.int8
+    assert [float(x) for x in s[0]] == fx["expected_scales"]
+    exp = np.zeros(fx["shape"], dtype=np.int8)
+    for c, v in fx["expected_codes_nonzero"].items():
+        exp[0, int(c)] = v
+    np.testing.assert_array_equal(q, exp)
+
+
+def test_quantizer_exact_rational_bruteforce():
+    """Recompute s and q for random fp16 weights with exact rational
+    arithmetic and a brute-force fp16 rounding, independent of float64."""
+    g = np.random.default_rng(2)
+    w = (g.standard_normal((3, 256)) * 0.02).astype(np.float16)
+    q, s = O.group_quantize(w)
+    for n in range(w.shape[0]):
+        for grp in range(2):
+            ws = [Fraction(float(v)) for v in w[n, grp * 128:(grp + 1) * 128]]
+            m = max(abs(v) for v in ws)
+            s_ref = nearest_f16(m / 7)
+            assert Fraction(float(s[n, grp])) == s_ref
+            for c, v in enumerate(ws):
+                r = nearest_f16(v / s_ref)
+                q_ref = max(-8, min(7, round(r)))          # round(): half to even
+                assert int(q[n, grp * 128 + c]) == q_ref
+
+
+def test_quantizer_invariants():
+    cfg = get_config("tiny")
+    w = G.expert_master(cfg, 0, 3, G.GATE).astype(np.float16)       # [512, 256]
+    w[5, 128:256] = 0                                               # an all-zero group
+    q, s = O.group_quantize(w)
+    assert q.min() >= -7 and q.max() <= 7                           # -8 never produced
+    qa = np.abs(q.astype(np.int32)).reshape(q.shape[0], -1, 128).max(-1)
+    nz = s.astype(np.float64) > 0
+    assert (qa[nz] == 7).all()
+    assert (qa[~nz] == 0).all() and not nz[5, 1]
+    err = np.abs(w.astype(np.float64) - O.dequant(O.pack_w4(q), s))
+    bound = (0.5 + 2.0 ** -9) * np.repeat(s.astype(np.float64), 128, axis=1)
+    assert (err <= bound).all()
+
+
+def test_quantizer_refuses_ragged_in_features():
+    with pytest.raises(ValueError):
+        O.group_quantize(np.zeros((2, 200), dtype=np.float16))
+
+
+# ---------------------------------------------------------------- packing / dequant
+def test_pack_layout_exhaustive():
+    """All 256 byte values: low nibble = even column, value = nibble - 8."""
+    packed = np.arange(256, dtype=np.uint8).reshape(1, 256)
+    q = O.unpack_w4(packed)
+    for b in range(256):
+        assert q[0, 2 * b] == (b & 15) - 8
+        assert q[0, 2 * b + 1] == (b >> 4) - 8
+    np.testing.assert_array_equal(O.pack_w4(q), packed)
+
+
+def test_dequant_exact():
+    g = np.random.default_rng(3)
+    q = g.integers(-8, 8, size=(4, 256)).astype(np.int8)
+    s = (g.uniform(1e-3, 1e-2, size=(4, 2))).astype(np.float16)
+    W = O.dequant(O.pack_w4(q), s)
+    for n in range(4):
+        for c in range(0, 256, 7):
+            assert Fraction(W[n, c]) == int(q[n, c]) * Fraction(float(s[n, c // 128]))
+    # q*s is exact in fp32 as well (4 + 11 significant bits)
+    np.testing.assert_array_equal(W.astype(np.float32).astype(np.float64), W)
+
+
+# ---------------------------------------------------------------- router
+def test_softmax_closed_form():
+    E = 6
+    l = np.log(np.arange(1, E + 1, dtype=np.float64))[None, :] + 3.0
+    p = O.softmax(l)
+    np.testing.assert_allclose(p[0], np.arange(1, E + 1) / (E * (E + 1) / 2), rtol=1e-15)
+
+
+def test_router_logits_bruteforce():
+    g = np.random.default_rng(4)
+    x = g.standard_normal((3, 5)).astype(np.float16)
+    wr = (g.standard_normal((4, 5)) * 0.1).astype(np.float16)
+    b = g.standard_normal(4).astype(np.float32)
+    l = O.router_logits(x, wr, b)
+    for t in range(3):
+        for e in range(4):
+            ref = math.fsum(float(x[t, h]) * float(wr[e, h]) for h in range(5)) + float(b[e])
+            assert abs(l[t, e] - ref) <= 1e-15 * (1 + abs(ref))
+
+
+def test_topk_bruteforce_all_subsets():
+    g = np.random.default_rng(5)
+    E, k = 7, 3
+    for _ in range(40):
+        l = np.round(g.standard_normal((1, E)) * 2) / 2          # many exact ties
+        idx = O.topk_order(l, k)[0].tolist()
+        # brute force: the best subset under (-logit, index) lexicographic order
+        best = min(itertools.permutations(range(E), k),
+                   key=lambda c: [(-l[0, e], e) for e in c])
+        assert idx == list(best)
+
+
+def test_route_duplicate_rows_tie_lower_index_wins():
+    cfg = get_config("tiny")
+    x = G.activations(cfg)
+    wr, _ = G.router(cfg)
+    wr = wr.copy()
+    wr[6] = wr[1]                                 # experts 1 and 6 tie exactly
+    wr[1] = wr[1] * np.float16(4)                 # and make them win most tokens
+    wr[6] = wr[1]
+    idx, w, l = O.route(x, wr, None, 2)
+    assert (l[:, 1] == l[:, 6]).all()
+    for t in range(x.shape[0]):
+        row = idx[t].tolist()
+        if 6 in row:
+            assert 1 in row and row.index(1) < row.index(6)
+    np.testing.assert_allclose(O.softmax(l).sum(1), 1.0, rtol=1e-14)
+
+
+def test_near_ties_flags_only_close_pairs():
+    l = np.array([[3.0, 1.0, 1.0 + 5e-7, -2.0], [3.0, 2.0, 1.0, 0.0]])
+    m = O.near_ties(l, 2)
+    assert m.tolist() == [True, False]
+
+
+# ---------------------------------------------------------------- permutation
+def test_permute_bruteforce_definition():
+    g = np.random.default_rng(6)
+    T, k, E = 13, 3, 9
+    idx = np.stack([g.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    idx[4] = [2, 0, 8]
+    off, perm_src, inv_pos = O.permute(idx, E)
+    flat = idx.reshape(-1).tolist()
+    cnt = [flat.count(e) for e in range(E)]
+    assert off.tolist() == [sum(cnt[:e]) for e in range(E + 1)]
+    for f, e in enumerate(flat):
+        r = off[e] + sum(1 for f2 in range(f) if flat[f2] == e)
+        assert inv_pos[f] == r and perm_src[r] == f
+    x = g.standard_normal((T, 16)).astype(np.float16)
+    xp = O.gather_rows(x, perm_src, k)
+    for f in range(T * k):
+        assert xp[inv_pos[f]].tobytes() == x[f // k].tobytes()
+
+
+def test_permute_all_to_one_expert_and_k_equals_E():
+    idx = np.zeros((5, 1), dtype=np.int32) + 3
+    off, perm_src, inv_pos = O.permute(idx, 6)
+    assert off.tolist() == [0, 0, 0, 0, 5, 5, 5]
+    assert perm_src.tolist() == [0, 1, 2, 3, 4]
+    idx = np.array([[2, 0, 1], [1, 2, 0]], dtype=np.int32)
+    off, perm_src, _ = O.permute(idx, 3)
+    assert off.tolist() == [0, 2, 4, 6]
+    assert perm_src.tolist() == [1, 5, 2, 3, 0, 4]
+
+
+# ---------------------------------------------------------------- FFN / layer
+def test_silu_closed_forms():
+    z = np.array([0.0, math.log(3.0), -math.log(3.0), 40.0, -800.0])
+    s = O.silu(z)
+    assert s[0] == 0.0
+    assert abs(s[1] - 0.75 * math.log(3.0)) < 1e-15
+    assert abs(s[2] + 0.25 * math.log(3.0)) < 1e-15
+    assert abs(s[3] - 40.0) < 1e-12
+    assert s[4] == 0.0
+
+
+def test_swiglu_small_loops():
+    """Pure-Python loops over tiny matrices: catches a transposed operand."""
+    g = np.random.default_rng(7)
+    X = g.standard_normal((2, 3))
+    Wg = g.standard_normal((4, 3))
+    Wu = g.standard_normal((4, 3))
+    Wd = g.standard_normal((3, 4))
+    Y = O.swiglu_ffn(X, Wg, Wu, Wd)
+    for t in range(2):
+        h = []
+        for f in range(4):
+            gg = sum(X[t, c] * Wg[f, c] for c in range(3))
+            uu = sum(X[t, c] * Wu[f, c] for c in range(3))
+            h.append(gg / (1 + math.exp(-gg)) * uu)
+        for o in range(3):
+            ref = sum(h[f] * Wd[o, f] for f in range(4))
+            assert abs(Y[t, o] - ref) < 1e-12
+
+
+def _tiny_layer(cfg, layer=0):
+    x = G.activations(cfg, layer=layer)
+    wr, b = G.router(cfg, layer)
+    experts = []
+    for e in range(cfg.num_experts):
+        mats = []
+        for m in (G.GATE, G.UP, G.DOWN):
+            q, s = O.group_quantize(G.expert_master(cfg, layer, e, m))
+            mats += [O.pack_w4(q), s]
+        experts.append(tuple(mats))
+    return x, wr, b, experts
+
+
+def test_layer_equals_dense_all_experts_then_mask():
+    cfg = get_config("tiny")
+    x, wr, b, experts = _tiny_layer(cfg)
+    res = O.moe_layer(x, wr, b, experts, cfg.top_k)
+    p = O.softmax(O.router_logits(x, wr, b))
+    dense = np.zeros((cfg.tokens, cfg.hidden))
+    for e in range(cfg.num_experts):
+        Ye = O.expert_ffn_w4(x, *experts[e])                     # every token, every expert
+        mask = (res["idx"] == e).any(axis=1)
+        dense += (p[:, e] * mask)[:, None] * Ye
+    np.testing.assert_allclose(res["out"], dense, rtol=0, atol=1e-12 * np.abs(dense).max())
+
+
+def test_layer_special_cases():
+    cfg = get_config("tiny", num_experts=1, top_k=1)
+    x, wr, b, experts = _tiny_layer(cfg)
+    res = O.moe_layer(x, wr, b, experts, 1)
+    np.testing.assert_allclose(res["w"], 1.0, rtol=1e-15)      # softmax of one logit
+    np.testing.assert_allclose(res["out"], O.expert_ffn_w4(x, *experts[0]), rtol=1e-13, atol=0)
+
+    # k = E: a dense softmax mixture of all experts
+    cfg = get_config("tiny", num_experts=3, top_k=3)
+    x, wr, b, experts = _tiny_layer(cfg)
+    res = O.moe_layer(x, wr, b, experts, 3)
+    p = O.softmax(O.router_logits(x, wr, b))
+    mix = sum(p[:, e:e + 1] * O.expert_ffn_w4(x, *experts[e]) for e in range(3))
+    np.testing.assert_allclose(res["out"], mix, rtol=0, atol=1e-12 * np.abs(mix).max())
+
+    # x = 0: silu(0) = 0, so every expert and the shared expert give 0
+    cfg = get_config("tiny")
+    _, wr, b, experts = _tiny_layer(cfg)
+    z = np.zeros((4, cfg.hidden), dtype=np.float16)
+    sh = tuple(G.normal16(np.random.default_rng(8), s, 0.02)
+               for s in ((64, cfg.hidden), (64, cfg.hidden), (cfg.hidden, 64)))
+    res = O.moe_layer(z, wr, b, experts, cfg.top_k, shared=sh)
+    assert not res["out"].any()
+
+    # identical experts: out = ys + (sum_j w_j) * FFN(x)
+    x, wr, b, experts = _tiny_layer(cfg)
+    same = [experts[0]] * cfg.num_experts
+    res = O.moe_layer(x, wr, b, same, cfg.top_k, shared=sh)
+    ref = O.swiglu_ffn(x, *sh) + res["w"].sum(1, keepdims=True) * O.expert_ffn_w4(x, *experts[0])
+    np.testing.assert_allclose(res["out"], ref, rtol=0, atol=1e-12 * np.abs(ref).max())
+
+
+def test_combine_bruteforce():
+    g = np.random.default_rng(9)
+    T, k, H = 4, 2, 5
+    y_perm = g.standard_normal((T * k, H))
+    ys = g.standard_normal((T, H))
+    inv = g.permutation(T * k).astype(np.int32)
+    w = g.uniform(size=(T, k))
+    out = O.combine(y_perm, ys, inv, w, T, k)
+    for t in range(T):
+        for h in range(H):
+            ref = ys[t, h] + sum(w[t, j] * y_perm[inv[t * k + j], h] for j in range(k))
+            assert abs(out[t, h] - ref) < 1e-14
+
+
+def test_rmsnorm_identity():
+    g = np.random.default_rng(10)
+    y = g.standard_normal((5, 64)) * np.array([[1e-4], [1e-2], [1], [10], [0.0]])
+    eps = 1e-6
+    r = O.rmsnorm(y, eps)
+    ms = np.mean(y * y, axis=1)
+    np.testing.assert_allclose(np.mean(r * r, axis=1), ms / (ms + eps), rtol=1e-12, atol=0)
