@@ -1,0 +1,289 @@
+"""Benchmark of the W4 g128 sparse-MoE layer on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload decode_fine]
+
+A step is one full layer forward (route -> permute -> grouped W4 FFN ->
+combine) over one batch of synthetic tokens already resident in HBM.  Several
+independently drawn weight sets are rotated so that no expert byte is served
+from the 256 MB Infinity Cache across steps.  Prints ONE JSON line.
+
+`roofline` is for the dominant stage, the grouped FFN (its two launches,
+gate/up then down): algorithmic bytes = distinct experts with tokens in the
+step x bytes per expert (packed int4 + fp16 scales) + the fp16 shared expert,
+divided by the stage's average duration measured with HIP events on the
+launch stream inside the timed region.
+
+`cpu_baseline` times the float64 oracle (test infrastructure, run only in
+this leg) on a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from workloads import get_config  # noqa: E402
+from workloads import gen as G  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 matrix peak
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="decode_fine",
+                    choices=["decode_fine", "decode_coarse", "prefill", "decode_stack", "tiny"])
+    ap.add_argument("--weight-sets", type=int, default=0, help="0 = workload default")
+    ap.add_argument("--batches", type=int, default=4, help="distinct token batches rotated")
+    ap.add_argument("--graph", action="store_true", help="replay the steps from a HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------- device weights
+def gpu_normal16(shape, std, seed, dev):
+    import torch
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    return (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * std).to(
+        torch.float16)
+
+
+def build_layer(cfg, wset, layer_idx, dev):
+    """fp16 masters N(0, weight_std) drawn on the device, quantized by the HIP
+    quantizer; router and bias from the numpy generators; fp16 shared expert."""
+    import torch
+    from w4_group_quantized_amd import W4MoELayer, _native as NAT
+    E, H, F = cfg.num_experts, cfg.hidden, cfg.ffn
+    mats = {}
+    for m, name in ((G.GATE, "gate"), (G.UP, "up"), (G.DOWN, "down")):
+        out_dim, in_dim = G.matrix_shape(cfg, m)
+        q = torch.empty((E, out_dim, in_dim // 2), dtype=torch.uint8, device=dev)
+        s = torch.empty((E, out_dim, in_dim // 128), dtype=torch.float16, device=dev)
+        # a few experts per draw keeps the fp32 temporaries small
+        per = max(1, min(E, (1 << 28) // (out_dim * in_dim)))
+        for e0 in range(0, E, per):
+            e1 = min(E, e0 + per)
+            seed = G.torch_seed(cfg, G.T_EXPERT, layer=layer_idx, expert=e0, matrix=m, batch=wset)
+            w = gpu_normal16(((e1 - e0) * out_dim, in_dim), cfg.weight_std, seed, dev)
+            NAT.moe_w4_quantize(w, (e1 - e0) * out_dim, in_dim, q[e0:e1], s[e0:e1])
+            del w
+        mats[name] = (q, s)
+    wr, b = G.router(cfg, layer_idx + 1000 * wset)
+    shared = None
+    if cfg.shared_ffn:
+        Fs = cfg.shared_ffn
+        shared = tuple(
+            gpu_normal16(shp, cfg.shared_std,
+                         G.torch_seed(cfg, G.T_SHARED, layer=layer_idx, matrix=m, batch=wset), dev)
+            for m, shp in ((G.GATE, (Fs, H)), (G.UP, (Fs, H)), (G.DOWN, (H, Fs))))
+    t = lambda a: torch.from_numpy(a).to(dev)  # noqa: E731
+    return W4MoELayer(cfg.top_k, t(wr), t(b) if b is not None else None,
+                      mats["gate"][0], mats["gate"][1], mats["up"][0], mats["up"][1],
+                      mats["down"][0], mats["down"][1], shared=shared)
+
+
+# ---------------------------------------------------------------- CPU baseline
+def cpu_baseline(cfg, budget_s):
+    """The float64 oracle on a bounded sample of the workload, on host cores.
+
+    The sample is one layer forward of `cfg` at its full shape (all layers'
+    shapes are equal in the stacked workload, so one layer stands for one of
+    its 42).  Expert weights are drawn directly as packed codes (the forward's
+    cost does not depend on their values) and only for the experts the oracle's
+    own routing selects; drawing them is not timed.  Repeats the forward until
+    `budget_s` is spent (at least once)."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    wr, b = G.router(cfg, 0)
+    x = G.activations(cfg, batch=0)
+    shared = G.shared_expert(cfg, 0)
+    idx, _, _ = O.route(x, wr, b, cfg.top_k)
+    cache = {}
+
+    class Lazy:
+        def __getitem__(self, e):
+            if e not in cache:
+                tup = []
+                for m in (G.GATE, G.UP, G.DOWN):
+                    tup += list(G.expert_codes(cfg, 0, int(e), m))
+                cache[e] = tuple(tup)
+            return cache[e]
+
+    lazy = Lazy()
+    for e in np.unique(idx):
+        lazy[int(e)]
+    runs, t_total = 0, 0.0
+    while runs == 0 or t_total < budget_s:
+        t0 = time.perf_counter()
+        O.moe_layer(x, wr, b, lazy, cfg.top_k, shared=shared)
+        t_total += time.perf_counter() - t0
+        runs += 1
+        if t_total > budget_s * 0.5 and runs >= 1 and t_total / runs > budget_s * 0.5:
+            break
+    per_call = t_total / runs
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {
+        "value": cfg.tokens / per_call, "unit": "tokens/s", "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": (f"{runs} float64 oracle layer forward(s) of {cfg.name} at full shape "
+                   f"(T={cfg.tokens}, {len(np.unique(idx))} distinct experts), "
+                   f"{per_call * 1e3:.1f} ms each; host {cpu_model or platform.processor()}, "
+                   f"{len(os.sched_getaffinity(0))} cpus visible"),
+    }
+
+
+# ---------------------------------------------------------------- main
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import w4_group_quantized_amd  # noqa: F401  (fails loudly without the HIP library)
+
+    cfg = get_config(args.workload)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    layers_per_step = cfg.layers
+    n_sets = args.weight_sets or (1 if layers_per_step > 1 or cfg.name == "decode_coarse" else 4)
+    if cfg.name == "prefill":
+        n_sets = args.weight_sets or 2
+
+    # weights: n_sets independent sets (each `layers_per_step` layers)
+    sets = []
+    for s in range(n_sets):
+        sets.append([build_layer(cfg, s, l, dev) for l in range(layers_per_step)])
+    T = cfg.tokens
+    xs = [torch.from_numpy(G.activations(cfg, batch=bt)).to(dev) for bt in range(args.batches)]
+    bufs = sets[0][0].alloc(T)
+    act = [torch.empty((T, cfg.hidden), dtype=torch.float16, device=dev) for _ in range(2)]
+    torch.cuda.synchronize()
+
+    n_combo = n_sets * args.batches
+
+    def step(i, ev_pair=None):
+        layers = sets[i % n_sets]
+        x = xs[(i // n_sets) % args.batches]
+        for li, layer in enumerate(layers):
+            last = li == len(layers) - 1
+            layer.route(x, bufs, T)
+            layer.permute(x, bufs, T)
+            if ev_pair is not None and li == 0:
+                ev_pair[0].record(stream)
+            layer.ffn(x, bufs, T)
+            if ev_pair is not None and li == 0:
+                ev_pair[1].record(stream)
+            if last:
+                layer.combine(bufs, T, rmsnorm=layers_per_step > 1, eps=cfg.rms_eps)
+            else:
+                nxt = act[li % 2]
+                layer.combine(bufs, T, rmsnorm=True, eps=cfg.rms_eps, out=nxt)
+                x = nxt
+
+    # algorithmic bytes of the FFN stage per (weight set, batch) combination,
+    # counted from the offsets each combination produces (first layer)
+    bytes_per_combo = []
+    u_per_combo = []
+    for c in range(n_combo):
+        layer = sets[c % n_sets][0]
+        x = xs[(c // n_sets) % args.batches]
+        layer.route(x, bufs, T)
+        layer.permute(x, bufs, T)
+        torch.cuda.synchronize()
+        cnt = np.diff(bufs.offsets.cpu().numpy())
+        U = int((cnt > 0).sum())
+        u_per_combo.append(U)
+        bytes_per_combo.append(U * cfg.expert_bytes() + cfg.shared_bytes())
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(K):
+        step(i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / K
+    ffn_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    ffn_bytes = np.array([bytes_per_combo[i % n_combo] for i in range(K)], dtype=np.float64)
+    achieved_gbs = float(ffn_bytes.mean() / (ffn_ms.mean() * 1e-3) / 1e9)
+    tokens_per_s = T * K / (ms_total * 1e-3)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        layer_cfg = cfg if cfg.layers == 1 else get_config(cfg.name, layers=1)
+        cpu = cpu_baseline(layer_cfg, args.cpu_budget_s)
+        if cfg.layers > 1:       # one oracle layer of the 42: scale to a whole step
+            cpu["value"] /= cfg.layers
+            cpu["sample"] += f"; value scaled to a {cfg.layers}-layer step"
+
+    res = {
+        "metric": "MoE-layer tokens/s",
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.name, "experts": cfg.num_experts, "shared_ffn": cfg.shared_ffn,
+            "hidden": cfg.hidden, "ffn": cfg.ffn, "top_k": cfg.top_k, "tokens": T,
+            "layers_per_step": layers_per_step, "weight_sets": n_sets, "batches": args.batches,
+            "weights": "int4 g128 (fp16 scales), router fp16, shared expert fp16",
+            "distinct_experts_per_step_mean": float(np.mean(u_per_combo)),
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
+            "kernel": "moe_w4_grouped_ffn (gate/up launch + down launch)",
+            "ffn_us_mean": float(ffn_ms.mean() * 1e3),
+            "ffn_bytes_mean": float(ffn_bytes.mean()),
+        },
+        "wall_s_timed": wall,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

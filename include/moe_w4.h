@@ -1,0 +1,187 @@
+/*
+ * moe_w4.h -- C ABI of the MI355X (gfx950) sparse-MoE expert layer with
+ * 4-bit group-quantized experts.
+ *
+ * One MoE layer forward is four calls, in this order, on one stream:
+ *
+ *   moe_route              router logits + softmax + top-k
+ *   moe_permute            per-expert token segments (histogram, scan, scatter)
+ *   moe_w4_grouped_ffn     SwiGLU FFN of every routed expert over its segment,
+ *                          int4 weights dequantized inside the kernel, plus the
+ *                          always-on fp16 shared expert
+ *   moe_unpermute_combine  weighted sum of each token's k expert outputs plus
+ *                          the shared expert's output (optional RMS norm)
+ *
+ * Sources: symmetric int4 group quantization with 128 weights per group along
+ * in_features, scale = max|w| / 7, codes clamped to [-8, 7]: lpnh.cn/news/
+ * 2730718 §2.1 (quantization strategy, pseudo-code).  Softmax over the expert
+ * logits and a descending partial sort for the top k: zwxr.cn/news/276292
+ * §3.2 (routing engine); softmax and top-k fused in one kernel: lpnh.cn/news/
+ * 2730718 §2.3.  Tokens that chose the same expert grouped for one grouped
+ * GEMM launch: xdnf.cn/news/329730 §3.2.  Gate / up / down expert matrices and
+ * "8 routed + 1 shared" experts per token: haowenji.com/articles/
+ * x-2109226022155796480 §01.
+ *
+ * Conventions for every call
+ * --------------------------
+ *  - Every pointer argument is a DEVICE pointer unless marked "host".  fp16
+ *    data is passed as uint16_t bit patterns (IEEE binary16).
+ *  - Every device pointer must be 16-byte aligned.
+ *  - The caller allocates and owns every buffer, including the workspace;
+ *    the library never allocates, frees or keeps a pointer after a call
+ *    returns.  Calls are asynchronous on `stream` (a hipStream_t; NULL = the
+ *    default stream), never synchronize the host and never read device memory
+ *    from the host, so a whole layer can be captured into a HIP graph.
+ *  - Outputs are overwritten, never accumulated.  No floating-point atomics
+ *    are used: the same inputs give bitwise identical outputs.
+ *  - Arguments are checked on the host before anything is launched; a failed
+ *    check launches nothing and returns a negative moe_status.  T = 0 returns
+ *    MOE_OK and launches nothing.
+ *  - Two calls that share a workspace must not run concurrently.
+ *
+ * Packed int4 weight format (this library's choice; the page stores int8
+ * codes): a matrix [out, in] is stored row-major as [out, in/2] bytes plus fp16
+ * scales [out, in/128].  A code q in [-8, 7] is stored as the nibble u = q + 8.
+ * Columns 8w..8w+7 of a row occupy bytes 4w..4w+3; read as a little-endian
+ * 32-bit word, nibble p (bits 4p..4p+3) holds column 8w + {0,2,4,6,1,3,5,7}[p].
+ * The dequantized weight is W[n][c] = q[n][c] * scale[n][c / 128].
+ */
+#ifndef MOE_W4_H
+#define MOE_W4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_EINVAL = -1,        /* null / misaligned pointer, negative size        */
+    MOE_EUNSUPPORTED = -2,  /* shape outside what the kernels implement        */
+    MOE_EWORKSPACE = -3,    /* ws_bytes smaller than moe_workspace_size()      */
+    MOE_EHIP = -4           /* the HIP runtime reported an error at launch     */
+} moe_status;
+
+/* One MoE layer.  A HOST struct holding DEVICE pointers.
+ *
+ *  num_experts  E, 1..1024
+ *  hidden       H, multiple of 128, <= 65536
+ *  ffn          F (per routed expert), multiple of 128
+ *  top_k        k, 1..min(E, 32)
+ *  group_size   must be 128
+ *  router_w     fp16 [E, H]
+ *  router_b     fp32 [E], or NULL for no bias (added to the logits before the
+ *               softmax, so it also changes the combine weights)
+ *  gate_q, up_q packed int4 [E, F, H/2];   gate_s, up_s  fp16 [E, F, H/128]
+ *  down_q       packed int4 [E, H, F/2];   down_s        fp16 [E, H, F/128]
+ *  shared_ffn   Fs of the always-on shared expert, multiple of 128, or 0
+ *  shared_gate, shared_up  fp16 [Fs, H];   shared_down   fp16 [H, Fs]
+ */
+typedef struct moe_layer {
+    int32_t num_experts;
+    int32_t hidden;
+    int32_t ffn;
+    int32_t top_k;
+    int32_t group_size;
+    int32_t shared_ffn;
+    const uint16_t *router_w;
+    const float *router_b;
+    const uint8_t *gate_q;
+    const uint16_t *gate_s;
+    const uint8_t *up_q;
+    const uint16_t *up_s;
+    const uint8_t *down_q;
+    const uint16_t *down_s;
+    const uint16_t *shared_gate;
+    const uint16_t *shared_up;
+    const uint16_t *shared_down;
+} moe_layer;
+
+/* Bytes of workspace that every call below needs for up to `max_tokens`
+ * tokens of `layer` (one workspace serves all four calls).  Returns 0 when
+ * the layer description is invalid.  `layer` is a host pointer. */
+size_t moe_workspace_size(const moe_layer *layer, int32_t max_tokens);
+
+/* Router: l[t][e] = sum_h x[t][h] * router_w[e][h] + router_b[e] (fp32
+ * accumulation), p = softmax over e (fp32, max subtracted), then the k largest
+ * logits in descending order, ties to the lower expert index.
+ *   x         fp16 [T, H]
+ *   topk_idx  int32 [T, k]  out: chosen experts, best first
+ *   topk_w    fp32  [T, k]  out: p of the chosen experts (not renormalised)
+ * Logits that are NaN rank below every number; the k indices are always
+ * distinct and in [0, E). */
+moe_status moe_route(const moe_layer *layer, const uint16_t *x, int32_t T,
+                     int32_t *topk_idx, float *topk_w,
+                     void *ws, size_t ws_bytes, void *stream);
+
+/* Permutation of the T*k (token, slot) pairs into per-expert segments.
+ * Flat index f = t*k + j; segment e holds the f with topk_idx[f] = e in
+ * increasing f.
+ *   x         fp16 [T, H]
+ *   topk_idx  int32 [T, k], each in [0, E)
+ *   offsets   int32 [E+1] out: segment e is rows offsets[e]..offsets[e+1]-1
+ *   perm_src  int32 [T*k] out: flat index f of permuted row r
+ *   inv_pos   int32 [T*k] out: permuted row of flat index f
+ *   x_perm    fp16 [T*k, H] out: x_perm[r] = x[perm_src[r] / k] (bit copy)
+ * Indices outside [0, E) are clamped into range on the device so no access
+ * leaves the buffers; such input is a caller error and gives unspecified
+ * (but in-bounds) segments. */
+moe_status moe_permute(const moe_layer *layer, const uint16_t *x,
+                       const int32_t *topk_idx, int32_t T,
+                       int32_t *offsets, int32_t *perm_src, int32_t *inv_pos,
+                       uint16_t *x_perm, void *ws, size_t ws_bytes, void *stream);
+
+/* Grouped SwiGLU FFN over the routed segments and the shared expert.
+ * For each expert e and each row r of its segment:
+ *   g = deq(gate_e) x_perm[r],  u = deq(up_e) x_perm[r]   (fp32 accumulation)
+ *   h = silu(g) * u  with silu(z) = z / (1 + exp(-z)), stored as fp16
+ *   y_perm[r] = deq(down_e) h                              (fp32 accumulation)
+ * and, when the layer has a shared expert, the same with its fp16 weights for
+ * every token of x, into y_shared.
+ *   x_perm    fp16 [T*k, H]    offsets int32 [E+1] (as written by moe_permute;
+ *             offsets[0] = 0, non-decreasing, offsets[E] = T*k)
+ *   x         fp16 [T, H]      (read only for the shared expert; may be NULL
+ *             when shared_ffn = 0)
+ *   y_perm    fp16 [T*k, H] out
+ *   y_shared  fp16 [T, H] out, or NULL when shared_ffn = 0 */
+moe_status moe_w4_grouped_ffn(const moe_layer *layer, const uint16_t *x_perm,
+                              const int32_t *offsets, const uint16_t *x, int32_t T,
+                              uint16_t *y_perm, uint16_t *y_shared,
+                              void *ws, size_t ws_bytes, void *stream);
+
+#define MOE_RMSNORM 1u
+
+/* Combine: out[t] = y_shared[t] + sum_j topk_w[t][j] * y_perm[inv_pos[t*k+j]]
+ * in fp32 (y_shared may be NULL: then that term is 0).  With flags &
+ * MOE_RMSNORM the row is then divided by sqrt(mean(row^2) + eps) (no gain, no
+ * residual), as between stacked layers.  Stored as fp16.
+ *   out  fp16 [T, H] out.  inv_pos entries must lie in [0, T*k) (clamped on
+ *        the device otherwise). */
+moe_status moe_unpermute_combine(const moe_layer *layer, const uint16_t *y_perm,
+                                 const uint16_t *y_shared, const int32_t *inv_pos,
+                                 const float *topk_w, int32_t T, uint32_t flags,
+                                 float eps, uint16_t *out, void *stream);
+
+/* Test hook: out[n][c] = q[n][c] * s[n][c/128] in fp32 (exact), for one packed
+ * matrix q [rows, cols/2], s fp16 [rows, cols/128]; cols multiple of 128. */
+moe_status moe_w4_dequant(const uint8_t *q, const uint16_t *s, int64_t rows,
+                          int64_t cols, float *out, void *stream);
+
+/* Group quantization of an fp16 matrix w [rows, cols] (cols multiple of 128),
+ * lpnh.cn/news/2730718 §2.1 with every step rounded to fp16 as on an fp16
+ * model: s = RN16(max|w_group| / 7), q = clamp(RNE(RN16(w / s)), -8, 7); an
+ * all-zero group gets s = 0, q = 0.  Writes packed q [rows, cols/2] and fp16
+ * s [rows, cols/128]. */
+moe_status moe_w4_quantize(const uint16_t *w, int64_t rows, int64_t cols,
+                           uint8_t *q, uint16_t *s, void *stream);
+
+/* Static description of a status code (host). */
+const char *moe_status_str(moe_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_W4_H */

@@ -1,0 +1,102 @@
+"""Helpers shared by the GPU parity tests.
+
+Inputs come from the seeded generators in workloads/ and, where the method's
+own offline step is needed (fp16 masters -> int4 codes), from the oracle's
+quantizer; expected values come from the oracle only.  The HIP path is
+reached through the C ABI (w4_group_quantized_amd binding).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from workloads import gen as G
+
+gpu = pytest.mark.gpu
+
+
+def require_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def to_dev(a: np.ndarray) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    return t.to(dev())
+
+
+def tol_check(gpu_vals, ref, what="", rel=1e-2, abs_=1e-3):
+    """max|gpu - oracle| <= rel * max|oracle| + abs."""
+    g = np.asarray(gpu_vals, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape, (what, g.shape, r.shape)
+    err = np.abs(g - r).max() if r.size else 0.0
+    bound = rel * (np.abs(r).max() if r.size else 0.0) + abs_
+    assert err <= bound, f"{what}: max err {err:.3e} > bound {bound:.3e}"
+    return err, bound
+
+
+def quantized_experts(cfg, layer=0, experts=None):
+    """Oracle-quantized expert weights from fp16 masters, stacked per matrix.
+
+    Returns dict of numpy arrays gate_q [E,F,H/2], gate_s [E,F,H/128], ...
+    and the per-expert tuple list the oracle takes."""
+    E = cfg.num_experts
+    ids = range(E) if experts is None else experts
+    mats = {n: [] for n in ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s")}
+    per_expert = []
+    for e in ids:
+        tup = []
+        for m, name in ((G.GATE, "gate"), (G.UP, "up"), (G.DOWN, "down")):
+            q, s = O.group_quantize(G.expert_master(cfg, layer, e, m))
+            p = O.pack_w4(q)
+            mats[name + "_q"].append(p)
+            mats[name + "_s"].append(s)
+            tup += [p, s]
+        per_expert.append(tuple(tup))
+    return {k: np.stack(v) for k, v in mats.items()}, per_expert
+
+
+def coded_experts(cfg, layer=0):
+    """Directly drawn packed codes + scales (no quantizer), stacked per matrix."""
+    mats = {n: [] for n in ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s")}
+    per_expert = []
+    for e in range(cfg.num_experts):
+        tup = []
+        for m, name in ((G.GATE, "gate"), (G.UP, "up"), (G.DOWN, "down")):
+            p, s = G.expert_codes(cfg, layer, e, m)
+            mats[name + "_q"].append(p)
+            mats[name + "_s"].append(s)
+            tup += [p, s]
+        per_expert.append(tuple(tup))
+    return {k: np.stack(v) for k, v in mats.items()}, per_expert
+
+
+def make_gpu_layer(cfg, mats, wr, b, shared):
+    from w4_group_quantized_amd import W4MoELayer
+    d = {k: to_dev(v) for k, v in mats.items()}
+    sh = tuple(to_dev(w) for w in shared) if shared is not None else None
+    layer = W4MoELayer(cfg.top_k, to_dev(wr), to_dev(b) if b is not None else None,
+                       d["gate_q"], d["gate_s"], d["up_q"], d["up_s"], d["down_q"], d["down_s"],
+                       shared=sh)
+    return layer
+
+
+def route_compare(idx_gpu, idx_ref, logits_ref, k, gap=1e-6):
+    """Top-k indices must match exactly except for tokens whose oracle logits
+    have a near tie (<= gap) among the first k+1; those are reported.
+    Returns the boolean mask of tokens that disagree (all near ties)."""
+    idx_gpu = np.asarray(idx_gpu)
+    diff = (idx_gpu != idx_ref).any(axis=1)
+    ties = O.near_ties(logits_ref, k, gap)
+    bad = diff & ~ties
+    assert not bad.any(), f"top-k mismatch on tokens {np.nonzero(bad)[0][:10]} (no near tie)"
+    if diff.any():
+        print(f"[reported] {int(diff.sum())} token(s) differ at a near tie <= {gap}")
+    return diff

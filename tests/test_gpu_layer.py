@@ -1,0 +1,82 @@
+"""End-to-end parity of one MoE layer forward (route -> permute -> grouped FFN
+-> combine, all through the C ABI) against the float64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from workloads import get_config
+from workloads import gen as G
+
+from gpu_util import (gpu, require_gpu, to_dev, tol_check, quantized_experts, make_gpu_layer,
+                      route_compare)
+
+pytestmark = gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def run_layer_case(cfg, T, batch=0):
+    mats, experts = quantized_experts(cfg)
+    wr, b = G.router(cfg)
+    shared = G.shared_expert(cfg)
+    x = G.activations(cfg, tokens=T, batch=batch)
+    ref = O.moe_layer(x, wr, b, experts, cfg.top_k, shared=shared)
+    layer = make_gpu_layer(cfg, mats, wr, b, shared)
+    buf = layer.alloc(T)
+    out = layer.forward(to_dev(x), buf)
+    torch.cuda.synchronize()
+    diff = route_compare(_np(buf.topk_idx), ref["idx"], ref["logits"], cfg.top_k)
+    if not diff.any():
+        np.testing.assert_array_equal(_np(buf.offsets), ref["offsets"])
+        np.testing.assert_array_equal(_np(buf.perm_src), ref["perm_src"])
+        np.testing.assert_array_equal(_np(buf.inv_pos), ref["inv_pos"])
+    ok = ~diff
+    tol_check(_np(out)[ok], ref["out"][ok], f"{cfg.name} out")
+    return layer, buf, x
+
+
+def test_tiny_layer_exact_config():
+    """8 experts, hidden 256, ffn 512, top-2, 16 tokens, seed 0."""
+    run_layer_case(get_config("tiny"), 16)
+
+
+@pytest.mark.parametrize("T", [1, 8, 13])
+def test_fine_grained_shape_scaled_down(T):
+    cfg = get_config("decode_fine", num_experts=48, hidden=512, ffn=256, shared_ffn=256)
+    run_layer_case(cfg, T, batch=T)
+
+
+def test_prefill_like_ragged_segments():
+    cfg = get_config("prefill", num_experts=16, hidden=256, ffn=384, top_k=4)
+    run_layer_case(cfg, 150)
+
+
+def test_layer_is_deterministic():
+    cfg = get_config("decode_fine", num_experts=32, hidden=384, ffn=256, shared_ffn=128)
+    layer, buf, x = run_layer_case(cfg, 11)
+    first = _np(buf.out).copy()
+    for _ in range(3):
+        layer.forward(to_dev(x), buf)
+    torch.cuda.synchronize()
+    assert _np(buf.out).tobytes() == first.tobytes()
+
+
+def test_zero_tokens_is_a_noop():
+    cfg = get_config("tiny")
+    mats, _ = quantized_experts(cfg, experts=range(cfg.num_experts))
+    wr, b = G.router(cfg)
+    layer = make_gpu_layer(cfg, mats, wr, b, None)
+    buf = layer.alloc(4)
+    buf.out.fill_(7)
+    x = to_dev(G.activations(cfg, tokens=4))
+    layer.forward(x[:0], buf, T=0)
+    torch.cuda.synchronize()
+    assert (_np(buf.out) == 7).all()

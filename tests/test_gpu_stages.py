@@ -1,0 +1,250 @@
+"""Stage-by-stage parity of the HIP kernels against the oracle (teacher-forced:
+each C entry point is fed the oracle's inputs for that stage, so an upstream
+near tie cannot cascade)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from workloads import get_config
+from workloads import gen as G
+
+from gpu_util import (gpu, require_gpu, to_dev, tol_check, quantized_experts, make_gpu_layer,
+                      route_compare, dev)
+
+pytestmark = gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+# ---------------------------------------------------------------- quantizer / dequant
+@pytest.mark.parametrize("shape", [(512, 256), (64, 4096), (37, 1024)])
+def test_quantize_bitexact(shape):
+    from w4_group_quantized_amd import quantize_fp16
+    cfg = get_config("tiny")
+    g = np.random.default_rng(shape[0])
+    w = (g.standard_normal(shape, dtype=np.float32) * 0.02).astype(np.float16)
+    w[3, :128] = 0                                    # all-zero group
+    w[5, 128:256] = np.float16(1e-7)                  # subnormal-range group
+    w[6, :] = -w[6, :]
+    q_ref, s_ref = O.group_quantize(w)
+    q, s = quantize_fp16(to_dev(w))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(_np(s).view(np.uint16), s_ref.view(np.uint16))
+    np.testing.assert_array_equal(_np(q), O.pack_w4(q_ref))
+    del cfg
+
+
+def test_quantize_golden_fixture():
+    import json, os
+    from w4_group_quantized_amd import quantize_fp16
+    fx = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "quantize_example.json")))
+    w = np.zeros(fx["shape"], dtype=np.float16)
+    for c, v in fx["weights_nonzero"].items():
+        w[0, int(c)] = v
+    q, s = quantize_fp16(to_dev(w))
+    torch.cuda.synchronize()
+    assert [float(x) for x in _np(s)[0]] == fx["expected_scales"]
+    codes = O.unpack_w4(_np(q))
+    exp = np.zeros(fx["shape"], dtype=np.int8)
+    for c, v in fx["expected_codes_nonzero"].items():
+        exp[0, int(c)] = v
+    np.testing.assert_array_equal(codes, exp)
+
+
+def test_dequant_bitexact_all_codes():
+    from w4_group_quantized_amd import dequantize
+    g = np.random.default_rng(11)
+    packed = g.integers(0, 256, size=(96, 384), dtype=np.uint8)    # every code, including -8
+    packed[0, :256] = np.arange(256, dtype=np.uint8)
+    s = (g.uniform(1e-4, 5e-2, size=(96, 6))).astype(np.float16)
+    s[1, 2] = 0
+    out = dequantize(to_dev(packed), to_dev(s))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(_np(out).astype(np.float64), O.dequant(packed, s))
+
+
+# ---------------------------------------------------------------- router
+ROUTE_CASES = [
+    ("tiny", {}, 16),
+    ("tiny", {}, 5),
+    ("decode_fine", {}, 8),
+    ("decode_fine", {}, 37),
+    ("decode_coarse", {}, 16),
+    ("prefill", {}, 300),
+]
+
+
+@pytest.mark.parametrize("name,over,T", ROUTE_CASES)
+def test_route(name, over, T):
+    cfg = get_config(name, **over)
+    wr, b = G.router(cfg)
+    x = G.activations(cfg, tokens=T, batch=7)
+    idx_ref, w_ref, l_ref = O.route(x, wr, b, cfg.top_k)
+    layer = _router_only_layer(cfg, wr, b)
+    buf = layer.alloc(T)
+    layer.route(to_dev(x), buf, T)
+    torch.cuda.synchronize()
+    diff = route_compare(_np(buf.topk_idx), idx_ref, l_ref, cfg.top_k)
+    ok = ~diff
+    tol_check(_np(buf.topk_w)[ok], w_ref[ok], "topk_w", rel=1e-5, abs_=1e-7)
+
+
+def _router_only_layer(cfg, wr, b):
+    from w4_group_quantized_amd import W4MoELayer
+    z8 = to_dev(np.zeros((1, 1, 16), np.uint8))
+    z16 = to_dev(np.zeros((1, 1, 8), np.float16))
+    layer = W4MoELayer(cfg.top_k, to_dev(wr), to_dev(b) if b is not None else None,
+                       z8, z16, z8, z16, z8, z16)
+    layer.desc.ffn = cfg.ffn
+    return layer
+
+
+def test_route_duplicate_rows_lower_index_wins():
+    cfg = get_config("decode_fine")
+    wr, b = G.router(cfg)
+    wr = wr.copy()
+    b = b.copy()
+    for lo, hi in ((3, 200), (17, 18), (0, 287)):
+        wr[hi] = wr[lo]
+        b[hi] = b[lo] = 3.0                          # make the pair win
+    x = G.activations(cfg, tokens=24, batch=3)
+    idx_ref, _, l_ref = O.route(x, wr, b, cfg.top_k)
+    layer = _router_only_layer(cfg, wr, b)
+    buf = layer.alloc(24)
+    layer.route(to_dev(x), buf, 24)
+    torch.cuda.synchronize()
+    idx = _np(buf.topk_idx)
+    np.testing.assert_array_equal(idx, idx_ref)      # exact ties: no near-tie excuse
+    for lo, hi in ((3, 200), (17, 18), (0, 287)):
+        for row in idx.tolist():
+            if hi in row:
+                assert lo in row and row.index(lo) < row.index(hi)
+
+
+def test_route_nonfinite_inputs_give_valid_indices():
+    cfg = get_config("tiny")
+    wr, _ = G.router(cfg)
+    x = G.activations(cfg, tokens=4).copy()
+    x[1, 7] = np.float16(np.nan)
+    x[2, 3] = np.float16(np.inf)
+    layer = _router_only_layer(cfg, wr, None)
+    buf = layer.alloc(4)
+    layer.route(to_dev(x), buf, 4)
+    torch.cuda.synchronize()
+    idx = _np(buf.topk_idx)
+    assert ((idx >= 0) & (idx < cfg.num_experts)).all()
+    assert all(len(set(r)) == cfg.top_k for r in idx.tolist())
+    w = _np(buf.topk_w)
+    assert np.isfinite(w[[0, 3]]).all() and np.isnan(w[1]).all()
+
+
+# ---------------------------------------------------------------- permutation
+PERM_CASES = [
+    (16, 2, 8, "random"),
+    (8, 8, 288, "random"),
+    (100, 8, 128, "random"),       # 800 entries: several chunks, ragged tail
+    (1, 4, 16, "random"),
+    (50, 1, 6, "one_expert"),
+    (7, 5, 5, "k_eq_E"),
+    (1000, 4, 1024, "random"),
+]
+
+
+@pytest.mark.parametrize("T,k,E,kind", PERM_CASES)
+def test_permute_bitexact(T, k, E, kind):
+    g = np.random.default_rng(T * 31 + k)
+    if kind == "one_expert":
+        idx = np.full((T, k), 3, dtype=np.int32)
+    elif kind == "k_eq_E":
+        idx = np.stack([g.permutation(E) for _ in range(T)]).astype(np.int32)
+    else:
+        idx = np.stack([g.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    H = 256
+    x = (g.standard_normal((T, H)) ).astype(np.float16)
+    off, perm_src, inv_pos = O.permute(idx, E)
+    xp_ref = O.gather_rows(x, perm_src, k)
+    cfg = get_config("tiny", num_experts=E, top_k=k, hidden=H)
+    wr = np.zeros((E, H), np.float16)
+    layer = _router_only_layer(cfg, wr, None)
+    buf = layer.alloc(T)
+    buf.topk_idx.copy_(to_dev(idx))
+    layer.permute(to_dev(x), buf, T)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(_np(buf.offsets), off)
+    np.testing.assert_array_equal(_np(buf.perm_src), perm_src)
+    np.testing.assert_array_equal(_np(buf.inv_pos), inv_pos)
+    assert _np(buf.x_perm).tobytes() == xp_ref.tobytes()
+
+
+# ---------------------------------------------------------------- FFN
+FFN_CASES = [
+    ("tiny", {}, 16, 0),
+    ("tiny", {"num_experts": 4, "top_k": 4}, 21, 0),                    # >16 rows per segment
+    ("tiny", {"num_experts": 12, "hidden": 512, "ffn": 384, "top_k": 3}, 9, 256),
+    ("tiny", {"num_experts": 6, "hidden": 384, "ffn": 256, "top_k": 2}, 70, 128),
+]
+
+
+@pytest.mark.parametrize("name,over,T,Fs", FFN_CASES)
+def test_ffn_teacher_forced(name, over, T, Fs):
+    cfg = get_config(name, shared_ffn=Fs, **over)
+    mats, experts = quantized_experts(cfg)
+    wr, b = G.router(cfg)
+    x = G.activations(cfg, tokens=T, batch=5)
+    shared = G.shared_expert(cfg) if Fs else None
+    idx, w, l = O.route(x, wr, b, cfg.top_k)
+    off, perm_src, inv_pos = O.permute(idx, cfg.num_experts)
+    x_perm = O.gather_rows(x, perm_src, cfg.top_k)
+    layer = make_gpu_layer(cfg, mats, wr, b, shared)
+    buf = layer.alloc(T)
+    buf.offsets.copy_(to_dev(off))
+    buf.x_perm.copy_(to_dev(x_perm))
+    layer.ffn(to_dev(x), buf, T)
+    torch.cuda.synchronize()
+    y_perm = _np(buf.y_perm)
+    for e in range(cfg.num_experts):
+        a, bnd = int(off[e]), int(off[e + 1])
+        if bnd > a:
+            ref = O.expert_ffn_w4(x_perm[a:bnd], *experts[e])
+            tol_check(y_perm[a:bnd], ref, f"expert {e}")
+    if Fs:
+        tol_check(_np(buf.y_shared), O.swiglu_ffn(x, *shared), "shared")
+
+
+# ---------------------------------------------------------------- combine
+@pytest.mark.parametrize("rms", [False, True])
+@pytest.mark.parametrize("T,k,H,with_shared", [(16, 2, 256, False), (9, 8, 4096, True),
+                                               (3, 32, 384, True)])
+def test_combine(T, k, H, with_shared, rms):
+    g = np.random.default_rng(T + k)
+    N = T * k
+    y_perm = (g.standard_normal((N, H)) * 0.3).astype(np.float16)
+    ys = (g.standard_normal((T, H)) * 0.3).astype(np.float16) if with_shared else None
+    inv = g.permutation(N).astype(np.int32)
+    w = g.uniform(0, 0.3, size=(T, k)).astype(np.float32)
+    ref = O.combine(y_perm, ys, inv, w, T, k)
+    if rms:
+        ref = O.rmsnorm(ref, 1e-6)
+    E = max(k, 8)
+    cfg = get_config("tiny", num_experts=E, top_k=k, hidden=H, shared_ffn=128 if with_shared else 0)
+    layer = _router_only_layer(cfg, np.zeros((E, H), np.float16), None)
+    if with_shared:
+        layer.Fs = 128
+        layer.desc.shared_ffn = 128
+    buf = layer.alloc(T)
+    buf.y_perm.copy_(to_dev(y_perm))
+    if with_shared:
+        buf.y_shared.copy_(to_dev(ys))
+    buf.inv_pos.copy_(to_dev(inv))
+    buf.topk_w.copy_(to_dev(w))
+    layer.combine(buf, T, rmsnorm=rms)
+    torch.cuda.synchronize()
+    tol_check(_np(buf.out), ref, "combine")

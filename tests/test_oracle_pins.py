@@ -108,12 +108,22 @@ def test_quantizer_refuses_ragged_in_features():
 
 # ---------------------------------------------------------------- packing / dequant
 def test_pack_layout_exhaustive():
-    """All 256 byte values: low nibble = even column, value = nibble - 8."""
-    packed = np.arange(256, dtype=np.uint8).reshape(1, 256)
+    """Every byte value at every byte position of a 32-bit word, against the
+    documented table: byte 0 -> columns (0, 2), byte 1 -> (4, 6),
+    byte 2 -> (1, 3), byte 3 -> (5, 7) as (low, high) nibble; value = nibble - 8."""
+    table = {0: (0, 2), 1: (4, 6), 2: (1, 3), 3: (5, 7)}
+    packed = np.zeros((256, 64), dtype=np.uint8)
+    for v in range(256):
+        for pos in range(4):
+            packed[v, 4 * pos + pos] = v       # word `pos`, byte `pos`
     q = O.unpack_w4(packed)
-    for b in range(256):
-        assert q[0, 2 * b] == (b & 15) - 8
-        assert q[0, 2 * b + 1] == (b >> 4) - 8
+    for v in range(256):
+        for pos in range(4):
+            lo, hi = table[pos]
+            assert q[v, 8 * pos + lo] == (v & 15) - 8
+            assert q[v, 8 * pos + hi] == (v >> 4) - 8
+            others = [c for c in range(8) if c not in (lo, hi)]
+            assert (q[v, 8 * pos + np.array(others)] == -8).all()
     np.testing.assert_array_equal(O.pack_w4(q), packed)
 
 

@@ -1,0 +1,219 @@
+// Grouped SwiGLU expert FFN over per-expert token segments, int4 weights
+// dequantized in registers right before the MFMA, plus the fp16 shared expert.
+//
+// Grouped GEMM over the selected experts, one launch for all of them:
+// xdnf.cn/news/329730 §3.2 and lpnh.cn/news/2730718 §2.3.  Expert = gate / up /
+// down matrices with a SiLU-gated product (haowenji.com/articles/
+// x-2109226022155796480 §01), shared expert always on.  Decode is bound by
+// streaming the selected experts' weights (lpnh.cn/news/2730718 §1.2,
+// haowenji.com ... §09): every weight byte is loaded once per 16-token tile and
+// unpacked once, then reused for all tokens of the tile on the matrix cores.
+//
+// Phase 1 (gate/up):  h[r] = silu(deq(Wg_e) x[r]) * (deq(Wu_e) x[r])  -> fp16
+// Phase 2 (down):     y[r] = deq(Wd_e) h[r]                          -> fp16
+// The phases are separate launches because phase 2 of an expert needs every
+// column of h for its rows.
+//
+// Work items (one 256-thread block each):
+//   routed item = (segment tile, n-tile): a segment tile is 16 consecutive rows
+//     of one expert's segment; an n-tile is 64*NT weight rows; each of the 4
+//     waves streams 16*NT rows over the whole K range.
+//   shared item = (16-token tile, 16 weight rows); the 4 waves split K 4 ways,
+//     so that a wave moves as many bytes as a routed wave (fp16 weights are 4x
+//     the bytes of int4).
+// The grid is sized for the worst case on the host; items past the live
+// segment tiles exit right after locating themselves (nothing is read back to
+// the host between calls).
+#include "common.h"
+#include "kernels.h"
+#include "tiles.h"
+
+namespace moe {
+
+constexpr int kTileM = 16;   // tokens per MFMA tile
+
+struct FfnArgs {
+  int E, H, F, Fs, T, N;            // N = T * k
+  const int32_t *offsets;           // [E+1]
+  const f16 *a_routed;              // phase 1: x_perm [N, H]; phase 2: h [N, F]
+  const f16 *a_shared;              // phase 1: x [T, H];      phase 2: h_shared [T, Fs]
+  const uint8_t *q0, *q1;           // phase 1: gate_q, up_q;  phase 2: down_q, unused
+  const f16 *s0, *s1;               // matching scales
+  const f16 *w0, *w1;               // shared expert fp16 weights (phase 2: w0 only)
+  f16 *out_routed;                  // phase 1: h [N, F];      phase 2: y_perm [N, H]
+  f16 *out_shared;                  // phase 1: h_shared;      phase 2: y_shared
+  int routed_items;                 // worst-case number of routed items
+};
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// Block-cooperative: which expert and which 16-row tile of its segment is
+// segment tile `slot`?  Tiles are numbered expert by expert.  Returns false
+// when slot is past the last tile.  Requires blockDim.x = 256, E <= 1024.
+__device__ bool locate_tile(const int32_t *__restrict__ off, int E, int slot, int *e_out,
+                            int *mt_out) {
+  __shared__ int s_scan[4];
+  __shared__ int s_res[2];
+  const int tid = threadIdx.x;
+  int c[4], sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = 4 * tid + i;
+    c[i] = e < E ? (off[e + 1] - off[e] + kTileM - 1) / kTileM : 0;
+    sum += c[i];
+  }
+  int total;
+  int run = block_excl_scan(sum, s_scan, &total);
+  if (tid == 0) s_res[0] = -1;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (slot >= run && slot < run + c[i]) {
+      s_res[0] = 4 * tid + i;
+      s_res[1] = slot - run;
+    }
+    run += c[i];
+  }
+  __syncthreads();
+  *e_out = s_res[0];
+  *mt_out = s_res[1];
+  return s_res[0] >= 0;
+}
+
+// PHASE 1: PAIR = gate and up tiles per wave, SwiGLU epilogue.
+// PHASE 2: one matrix, plain epilogue.
+template <int PHASE, int NT>
+__global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
+  constexpr bool kPair = PHASE == 1;
+  constexpr int kMats = kPair ? 2 : 1;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  const int r = lane & 15, kb = lane >> 4;
+  const int K = kPair ? p.H : p.F;             // in_features of this phase
+  const int Nrows = kPair ? p.F : p.H;         // out_features of this phase
+  const int G = K / kGroup;
+  __shared__ float red[3 * 2 * 4 * kWave];
+
+  if ((int)blockIdx.x < p.routed_items) {
+    const int ntiles = Nrows / (64 * NT);
+    const int slot = blockIdx.x / ntiles, nt = blockIdx.x % ntiles;
+    int e, mt;
+    if (!locate_tile(p.offsets, p.E, slot, &e, &mt)) return;
+    const int seg0 = p.offsets[e] + mt * kTileM;
+    // offsets come from device memory: keep every row inside [0, N)
+    if (seg0 < 0 || seg0 >= p.N) return;
+    const int rows = min(min(kTileM, p.offsets[e + 1] - seg0), p.N - seg0);
+    const f16 *arow = r < rows ? p.a_routed + (size_t)(seg0 + r) * K : nullptr;
+    const uint8_t *qrow[kMats * NT];
+    const f16 *srow[kMats * NT];
+    int nrow[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      nrow[t] = nt * 64 * NT + (wid * NT + t) * 16 + r;
+      const size_t row = (size_t)e * Nrows + nrow[t];
+      qrow[t] = p.q0 + row * (K / 2);
+      srow[t] = p.s0 + row * G;
+      if (kPair) {
+        qrow[NT + t] = p.q1 + row * (K / 2);
+        srow[NT + t] = p.s1 + row * G;
+      }
+    }
+    f32x4 acc[kMats * NT];
+#pragma unroll
+    for (int t = 0; t < kMats * NT; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    w4_tiles<kMats * NT>(arow, qrow, srow, kb, 0, G, acc);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tok = 4 * kb + j;
+        if (tok < rows) {
+          const float v = kPair ? silu(acc[t][j]) * acc[NT + t][j] : acc[t][j];
+          p.out_routed[(size_t)(seg0 + tok) * Nrows + nrow[t]] = (f16)v;
+        }
+      }
+    return;
+  }
+
+  // shared expert: fp16 weights, 16 weight rows per block, K split over waves
+  const int Ks = kPair ? p.H : p.Fs;
+  const int Ns = kPair ? p.Fs : p.H;
+  const int Gs = Ks / kGroup;
+  const int sitem = blockIdx.x - p.routed_items;
+  const int sntiles = Ns / 16;
+  const int mt = sitem / sntiles, nt = sitem % sntiles;
+  const int tok0 = mt * kTileM;
+  if (tok0 >= p.T) return;
+  const int rows = min(kTileM, p.T - tok0);
+  const f16 *arow = r < rows ? p.a_shared + (size_t)(tok0 + r) * Ks : nullptr;
+  const int nrow = nt * 16 + r;
+  const f16 *wrow[kMats];
+  wrow[0] = p.w0 + (size_t)nrow * Ks;
+  if (kPair) wrow[kMats - 1] = p.w1 + (size_t)nrow * Ks;
+  f32x4 acc[kMats];
+#pragma unroll
+  for (int t = 0; t < kMats; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const int g0 = wid * Gs / 4, g1 = (wid + 1) * Gs / 4;
+  f16_tiles<kMats>(arow, wrow, kb, g0, g1, acc);
+  ksplit_reduce<kMats>(acc, red);
+  if (wid != 0) return;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int tok = 4 * kb + j;
+    if (tok < rows) {
+      const float v = kPair ? silu(acc[0][j]) * acc[kMats - 1][j] : acc[0][j];
+      p.out_shared[(size_t)(tok0 + tok) * Ns + nrow] = (f16)v;
+    }
+  }
+}
+
+constexpr int kNT1 = 1;   // phase 1: 64 gate rows + 64 up rows per block
+constexpr int kNT2 = 2;   // phase 2: 128 down rows per block
+
+hipError_t launch_ffn(const moe_layer &L, const uint16_t *x_perm, const int32_t *offsets,
+                      const uint16_t *x, int32_t T, uint16_t *y_perm, uint16_t *y_shared,
+                      uint16_t *h, uint16_t *h_shared, hipStream_t st) {
+  const int E = L.num_experts, H = L.hidden, F = L.ffn, Fs = L.shared_ffn, k = L.top_k;
+  const int N = T * k;
+  // worst case number of 16-row segment tiles: every non-empty segment adds at
+  // most one partial tile
+  const int max_tiles = (E < N ? E : N) + (N + kTileM - 1) / kTileM;
+  const int mtiles_shared = (T + kTileM - 1) / kTileM;
+
+  FfnArgs a{};
+  a.E = E; a.H = H; a.F = F; a.Fs = Fs; a.T = T; a.N = N;
+  a.offsets = offsets;
+
+  // phase 1
+  a.a_routed = reinterpret_cast<const f16 *>(x_perm);
+  a.a_shared = reinterpret_cast<const f16 *>(x);
+  a.q0 = L.gate_q; a.q1 = L.up_q;
+  a.s0 = reinterpret_cast<const f16 *>(L.gate_s);
+  a.s1 = reinterpret_cast<const f16 *>(L.up_s);
+  a.w0 = reinterpret_cast<const f16 *>(L.shared_gate);
+  a.w1 = reinterpret_cast<const f16 *>(L.shared_up);
+  a.out_routed = reinterpret_cast<f16 *>(h);
+  a.out_shared = reinterpret_cast<f16 *>(h_shared);
+  a.routed_items = max_tiles * (F / (64 * kNT1));
+  int shared_items = Fs ? mtiles_shared * (Fs / 16) : 0;
+  hipLaunchKernelGGL((ffn_decode_kernel<1, kNT1>), dim3(a.routed_items + shared_items),
+                     dim3(256), 0, st, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+
+  // phase 2
+  a.a_routed = reinterpret_cast<const f16 *>(h);
+  a.a_shared = reinterpret_cast<const f16 *>(h_shared);
+  a.q0 = L.down_q; a.q1 = nullptr;
+  a.s0 = reinterpret_cast<const f16 *>(L.down_s); a.s1 = nullptr;
+  a.w0 = reinterpret_cast<const f16 *>(L.shared_down); a.w1 = nullptr;
+  a.out_routed = reinterpret_cast<f16 *>(y_perm);
+  a.out_shared = reinterpret_cast<f16 *>(y_shared);
+  a.routed_items = max_tiles * (H / (64 * kNT2));
+  shared_items = Fs ? mtiles_shared * (H / 16) : 0;
+  hipLaunchKernelGGL((ffn_decode_kernel<2, kNT2>), dim3(a.routed_items + shared_items),
+                     dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,42 @@
+// Host-side launchers of the gfx950 kernels (internal to libmoe_w4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/moe_w4.h"
+
+namespace moe {
+
+constexpr int kPermChunk = 256;   // flat (token, slot) entries per permutation block
+constexpr int kGroupSize = 128;   // the only group size the kernels implement
+
+// Byte offsets of the per-call scratch regions inside the caller's workspace.
+struct WsLayout {
+  size_t logits;    // fp32 [T, E]
+  size_t counts;    // int32 [nchunks, E]
+  size_t bases;     // int32 [nchunks, E]
+  size_t h;         // fp16 [T*k, F]
+  size_t h_shared;  // fp16 [T, Fs]
+  size_t total;
+};
+WsLayout ws_layout(const moe_layer &L, int32_t T);
+
+hipError_t launch_quantize(const uint16_t *w, int64_t rows, int64_t cols, uint8_t *q,
+                           uint16_t *s, hipStream_t st);
+hipError_t launch_dequant(const uint8_t *q, const uint16_t *s, int64_t rows, int64_t cols,
+                          float *out, hipStream_t st);
+hipError_t launch_route(const moe_layer &L, const uint16_t *x, int32_t T, int32_t *idx,
+                        float *w, float *logits, hipStream_t st);
+hipError_t launch_permute(const moe_layer &L, const uint16_t *x, const int32_t *idx, int32_t T,
+                          int32_t *offsets, int32_t *perm_src, int32_t *inv_pos,
+                          uint16_t *x_perm, int32_t *counts, int32_t *bases, hipStream_t st);
+hipError_t launch_ffn(const moe_layer &L, const uint16_t *x_perm, const int32_t *offsets,
+                      const uint16_t *x, int32_t T, uint16_t *y_perm, uint16_t *y_shared,
+                      uint16_t *h, uint16_t *h_shared, hipStream_t st);
+hipError_t launch_combine(const moe_layer &L, const uint16_t *y_perm, const uint16_t *y_shared,
+                          const int32_t *inv_pos, const float *w, int32_t T, uint32_t flags,
+                          float eps, uint16_t *out, hipStream_t st);
+
+}  // namespace moe

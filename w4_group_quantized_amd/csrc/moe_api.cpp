@@ -1,0 +1,181 @@
+// C ABI of libmoe_w4: argument checks on the host, workspace carving, and the
+// launches.  Nothing here allocates, frees or synchronizes.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/moe_w4.h"
+#include "kernels.h"
+
+namespace moe {
+
+static inline size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+static inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+static inline bool ok_ptr(const void *p) { return p != nullptr && aligned16(p); }
+
+WsLayout ws_layout(const moe_layer &L, int32_t T) {
+  WsLayout w{};
+  const size_t Tz = (size_t)(T > 0 ? T : 0);
+  const size_t E = (size_t)L.num_experts, k = (size_t)L.top_k;
+  const size_t N = Tz * k;
+  const size_t nch = (N + kPermChunk - 1) / kPermChunk;
+  size_t off = 0;
+  w.logits = off;   off += align_up(Tz * E * sizeof(float));
+  w.counts = off;   off += align_up(nch * E * sizeof(int32_t));
+  w.bases = off;    off += align_up(nch * E * sizeof(int32_t));
+  w.h = off;        off += align_up(N * (size_t)L.ffn * 2);
+  w.h_shared = off; off += align_up(Tz * (size_t)L.shared_ffn * 2);
+  w.total = off;
+  return w;
+}
+
+// Shape limits of the kernels.
+static moe_status check_layer(const moe_layer *L) {
+  if (!L) return MOE_EINVAL;
+  if (L->group_size != kGroupSize) return MOE_EUNSUPPORTED;
+  if (L->num_experts < 1 || L->num_experts > 1024) return MOE_EUNSUPPORTED;
+  if (L->hidden < 128 || L->hidden > 65536 || L->hidden % 128) return MOE_EUNSUPPORTED;
+  if (L->ffn < 128 || L->ffn > 262144 || L->ffn % 128) return MOE_EUNSUPPORTED;
+  if (L->top_k < 1 || L->top_k > 32 || L->top_k > L->num_experts) return MOE_EUNSUPPORTED;
+  if (L->shared_ffn < 0 || L->shared_ffn > 262144 || L->shared_ffn % 128)
+    return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+static moe_status check_tokens(const moe_layer *L, int32_t T) {
+  if (T < 0) return MOE_EINVAL;
+  // every flat index and every element offset of the permuted rows must fit
+  if ((int64_t)T * L->top_k > (int64_t)0x7fffffff / 2) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+static moe_status check_ws(const moe_layer *L, int32_t T, const void *ws, size_t ws_bytes) {
+  const size_t need = ws_layout(*L, T).total;
+  if (need && !ok_ptr(ws)) return MOE_EINVAL;
+  if (ws_bytes < need) return MOE_EWORKSPACE;
+  return MOE_OK;
+}
+
+static inline moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+size_t moe_workspace_size(const moe_layer *layer, int32_t max_tokens) {
+  if (check_layer(layer) != MOE_OK || max_tokens < 0) return 0;
+  return ws_layout(*layer, max_tokens).total;
+}
+
+moe_status moe_route(const moe_layer *L, const uint16_t *x, int32_t T, int32_t *topk_idx,
+                     float *topk_w, void *ws, size_t ws_bytes, void *stream) {
+  moe_status s;
+  if ((s = check_layer(L)) != MOE_OK) return s;
+  if ((s = check_tokens(L, T)) != MOE_OK) return s;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(L->router_w) || !ok_ptr(x) || !ok_ptr(topk_idx) || !ok_ptr(topk_w))
+    return MOE_EINVAL;
+  if (L->router_b && !aligned16(L->router_b)) return MOE_EINVAL;
+  if ((s = check_ws(L, T, ws, ws_bytes)) != MOE_OK) return s;
+  const WsLayout w = ws_layout(*L, T);
+  float *logits = reinterpret_cast<float *>(static_cast<char *>(ws) + w.logits);
+  return hip_status(launch_route(*L, x, T, topk_idx, topk_w, logits, (hipStream_t)stream));
+}
+
+moe_status moe_permute(const moe_layer *L, const uint16_t *x, const int32_t *topk_idx, int32_t T,
+                       int32_t *offsets, int32_t *perm_src, int32_t *inv_pos, uint16_t *x_perm,
+                       void *ws, size_t ws_bytes, void *stream) {
+  moe_status s;
+  if ((s = check_layer(L)) != MOE_OK) return s;
+  if ((s = check_tokens(L, T)) != MOE_OK) return s;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(x) || !ok_ptr(topk_idx) || !ok_ptr(offsets) || !ok_ptr(perm_src) ||
+      !ok_ptr(inv_pos) || !ok_ptr(x_perm))
+    return MOE_EINVAL;
+  if ((s = check_ws(L, T, ws, ws_bytes)) != MOE_OK) return s;
+  const WsLayout w = ws_layout(*L, T);
+  char *base = static_cast<char *>(ws);
+  return hip_status(launch_permute(*L, x, topk_idx, T, offsets, perm_src, inv_pos, x_perm,
+                                   reinterpret_cast<int32_t *>(base + w.counts),
+                                   reinterpret_cast<int32_t *>(base + w.bases),
+                                   (hipStream_t)stream));
+}
+
+moe_status moe_w4_grouped_ffn(const moe_layer *L, const uint16_t *x_perm, const int32_t *offsets,
+                              const uint16_t *x, int32_t T, uint16_t *y_perm, uint16_t *y_shared,
+                              void *ws, size_t ws_bytes, void *stream) {
+  moe_status s;
+  if ((s = check_layer(L)) != MOE_OK) return s;
+  if ((s = check_tokens(L, T)) != MOE_OK) return s;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(x_perm) || !ok_ptr(offsets) || !ok_ptr(y_perm) || !ok_ptr(L->gate_q) ||
+      !ok_ptr(L->gate_s) || !ok_ptr(L->up_q) || !ok_ptr(L->up_s) || !ok_ptr(L->down_q) ||
+      !ok_ptr(L->down_s))
+    return MOE_EINVAL;
+  if (L->shared_ffn > 0 && (!ok_ptr(x) || !ok_ptr(y_shared) || !ok_ptr(L->shared_gate) ||
+                            !ok_ptr(L->shared_up) || !ok_ptr(L->shared_down)))
+    return MOE_EINVAL;
+  if ((s = check_ws(L, T, ws, ws_bytes)) != MOE_OK) return s;
+  const WsLayout w = ws_layout(*L, T);
+  char *base = static_cast<char *>(ws);
+  return hip_status(launch_ffn(*L, x_perm, offsets, x, T, y_perm,
+                               L->shared_ffn > 0 ? y_shared : nullptr,
+                               reinterpret_cast<uint16_t *>(base + w.h),
+                               reinterpret_cast<uint16_t *>(base + w.h_shared),
+                               (hipStream_t)stream));
+}
+
+moe_status moe_unpermute_combine(const moe_layer *L, const uint16_t *y_perm,
+                                 const uint16_t *y_shared, const int32_t *inv_pos,
+                                 const float *topk_w, int32_t T, uint32_t flags, float eps,
+                                 uint16_t *out, void *stream) {
+  moe_status s;
+  if ((s = check_layer(L)) != MOE_OK) return s;
+  if ((s = check_tokens(L, T)) != MOE_OK) return s;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(y_perm) || !ok_ptr(inv_pos) || !ok_ptr(topk_w) || !ok_ptr(out)) return MOE_EINVAL;
+  if (y_shared && !aligned16(y_shared)) return MOE_EINVAL;
+  if (flags & ~MOE_RMSNORM) return MOE_EINVAL;
+  if ((flags & MOE_RMSNORM) && !(eps >= 0.0f)) return MOE_EINVAL;
+  return hip_status(launch_combine(*L, y_perm, y_shared, inv_pos, topk_w, T, flags, eps, out,
+                                   (hipStream_t)stream));
+}
+
+moe_status moe_w4_dequant(const uint8_t *q, const uint16_t *s, int64_t rows, int64_t cols,
+                          float *out, void *stream) {
+  if (rows < 0 || cols < 0) return MOE_EINVAL;
+  if (cols % 128) return MOE_EUNSUPPORTED;
+  if (rows == 0 || cols == 0) return MOE_OK;
+  if ((rows * (cols / 8) + 255) / 256 > 0x7fffffffLL) return MOE_EUNSUPPORTED;
+  if (!ok_ptr(q) || !ok_ptr(s) || !ok_ptr(out)) return MOE_EINVAL;
+  return hip_status(launch_dequant(q, s, rows, cols, out, (hipStream_t)stream));
+}
+
+moe_status moe_w4_quantize(const uint16_t *w, int64_t rows, int64_t cols, uint8_t *q, uint16_t *s,
+                           void *stream) {
+  if (rows < 0 || cols < 0) return MOE_EINVAL;
+  if (cols % 128) return MOE_EUNSUPPORTED;
+  if (rows == 0 || cols == 0) return MOE_OK;
+  if ((rows * (cols / 8) + 255) / 256 > 0x7fffffffLL) return MOE_EUNSUPPORTED;
+  if (!ok_ptr(w) || !ok_ptr(q) || !ok_ptr(s)) return MOE_EINVAL;
+  return hip_status(launch_quantize(w, rows, cols, q, s, (hipStream_t)stream));
+}
+
+const char *moe_status_str(moe_status status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument (null or misaligned pointer, negative size, bad flag)";
+    case MOE_EUNSUPPORTED: return "unsupported shape (group size, hidden/ffn multiple of 128, "
+                                  "top_k, expert count)";
+    case MOE_EWORKSPACE: return "workspace smaller than moe_workspace_size()";
+    case MOE_EHIP: return "HIP runtime error at launch";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

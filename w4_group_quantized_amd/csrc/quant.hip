@@ -1,0 +1,99 @@
+// Group quantization (fp16 -> packed int4 + fp16 scales) and the exact
+// dequantization test hook.
+//
+// Quantizer: lpnh.cn/news/2730718 §2.1 (group-quantization pseudo-code),
+// applied to fp16 weights (§3.2), so each arithmetic step rounds to fp16:
+//   s = RN16(max|w| / 7),  q = clamp(RNE(RN16(w / s)), -8, 7);  s = 0 -> q = 0.
+// Quotients are formed with the correctly rounded fp32 division and then
+// rounded to fp16; with 24 >= 2*11 + 2 bits that double rounding equals a
+// single correct rounding to fp16.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// One thread per 8 consecutive columns (one 32-bit packed word); 16 threads
+// cover one 128-column group, a wave covers 4 groups.
+__global__ __launch_bounds__(256) void quantize_kernel(const f16 *__restrict__ w,
+                                                       int64_t rows, int64_t cols,
+                                                       uint32_t *__restrict__ q,
+                                                       f16 *__restrict__ s) {
+  const int64_t words_per_row = cols / 8;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = rows * words_per_row;
+  // Lanes past the end still take part in the 16-lane max so that the
+  // shuffles see a full group; they load nothing and store nothing.
+  const bool live = t < total;
+  float v[8];
+  float m = 0.0f;
+  if (live) {
+    const int64_t row = t / words_per_row, word = t % words_per_row;
+    u32x4 raw = ld16(w + row * cols + word * 8);
+    f16x8 h = as_f16x8(raw);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[i] = (float)h[i];
+      m = fmaxf(m, fabsf(v[i]));
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+  if (!live) return;
+  const f16 s16 = (f16)__fdiv_rn(m, 7.0f);
+  const float sf = (float)s16;
+  uint32_t u[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float qi = 0.0f;
+    if (sf > 0.0f) {
+      const f16 r16 = (f16)__fdiv_rn(v[i], sf);
+      qi = fminf(fmaxf(rintf((float)r16), -8.0f), 7.0f);
+    }
+    u[i] = (uint32_t)((int)qi + 8);
+  }
+  // nibble p holds column {0,2,4,6,1,3,5,7}[p]
+  const uint32_t word = u[0] | (u[2] << 4) | (u[4] << 8) | (u[6] << 12) | (u[1] << 16) |
+                        (u[3] << 20) | (u[5] << 24) | (u[7] << 28);
+  q[t] = word;
+  if ((t & 15) == 0) s[t / 16] = s16;
+}
+
+// out[n][c] = q[n][c] * s[n][c/128] in fp32 (exact), decoding with the same
+// unpack8() the FFN kernels use.
+__global__ __launch_bounds__(256) void dequant_kernel(const uint32_t *__restrict__ q,
+                                                      const f16 *__restrict__ s,
+                                                      int64_t rows, int64_t cols,
+                                                      float *__restrict__ out) {
+  const int64_t words_per_row = cols / 8;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= rows * words_per_row) return;
+  const float sc = (float)s[t / 16];
+  const f16x8 c = unpack8(q[t]);
+  f32x4 a = {(float)c[0] * sc, (float)c[1] * sc, (float)c[2] * sc, (float)c[3] * sc};
+  f32x4 b = {(float)c[4] * sc, (float)c[5] * sc, (float)c[6] * sc, (float)c[7] * sc};
+  f32x4 *o = reinterpret_cast<f32x4 *>(out + t * 8);
+  o[0] = a;
+  o[1] = b;
+}
+
+hipError_t launch_quantize(const uint16_t *w, int64_t rows, int64_t cols, uint8_t *q,
+                           uint16_t *s, hipStream_t st) {
+  const int64_t total = rows * (cols / 8);
+  const int64_t blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
+                     reinterpret_cast<const f16 *>(w), rows, cols,
+                     reinterpret_cast<uint32_t *>(q), reinterpret_cast<f16 *>(s));
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const uint8_t *q, const uint16_t *s, int64_t rows, int64_t cols,
+                          float *out, hipStream_t st) {
+  const int64_t total = rows * (cols / 8);
+  const int64_t blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
+                     reinterpret_cast<const uint32_t *>(q), reinterpret_cast<const f16 *>(s),
+                     rows, cols, out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,128 @@
+"""Device-resident W4 MoE layer: weights, preallocated buffers, one forward.
+
+PyTorch provides device memory and streams only; every step of the layer
+runs in the HIP kernels behind the four C entry points, called in order on
+one stream with no host synchronization in between.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import _native as N
+
+
+def _u16(t: torch.Tensor) -> torch.Tensor:
+    assert t.dtype in (torch.float16, torch.uint16, torch.int16), t.dtype
+    return t
+
+
+@dataclass
+class MoEBuffers:
+    """Outputs and workspace of one layer forward for up to `max_tokens` tokens."""
+    max_tokens: int
+    topk_idx: torch.Tensor      # int32 [T, k]
+    topk_w: torch.Tensor        # fp32 [T, k]
+    offsets: torch.Tensor       # int32 [E+1]
+    perm_src: torch.Tensor      # int32 [T*k]
+    inv_pos: torch.Tensor       # int32 [T*k]
+    x_perm: torch.Tensor        # fp16 [T*k, H]
+    y_perm: torch.Tensor        # fp16 [T*k, H]
+    y_shared: torch.Tensor      # fp16 [T, H] (empty when no shared expert)
+    out: torch.Tensor           # fp16 [T, H]
+    ws: torch.Tensor            # uint8 workspace
+
+
+class W4MoELayer:
+    """One MoE layer whose routed experts are int4 g128 and whose optional
+    shared expert is fp16.  All tensors live on one GPU.
+
+    router_w fp16 [E,H], router_b fp32 [E] or None,
+    gate_q/up_q uint8 [E,F,H/2], gate_s/up_s fp16 [E,F,H/128],
+    down_q uint8 [E,H,F/2], down_s fp16 [E,H,F/128],
+    shared = None or (Wg fp16 [Fs,H], Wu fp16 [Fs,H], Wd fp16 [H,Fs]).
+    """
+
+    def __init__(self, top_k, router_w, router_b, gate_q, gate_s, up_q, up_s, down_q, down_s,
+                 shared=None):
+        E, H = router_w.shape
+        F = gate_q.shape[1]
+        self.E, self.H, self.F, self.k = E, H, F, top_k
+        self.Fs = shared[0].shape[0] if shared is not None else 0
+        self.tensors = (router_w, router_b, gate_q, gate_s, up_q, up_s, down_q, down_s, shared)
+        sg, su, sd = shared if shared is not None else (None, None, None)
+        self.desc = N.make_layer(E, H, F, top_k, router_w, router_b, gate_q, gate_s, up_q, up_s,
+                                 down_q, down_s, self.Fs, sg, su, sd)
+
+    @property
+    def device(self):
+        return self.tensors[0].device
+
+    def workspace_size(self, max_tokens: int) -> int:
+        return N.moe_workspace_size(self.desc, max_tokens)
+
+    def alloc(self, max_tokens: int) -> MoEBuffers:
+        d, T, k, H, E = self.device, max_tokens, self.k, self.H, self.E
+        i32, f16 = torch.int32, torch.float16
+        return MoEBuffers(
+            max_tokens=T,
+            topk_idx=torch.empty((T, k), dtype=i32, device=d),
+            topk_w=torch.empty((T, k), dtype=torch.float32, device=d),
+            offsets=torch.empty((E + 1,), dtype=i32, device=d),
+            perm_src=torch.empty((T * k,), dtype=i32, device=d),
+            inv_pos=torch.empty((T * k,), dtype=i32, device=d),
+            x_perm=torch.empty((T * k, H), dtype=f16, device=d),
+            y_perm=torch.empty((T * k, H), dtype=f16, device=d),
+            y_shared=torch.empty((T if self.Fs else 0, H), dtype=f16, device=d),
+            out=torch.empty((T, H), dtype=f16, device=d),
+            ws=torch.empty((max(self.workspace_size(T), 256),), dtype=torch.uint8, device=d),
+        )
+
+    # the four stages, each one C call
+    def route(self, x, buf, T, stream=None):
+        N.moe_route(self.desc, x, T, buf.topk_idx, buf.topk_w, buf.ws, buf.ws.numel(), stream)
+
+    def permute(self, x, buf, T, stream=None):
+        N.moe_permute(self.desc, x, buf.topk_idx, T, buf.offsets, buf.perm_src, buf.inv_pos,
+                      buf.x_perm, buf.ws, buf.ws.numel(), stream)
+
+    def ffn(self, x, buf, T, stream=None):
+        N.moe_w4_grouped_ffn(self.desc, buf.x_perm, buf.offsets, x if self.Fs else None, T,
+                             buf.y_perm, buf.y_shared if self.Fs else None, buf.ws,
+                             buf.ws.numel(), stream)
+
+    def combine(self, buf, T, rmsnorm=False, eps=1e-6, out=None, stream=None):
+        N.moe_unpermute_combine(self.desc, buf.y_perm, buf.y_shared if self.Fs else None,
+                                buf.inv_pos, buf.topk_w, T, N.MOE_RMSNORM if rmsnorm else 0,
+                                eps, buf.out if out is None else out, stream)
+
+    def forward(self, x, buf, T=None, rmsnorm=False, eps=1e-6, out=None, stream=None):
+        """x fp16 [T, H] on the device -> buf.out (or `out`) fp16 [T, H]."""
+        T = x.shape[0] if T is None else T
+        if T > buf.max_tokens:
+            raise ValueError("more tokens than the buffers were allocated for")
+        self.route(x, buf, T, stream)
+        self.permute(x, buf, T, stream)
+        self.ffn(x, buf, T, stream)
+        self.combine(buf, T, rmsnorm, eps, out, stream)
+        return buf.out[:T] if out is None else out
+
+
+def quantize_fp16(w: torch.Tensor, stream=None):
+    """Group-quantize an fp16 device matrix [rows, cols] with the HIP kernel.
+
+    Returns (packed uint8 [rows, cols/2], scales fp16 [rows, cols/128])."""
+    rows, cols = w.shape
+    q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=w.device)
+    s = torch.empty((rows, cols // 128), dtype=torch.float16, device=w.device)
+    N.moe_w4_quantize(w, rows, cols, q, s, stream)
+    return q, s
+
+
+def dequantize(q: torch.Tensor, s: torch.Tensor, stream=None):
+    """Exact fp32 dequantization of one packed matrix (the test hook)."""
+    rows, half = q.shape
+    out = torch.empty((rows, half * 2), dtype=torch.float32, device=q.device)
+    N.moe_w4_dequant(q, s, rows, half * 2, out, stream)
+    return out
