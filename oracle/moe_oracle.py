@@ -19,9 +19,16 @@ are silent or garbled are stated in the docstrings; the same list, with the
 reasons, is kept in the design notes at the repository root.
 
 Packed int4 storage (a format of this library, not of the pages, which keep
-int8 codes): row-major [out, in/2] bytes; byte j of a row holds column 2j in
-bits 0-3 and column 2j+1 in bits 4-7, each stored as the unsigned nibble
-u = q + 8 (offset binary, 0..15).  Scales are fp16, row-major [out, in/128].
+int8 codes): row-major [out, in/2] bytes.  Each code is stored as the
+unsigned nibble u = q + 8 (offset binary, 0..15).  Every run of 8 columns
+8w..8w+7 of a row fills the 4 bytes 4w..4w+3 as
+
+    byte 4w+0 = u[8w+0] | u[8w+2] << 4      byte 4w+2 = u[8w+1] | u[8w+3] << 4
+    byte 4w+1 = u[8w+4] | u[8w+6] << 4      byte 4w+3 = u[8w+5] | u[8w+7] << 4
+
+i.e. read as a little-endian 32-bit word, nibble p (bits 4p..4p+3) holds
+column 8w + (0, 2, 4, 6, 1, 3, 5, 7)[p].  Scales are fp16, row-major
+[out, in/128].
 """
 from __future__ import annotations
 
@@ -84,22 +91,34 @@ def group_quantize(w16: np.ndarray, group: int = GROUP):
             s.reshape(out_dim, in_dim // group).astype(np.float16))
 
 
+# column offset (within a run of 8) held by the low / high nibble of byte b
+_LO_COL = (0, 4, 1, 5)
+_HI_COL = (2, 6, 3, 7)
+
+
 def pack_w4(q: np.ndarray) -> np.ndarray:
-    """int8 codes [out, in] in [-8, 7] -> packed bytes [out, in/2] (offset binary)."""
+    """int8 codes [out, in] in [-8, 7] -> packed bytes [out, in/2]."""
     q = np.asarray(q)
     if q.min(initial=0) < QMIN or q.max(initial=0) > QHI:
         raise ValueError("codes outside [-8, 7]")
-    u = (q.astype(np.int16) + 8).astype(np.uint8)
-    return (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+    if q.shape[1] % 8:
+        raise ValueError("in_features must be a multiple of 8")
+    u = (q.astype(np.int16) + 8).astype(np.uint8).reshape(q.shape[0], -1, 8)
+    out = np.empty((q.shape[0], q.shape[1] // 8, 4), dtype=np.uint8)
+    for b in range(4):
+        out[:, :, b] = u[:, :, _LO_COL[b]] | (u[:, :, _HI_COL[b]] << 4)
+    return out.reshape(q.shape[0], q.shape[1] // 2)
 
 
 def unpack_w4(packed: np.ndarray) -> np.ndarray:
     """Packed bytes [out, in/2] -> int8 codes [out, in]."""
     p = np.asarray(packed, dtype=np.uint8)
-    out = np.empty((p.shape[0], p.shape[1] * 2), dtype=np.int8)
-    out[:, 0::2] = (p & 0x0F).astype(np.int8) - 8
-    out[:, 1::2] = (p >> 4).astype(np.int8) - 8
-    return out
+    p = p.reshape(p.shape[0], -1, 4)
+    u = np.empty((p.shape[0], p.shape[1], 8), dtype=np.int8)
+    for b in range(4):
+        u[:, :, _LO_COL[b]] = (p[:, :, b] & 0x0F).astype(np.int8)
+        u[:, :, _HI_COL[b]] = (p[:, :, b] >> 4).astype(np.int8)
+    return (u - 8).reshape(p.shape[0], -1)
 
 
 def dequant(packed: np.ndarray, s: np.ndarray, group: int = GROUP) -> np.ndarray:
