@@ -1,0 +1,101 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before launching
+anything (so none of these calls touches a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_w4.h")
+
+N = pytest.importorskip("w4_group_quantized_amd._native",
+                        reason="libmoe_w4.so not built (python -m w4_group_quantized_amd.build)")
+
+OK, EINVAL, EUNSUP, EWS = 0, -1, -2, -3
+FAKE = 1 << 20          # a 16-byte aligned non-null address that is never dereferenced
+MISALIGNED = FAKE + 4
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_function_is_exported():
+    names = declared_functions()
+    assert set(names) == set(N.EXPORTS), names
+    for n in names:
+        assert hasattr(N.lib, n), n
+
+
+def layer(**kw):
+    d = dict(num_experts=8, hidden=256, ffn=512, top_k=2, router_w=FAKE, router_b=None,
+             gate_q=FAKE, gate_s=FAKE, up_q=FAKE, up_s=FAKE, down_q=FAKE, down_s=FAKE)
+    d.update(kw)
+    return N.make_layer(**d)
+
+
+def route(L, x=FAKE, T=4, idx=FAKE, w=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return N.lib.moe_route(ctypes.byref(L), x, T, idx, w, ws, ws_bytes, None)
+
+
+def test_workspace_size_and_invalid_layers():
+    L = layer()
+    assert N.moe_workspace_size(L, 16) > 0
+    assert N.moe_workspace_size(L, 0) >= 0
+    assert N.moe_workspace_size(layer(hidden=200), 16) == 0
+    assert N.moe_workspace_size(L, -1) == 0
+    assert N.moe_workspace_size(L, 32) >= N.moe_workspace_size(L, 16)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(group_size=64), EUNSUP),
+    (dict(hidden=200), EUNSUP),
+    (dict(ffn=100), EUNSUP),
+    (dict(top_k=9), EUNSUP),
+    (dict(top_k=0), EUNSUP),
+    (dict(num_experts=2000), EUNSUP),
+])
+def test_route_rejects_unsupported_layers(kw, status):
+    assert route(layer(**kw)) == status
+
+
+def test_route_argument_errors():
+    L = layer()
+    assert route(L, T=-1) == EINVAL
+    assert route(L, x=None) == EINVAL
+    assert route(L, x=MISALIGNED) == EINVAL
+    assert route(layer(router_w=None)) == EINVAL
+    assert route(L, ws_bytes=16) == EWS
+    assert route(L, T=0, x=None, idx=None, w=None, ws=None, ws_bytes=0) == OK   # no-op
+
+
+def test_other_calls_argument_errors():
+    L = layer()
+    big = 1 << 30
+    assert N.lib.moe_permute(ctypes.byref(L), FAKE, None, 4, FAKE, FAKE, FAKE, FAKE, FAKE, big,
+                             None) == EINVAL
+    assert N.lib.moe_permute(ctypes.byref(L), FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, FAKE, 8,
+                             None) == EWS
+    assert N.lib.moe_w4_grouped_ffn(ctypes.byref(layer(down_q=None)), FAKE, FAKE, FAKE, 4, FAKE,
+                                    None, FAKE, big, None) == EINVAL
+    Ls = layer(shared_ffn=256)       # shared expert declared but its weights missing
+    assert N.lib.moe_w4_grouped_ffn(ctypes.byref(Ls), FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, big,
+                                    None) == EINVAL
+    assert N.lib.moe_unpermute_combine(ctypes.byref(L), FAKE, None, FAKE, FAKE, 4, 2, 1e-6, FAKE,
+                                       None) == EINVAL                      # unknown flag
+    assert N.lib.moe_unpermute_combine(ctypes.byref(L), FAKE, None, FAKE, FAKE, 4, 1, -1.0,
+                                       FAKE, None) == EINVAL                # negative eps
+    assert N.lib.moe_w4_dequant(FAKE, FAKE, 4, 100, FAKE, None) == EUNSUP
+    assert N.lib.moe_w4_quantize(FAKE, 4, 256, None, FAKE, None) == EINVAL
+    assert N.lib.moe_w4_quantize(FAKE, -4, 256, FAKE, FAKE, None) == EINVAL
+    assert N.lib.moe_w4_quantize(None, 0, 256, None, None, None) == OK     # empty: no-op
+
+
+def test_status_strings():
+    for s in (OK, EINVAL, EUNSUP, EWS, -4):
+        assert N.moe_status_str(s)
+    assert "unknown" in N.moe_status_str(-99)

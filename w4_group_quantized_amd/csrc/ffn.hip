@@ -55,11 +55,15 @@ __device__ bool locate_tile(const int32_t *__restrict__ off, int E, int slot, in
   __shared__ int s_scan[4];
   __shared__ int s_res[2];
   const int tid = threadIdx.x;
+  // five independent loads with clamped (in-bounds) indices, then the counts
+  int o[5];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) o[i] = off[min(4 * tid + i, E)];
   int c[4], sum = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = 4 * tid + i;
-    c[i] = e < E ? (off[e + 1] - off[e] + kTileM - 1) / kTileM : 0;
+    c[i] = e < E ? (o[i + 1] - o[i] + kTileM - 1) / kTileM : 0;
     sum += c[i];
   }
   int total;
@@ -82,7 +86,7 @@ __device__ bool locate_tile(const int32_t *__restrict__ off, int E, int slot, in
 
 // PHASE 1: PAIR = gate and up tiles per wave, SwiGLU epilogue.
 // PHASE 2: one matrix, plain epilogue.
-template <int PHASE, int NT>
+template <int PHASE, int NT, int S>
 __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
   constexpr bool kPair = PHASE == 1;
   constexpr int kMats = kPair ? 2 : 1;
@@ -103,7 +107,8 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
     // offsets come from device memory: keep every row inside [0, N)
     if (seg0 < 0 || seg0 >= p.N) return;
     const int rows = min(min(kTileM, p.offsets[e + 1] - seg0), p.N - seg0);
-    const f16 *arow = r < rows ? p.a_routed + (size_t)(seg0 + r) * K : nullptr;
+    // token rows past the tile read a duplicate row; their outputs are dropped
+    const f16 *arow = p.a_routed + (size_t)(seg0 + min(r, rows - 1)) * K;
     const uint8_t *qrow[kMats * NT];
     const f16 *srow[kMats * NT];
     int nrow[NT];
@@ -121,7 +126,7 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
     f32x4 acc[kMats * NT];
 #pragma unroll
     for (int t = 0; t < kMats * NT; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    w4_tiles<kMats * NT>(arow, qrow, srow, kb, 0, G, acc);
+    w4_tiles<kMats * NT, S>(arow, qrow, srow, kb, 0, G, acc);
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -145,7 +150,7 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
   const int tok0 = mt * kTileM;
   if (tok0 >= p.T) return;
   const int rows = min(kTileM, p.T - tok0);
-  const f16 *arow = r < rows ? p.a_shared + (size_t)(tok0 + r) * Ks : nullptr;
+  const f16 *arow = p.a_shared + (size_t)(tok0 + min(r, rows - 1)) * Ks;
   const int nrow = nt * 16 + r;
   const f16 *wrow[kMats];
   wrow[0] = p.w0 + (size_t)nrow * Ks;
@@ -169,6 +174,8 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
 
 constexpr int kNT1 = 1;   // phase 1: 64 gate rows + 64 up rows per block
 constexpr int kNT2 = 2;   // phase 2: 128 down rows per block
+constexpr int kS1 = 1;    // groups per pipeline stage, phase 1
+constexpr int kS2 = 1;    // groups per pipeline stage, phase 2
 
 hipError_t launch_ffn(const moe_layer &L, const uint16_t *x_perm, const int32_t *offsets,
                       const uint16_t *x, int32_t T, uint16_t *y_perm, uint16_t *y_shared,
@@ -196,7 +203,7 @@ hipError_t launch_ffn(const moe_layer &L, const uint16_t *x_perm, const int32_t 
   a.out_shared = reinterpret_cast<f16 *>(h_shared);
   a.routed_items = max_tiles * (F / (64 * kNT1));
   int shared_items = Fs ? mtiles_shared * (Fs / 16) : 0;
-  hipLaunchKernelGGL((ffn_decode_kernel<1, kNT1>), dim3(a.routed_items + shared_items),
+  hipLaunchKernelGGL((ffn_decode_kernel<1, kNT1, kS1>), dim3(a.routed_items + shared_items),
                      dim3(256), 0, st, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -211,7 +218,7 @@ hipError_t launch_ffn(const moe_layer &L, const uint16_t *x_perm, const int32_t 
   a.out_shared = reinterpret_cast<f16 *>(y_shared);
   a.routed_items = max_tiles * (H / (64 * kNT2));
   shared_items = Fs ? mtiles_shared * (H / 16) : 0;
-  hipLaunchKernelGGL((ffn_decode_kernel<2, kNT2>), dim3(a.routed_items + shared_items),
+  hipLaunchKernelGGL((ffn_decode_kernel<2, kNT2, kS2>), dim3(a.routed_items + shared_items),
                      dim3(256), 0, st, a);
   return hipGetLastError();
 }

@@ -29,7 +29,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const f16 *__restric
   const int mt = blockIdx.x / etiles, et = blockIdx.x % etiles;
   const int tok0 = mt * 16;
   const int rows = min(16, T - tok0);
-  const f16 *arow = r < rows ? x + (size_t)(tok0 + r) * H : nullptr;
+  const f16 *arow = x + (size_t)(tok0 + min(r, rows - 1)) * H;   // surplus rows: duplicates, dropped
   const int e = et * 16 + r;
   const f16 *wrow[1] = {wr + (size_t)min(e, E - 1) * H};
   f32x4 acc[1] = {{0.f, 0.f, 0.f, 0.f}};

@@ -8,89 +8,147 @@
 // one 16-byte load and its activations four 16-byte loads.  The accumulator
 // lane l receives D[4*kb + j][l % 16], j = 0..3: tokens 4*kb + j of weight row
 // l % 16, so each lane applies a single group scale per tile.
+//
+// The K loop is software-pipelined by hand: two register stages (ping-pong)
+// of S quantization groups each; the loads of one stage are in flight while
+// the other is unpacked and multiplied.  Scheduling barriers keep the
+// compiler from sinking the prefetch loads next to their uses.
 #pragma once
 
 #include "common.h"
 
 namespace moe {
 
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// One pipeline stage of the int4 path: S groups of activations, weights and
+// scales for NT weight tiles.
+template <int NT, int S>
+struct W4Stage {
+  u32x4 x[S][4];
+  u32x4 q[S][NT];
+  f16 s[S][NT];
+};
+
+template <int NT, int S>
+__device__ __forceinline__ void w4_load(W4Stage<NT, S> &st, const f16 *__restrict__ arow,
+                                        const uint8_t *const (&qrow)[NT],
+                                        const f16 *const (&srow)[NT], int kb, int g, int G) {
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+    const int gg = min(g + i, G - 1);   // past the end: reload the last group (never used)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      st.q[i][t] = ld16(qrow[t] + (size_t)gg * (kGroup / 2) + kb * 16);
+      st.s[i][t] = srow[t][gg];
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      st.x[i][m] = ld16(arow + (size_t)gg * kGroup + kb * 32 + m * 8);
+  }
+}
+
+template <int NT, int S>
+__device__ __forceinline__ void w4_compute(const W4Stage<NT, S> &st, int ngroups,
+                                           f32x4 (&acc)[NT]) {
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+    if (i < ngroups) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          tmp = mfma_16x16x32(as_f16x8(st.x[i][m]), unpack8(st.q[i][t][m]), tmp);
+        const float s = (float)st.s[i][t];
+        acc[t] += s * tmp;
+      }
+    }
+  }
+}
+
 // int4 weights: acc[t] += sum_g scale[t][g] * sum_{k in g} A[tok][k] * q[t][k]
-// for g in [g0, g1).  arow: this lane's activation row (nullptr -> zeros);
-// qrow[t]: this lane's packed weight row of tile t; srow[t]: its scales.
-template <int NT>
+// for g in [g0, g1).  arow: this lane's activation row (always a valid row;
+// lanes whose token is past the tile read a duplicate row and their output
+// rows are discarded); qrow[t]: this lane's packed weight row of tile t;
+// srow[t]: its scales.  The loop body has no control flow, so the two stages
+// stay in fixed registers and only the stage about to be used is waited for.
+template <int NT, int S>
 __device__ __forceinline__ void w4_tiles(const f16 *__restrict__ arow,
                                          const uint8_t *const (&qrow)[NT],
                                          const f16 *const (&srow)[NT], int kb, int g0, int g1,
                                          f32x4 (&acc)[NT]) {
   if (g0 >= g1) return;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  u32x4 xa[4], wq[NT];
-  f16 sc[NT];
-  auto load = [&](int g, u32x4 (&x)[4], u32x4 (&q)[NT], f16 (&s)[NT]) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-      x[m] = arow ? ld16(arow + (size_t)g * kGroup + kb * 32 + m * 8) : zero;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      q[t] = ld16(qrow[t] + (size_t)g * (kGroup / 2) + kb * 16);
-      s[t] = srow[t][g];
-    }
-  };
-  load(g0, xa, wq, sc);
-  for (int g = g0; g < g1; ++g) {
-    u32x4 xn[4], qn[NT];
-    f16 sn[NT];
-    load(g + 1 < g1 ? g + 1 : g, xn, qn, sn);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int m = 0; m < 4; ++m) tmp = mfma_16x16x32(as_f16x8(xa[m]), unpack8(wq[t][m]), tmp);
-      const float s = (float)sc[t];
-      acc[t] += s * tmp;
-    }
-#pragma unroll
-    for (int m = 0; m < 4; ++m) xa[m] = xn[m];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      wq[t] = qn[t];
-      sc[t] = sn[t];
+  W4Stage<NT, S> a, b;
+  w4_load<NT, S>(a, arow, qrow, srow, kb, g0, g1);
+  int g = g0;
+  for (; g + 2 * S <= g1; g += 2 * S) {
+    w4_load<NT, S>(b, arow, qrow, srow, kb, g + S, g1);
+    sched_fence();
+    w4_compute<NT, S>(a, S, acc);
+    sched_fence();
+    w4_load<NT, S>(a, arow, qrow, srow, kb, g + 2 * S, g1);
+    sched_fence();
+    w4_compute<NT, S>(b, S, acc);
+    sched_fence();
+  }
+  const int rest = g1 - g;          // 0 <= rest < 2S groups; stage a holds group g..
+  if (rest > 0) {
+    w4_compute<NT, S>(a, rest, acc);
+    if (rest > S) {
+      w4_load<NT, S>(b, arow, qrow, srow, kb, g + S, g1);
+      w4_compute<NT, S>(b, rest - S, acc);
     }
   }
 }
 
 // fp16 weights: acc[t] += sum_{k in groups [g0, g1)} A[tok][k] * W[t][k].
 template <int NT>
+struct F16Stage {
+  u32x4 x[4];
+  u32x4 w[NT][4];
+};
+
+template <int NT>
+__device__ __forceinline__ void f16_load(F16Stage<NT> &st, const f16 *__restrict__ arow,
+                                         const f16 *const (&wrow)[NT], int kb, int g, int G) {
+  const int gg = min(g, G - 1);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const size_t k = (size_t)gg * kGroup + kb * 32 + m * 8;
+    st.x[m] = ld16(arow + k);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) st.w[t][m] = ld16(wrow[t] + k);
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ void f16_compute(const F16Stage<NT> &st, f32x4 (&acc)[NT]) {
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[t] = mfma_16x16x32(as_f16x8(st.x[m]), as_f16x8(st.w[t][m]), acc[t]);
+}
+
+template <int NT>
 __device__ __forceinline__ void f16_tiles(const f16 *__restrict__ arow,
                                           const f16 *const (&wrow)[NT], int kb, int g0, int g1,
                                           f32x4 (&acc)[NT]) {
   if (g0 >= g1) return;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  u32x4 xa[4], wb[NT][4];
-  auto load = [&](int g, u32x4 (&x)[4], u32x4 (&w)[NT][4]) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const size_t k = (size_t)g * kGroup + kb * 32 + m * 8;
-      x[m] = arow ? ld16(arow + k) : zero;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) w[t][m] = ld16(wrow[t] + k);
-    }
-  };
-  load(g0, xa, wb);
-  for (int g = g0; g < g1; ++g) {
-    u32x4 xn[4], wn[NT][4];
-    load(g + 1 < g1 ? g + 1 : g, xn, wn);
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int m = 0; m < 4; ++m) acc[t] = mfma_16x16x32(as_f16x8(xa[m]), as_f16x8(wb[t][m]), acc[t]);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      xa[m] = xn[m];
-#pragma unroll
-      for (int t = 0; t < NT; ++t) wb[t][m] = wn[t][m];
-    }
+  F16Stage<NT> a, b;
+  f16_load<NT>(a, arow, wrow, kb, g0, g1);
+  int g = g0;
+  for (; g + 2 <= g1; g += 2) {
+    f16_load<NT>(b, arow, wrow, kb, g + 1, g1);
+    sched_fence();
+    f16_compute<NT>(a, acc);
+    sched_fence();
+    f16_load<NT>(a, arow, wrow, kb, g + 2, g1);
+    sched_fence();
+    f16_compute<NT>(b, acc);
+    sched_fence();
   }
+  if (g < g1) f16_compute<NT>(a, acc);
 }
 
 // Sum the accumulators of the 4 waves of a block (K split 4 ways) into wave 0,
