@@ -40,10 +40,17 @@
  *  - Two calls that share a workspace must not run concurrently.
  *
  * Packed int4 weight format (this library's choice; the page stores int8
- * codes): a matrix [out, in] is stored row-major as [out, in/2] bytes plus fp16
- * scales [out, in/128].  A code q in [-8, 7] is stored as the nibble u = q + 8.
- * Columns 8w..8w+7 of a row occupy bytes 4w..4w+3; read as a little-endian
- * 32-bit word, nibble p (bits 4p..4p+3) holds column 8w + {0,2,4,6,1,3,5,7}[p].
+ * codes).  A matrix [out, in] (out a multiple of 16, in a multiple of 128) is
+ * stored as out*in/2 bytes of codes plus out*in/128 fp16 scales.  A code q in
+ * [-8, 7] is the nibble u = q + 8.  Eight consecutive columns 8w..8w+7 of a
+ * row form one little-endian 32-bit word whose nibble p (bits 4p..4p+3) holds
+ * column 8w + {0,2,4,6,1,3,5,7}[p]; four words (32 columns) form a 16-byte
+ * chunk.  Rows are stored in tiles of 16, the 16 rows' chunks side by side,
+ * so the 16 rows x 128 columns of one quantization group are 1 KB contiguous
+ * (the weight layout is reordered for contiguous access, as
+ * dpshk.com/news/6309482 §3.2 recommends):
+ *     byte(row n, chunk c, b) = (n/16)*16*(in/2) + c*256 + (n%16)*16 + b
+ *     scale(row n, group g)   = (n/16)*16*(in/128) + g*16 + n%16
  * The dequantized weight is W[n][c] = q[n][c] * scale[n][c / 128].
  */
 #ifndef MOE_W4_H
@@ -74,8 +81,9 @@ typedef enum {
  *  router_w     fp16 [E, H]
  *  router_b     fp32 [E], or NULL for no bias (added to the logits before the
  *               softmax, so it also changes the combine weights)
- *  gate_q, up_q packed int4 [E, F, H/2];   gate_s, up_s  fp16 [E, F, H/128]
- *  down_q       packed int4 [E, H, F/2];   down_s        fp16 [E, H, F/128]
+ *  gate_q, up_q packed int4, E matrices [F, H] back to back (E*F*H/2 bytes);
+ *               gate_s, up_s their fp16 scales (E*F*H/128)
+ *  down_q       packed int4, E matrices [H, F] (E*H*F/2 bytes); down_s scales
  *  shared_ffn   Fs of the always-on shared expert, multiple of 128, or 0
  *  shared_gate, shared_up  fp16 [Fs, H];   shared_down   fp16 [H, Fs]
  */
@@ -164,21 +172,26 @@ moe_status moe_unpermute_combine(const moe_layer *layer, const uint16_t *y_perm,
                                  const float *topk_w, int32_t T, uint32_t flags,
                                  float eps, uint16_t *out, void *stream);
 
-/* Test hook: out[n][c] = q[n][c] * s[n][c/128] in fp32 (exact), for one packed
- * matrix q [rows, cols/2], s fp16 [rows, cols/128]; cols multiple of 128. */
+/* Test hook: out[n][c] = q[n][c] * s[n][c/128] in fp32 (exact, row-major
+ * [rows, cols]) for one matrix in the packed format above; rows multiple of
+ * 16, cols multiple of 128 (MOE_EUNSUPPORTED otherwise). */
 moe_status moe_w4_dequant(const uint8_t *q, const uint16_t *s, int64_t rows,
                           int64_t cols, float *out, void *stream);
 
 /* Group quantization of an fp16 matrix w [rows, cols] (cols multiple of 128),
  * lpnh.cn/news/2730718 §2.1 with every step rounded to fp16 as on an fp16
  * model: s = RN16(max|w_group| / 7), q = clamp(RNE(RN16(w / s)), -8, 7); an
- * all-zero group gets s = 0, q = 0.  Writes packed q [rows, cols/2] and fp16
- * s [rows, cols/128]. */
+ * all-zero group gets s = 0, q = 0.  w is row-major; writes q and s in the
+ * packed format above.  rows multiple of 16, cols multiple of 128. */
 moe_status moe_w4_quantize(const uint16_t *w, int64_t rows, int64_t cols,
                            uint8_t *q, uint16_t *s, void *stream);
 
 /* Static description of a status code (host). */
 const char *moe_status_str(moe_status status);
+
+/* Host: the HIP runtime's message for the error behind the last MOE_EHIP
+ * returned on the calling thread ("no HIP error" if there was none). */
+const char *moe_last_hip_error(void);
 
 #ifdef __cplusplus
 }

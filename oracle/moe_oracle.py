@@ -19,16 +19,22 @@ are silent or garbled are stated in the docstrings; the same list, with the
 reasons, is kept in the design notes at the repository root.
 
 Packed int4 storage (a format of this library, not of the pages, which keep
-int8 codes): row-major [out, in/2] bytes.  Each code is stored as the
-unsigned nibble u = q + 8 (offset binary, 0..15).  Every run of 8 columns
-8w..8w+7 of a row fills the 4 bytes 4w..4w+3 as
+int8 codes).  Each code is stored as the unsigned nibble u = q + 8 (offset
+binary, 0..15).  Eight consecutive columns 8w..8w+7 of a row form one 32-bit
+little-endian word whose nibble p (bits 4p..4p+3) holds column
+8w + (0, 2, 4, 6, 1, 3, 5, 7)[p]; four such words (32 columns) form a 16-byte
+chunk.  A matrix [out, in] (out a multiple of 16, in a multiple of 128) is
+stored tile by tile: 16 rows at a time, and inside a tile chunk by chunk with
+the 16 rows' chunks side by side:
 
-    byte 4w+0 = u[8w+0] | u[8w+2] << 4      byte 4w+2 = u[8w+1] | u[8w+3] << 4
-    byte 4w+1 = u[8w+4] | u[8w+6] << 4      byte 4w+3 = u[8w+5] | u[8w+7] << 4
+    byte offset(row n, chunk c, byte b) = (n // 16) * 16 * (in/2)
+                                          + c * 256 + (n % 16) * 16 + b
 
-i.e. read as a little-endian 32-bit word, nibble p (bits 4p..4p+3) holds
-column 8w + (0, 2, 4, 6, 1, 3, 5, 7)[p].  Scales are fp16, row-major
-[out, in/128].
+so the 16 rows x 128 columns of one quantization group are 1 KB contiguous.
+The fp16 scales [out, in/128] are stored the same way, 16 rows side by side:
+offset(row n, group g) = (n // 16) * 16 * (in/128) + g * 16 + n % 16.
+Both are kept as arrays of the logical shape [out, in/2] bytes and
+[out, in/128] fp16 whose memory follows these offsets.
 """
 from __future__ import annotations
 
@@ -96,23 +102,36 @@ _LO_COL = (0, 4, 1, 5)
 _HI_COL = (2, 6, 3, 7)
 
 
+def _rows_to_tiles(a: np.ndarray, unit: int) -> np.ndarray:
+    """Row-major [out, n*unit] -> tile order: 16 rows side by side per unit."""
+    out_dim, cols = a.shape
+    t = a.reshape(out_dim // 16, 16, cols // unit, unit).transpose(0, 2, 1, 3)
+    return np.ascontiguousarray(t).reshape(out_dim, cols)
+
+
+def _tiles_to_rows(a: np.ndarray, unit: int) -> np.ndarray:
+    out_dim, cols = a.shape
+    t = a.reshape(out_dim // 16, cols // unit, 16, unit).transpose(0, 2, 1, 3)
+    return np.ascontiguousarray(t).reshape(out_dim, cols)
+
+
 def pack_w4(q: np.ndarray) -> np.ndarray:
-    """int8 codes [out, in] in [-8, 7] -> packed bytes [out, in/2]."""
+    """int8 codes [out, in] in [-8, 7] -> stored bytes [out, in/2]."""
     q = np.asarray(q)
     if q.min(initial=0) < QMIN or q.max(initial=0) > QHI:
         raise ValueError("codes outside [-8, 7]")
-    if q.shape[1] % 8:
-        raise ValueError("in_features must be a multiple of 8")
+    if q.shape[0] % 16 or q.shape[1] % GROUP:
+        raise ValueError("out_features must be a multiple of 16, in_features of 128")
     u = (q.astype(np.int16) + 8).astype(np.uint8).reshape(q.shape[0], -1, 8)
-    out = np.empty((q.shape[0], q.shape[1] // 8, 4), dtype=np.uint8)
+    rows = np.empty((q.shape[0], q.shape[1] // 8, 4), dtype=np.uint8)
     for b in range(4):
-        out[:, :, b] = u[:, :, _LO_COL[b]] | (u[:, :, _HI_COL[b]] << 4)
-    return out.reshape(q.shape[0], q.shape[1] // 2)
+        rows[:, :, b] = u[:, :, _LO_COL[b]] | (u[:, :, _HI_COL[b]] << 4)
+    return _rows_to_tiles(rows.reshape(q.shape[0], q.shape[1] // 2), 16)
 
 
 def unpack_w4(packed: np.ndarray) -> np.ndarray:
-    """Packed bytes [out, in/2] -> int8 codes [out, in]."""
-    p = np.asarray(packed, dtype=np.uint8)
+    """Stored bytes [out, in/2] -> int8 codes [out, in]."""
+    p = _tiles_to_rows(np.asarray(packed, dtype=np.uint8), 16)
     p = p.reshape(p.shape[0], -1, 4)
     u = np.empty((p.shape[0], p.shape[1], 8), dtype=np.int8)
     for b in range(4):
@@ -121,11 +140,20 @@ def unpack_w4(packed: np.ndarray) -> np.ndarray:
     return (u - 8).reshape(p.shape[0], -1)
 
 
-def dequant(packed: np.ndarray, s: np.ndarray, group: int = GROUP) -> np.ndarray:
-    """W[n, c] = q[n, c] * s[n, c // group], in float64 (exact: an int4 code
-    times an fp16 scale needs at most 4 + 11 significant bits)."""
+def pack_scales(s: np.ndarray) -> np.ndarray:
+    """fp16 scales [out, in/128] -> stored order (16 rows side by side)."""
+    return _rows_to_tiles(np.asarray(s, dtype=np.float16), 1)
+
+
+def unpack_scales(stored: np.ndarray) -> np.ndarray:
+    return _tiles_to_rows(np.asarray(stored, dtype=np.float16), 1)
+
+
+def dequant(packed: np.ndarray, s_stored: np.ndarray, group: int = GROUP) -> np.ndarray:
+    """W[n, c] = q[n, c] * s[n, c // group] in float64, from the stored arrays
+    (exact: an int4 code times an fp16 scale needs at most 4 + 11 bits)."""
     q = unpack_w4(packed).astype(np.float64)
-    s64 = np.asarray(s, dtype=np.float64)
+    s64 = unpack_scales(s_stored).astype(np.float64)
     return q * np.repeat(s64, group, axis=1)
 
 

@@ -55,10 +55,10 @@ def quantized_experts(cfg, layer=0, experts=None):
         tup = []
         for m, name in ((G.GATE, "gate"), (G.UP, "up"), (G.DOWN, "down")):
             q, s = O.group_quantize(G.expert_master(cfg, layer, e, m))
-            p = O.pack_w4(q)
+            p, ss = O.pack_w4(q), O.pack_scales(s)
             mats[name + "_q"].append(p)
-            mats[name + "_s"].append(s)
-            tup += [p, s]
+            mats[name + "_s"].append(ss)
+            tup += [p, ss]
         per_expert.append(tuple(tup))
     return {k: np.stack(v) for k, v in mats.items()}, per_expert
 

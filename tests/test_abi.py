@@ -11,7 +11,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe_w4.h")
 
 N = pytest.importorskip("w4_group_quantized_amd._native",
-                        reason="libmoe_w4.so not built (python -m w4_group_quantized_amd.build)")
+                        reason="libmoe_w4.so not built (python w4_group_quantized_amd/build.py)")
 
 OK, EINVAL, EUNSUP, EWS = 0, -1, -2, -3
 FAKE = 1 << 20          # a 16-byte aligned non-null address that is never dereferenced
@@ -90,8 +90,9 @@ def test_other_calls_argument_errors():
     assert N.lib.moe_unpermute_combine(ctypes.byref(L), FAKE, None, FAKE, FAKE, 4, 1, -1.0,
                                        FAKE, None) == EINVAL                # negative eps
     assert N.lib.moe_w4_dequant(FAKE, FAKE, 4, 100, FAKE, None) == EUNSUP
-    assert N.lib.moe_w4_quantize(FAKE, 4, 256, None, FAKE, None) == EINVAL
-    assert N.lib.moe_w4_quantize(FAKE, -4, 256, FAKE, FAKE, None) == EINVAL
+    assert N.lib.moe_w4_quantize(FAKE, 16, 256, None, FAKE, None) == EINVAL
+    assert N.lib.moe_w4_quantize(FAKE, -16, 256, FAKE, FAKE, None) == EINVAL
+    assert N.lib.moe_w4_quantize(FAKE, 8, 256, FAKE, FAKE, None) == EUNSUP        # rows % 16
     assert N.lib.moe_w4_quantize(None, 0, 256, None, None, None) == OK     # empty: no-op
 
 

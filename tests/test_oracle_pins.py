@@ -96,7 +96,7 @@ def test_quantizer_invariants():
     nz = s.astype(np.float64) > 0
     assert (qa[nz] == 7).all()
     assert (qa[~nz] == 0).all() and not nz[5, 1]
-    err = np.abs(w.astype(np.float64) - O.dequant(O.pack_w4(q), s))
+    err = np.abs(w.astype(np.float64) - O.dequant(O.pack_w4(q), O.pack_scales(s)))
     bound = (0.5 + 2.0 ** -9) * np.repeat(s.astype(np.float64), 128, axis=1)
     assert (err <= bound).all()
 
@@ -108,31 +108,44 @@ def test_quantizer_refuses_ragged_in_features():
 
 # ---------------------------------------------------------------- packing / dequant
 def test_pack_layout_exhaustive():
-    """Every byte value at every byte position of a 32-bit word, against the
-    documented table: byte 0 -> columns (0, 2), byte 1 -> (4, 6),
-    byte 2 -> (1, 3), byte 3 -> (5, 7) as (low, high) nibble; value = nibble - 8."""
+    """Every byte value at many storage offsets of a [32, 256] matrix, against
+    the documented layout: offset(row n, chunk c, byte b) = (n//16)*16*128 +
+    c*256 + (n%16)*16 + b; byte b holds, as (low, high) nibble, columns
+    32c + 8*(b//4) + {0:(0,2), 1:(4,6), 2:(1,3), 3:(5,7)}[b%4]; value = nibble-8."""
     table = {0: (0, 2), 1: (4, 6), 2: (1, 3), 3: (5, 7)}
-    packed = np.zeros((256, 64), dtype=np.uint8)
+    rows, cols = 32, 256
+    rng = np.random.default_rng(12)
     for v in range(256):
-        for pos in range(4):
-            packed[v, 4 * pos + pos] = v       # word `pos`, byte `pos`
-    q = O.unpack_w4(packed)
-    for v in range(256):
-        for pos in range(4):
-            lo, hi = table[pos]
-            assert q[v, 8 * pos + lo] == (v & 15) - 8
-            assert q[v, 8 * pos + hi] == (v >> 4) - 8
-            others = [c for c in range(8) if c not in (lo, hi)]
-            assert (q[v, 8 * pos + np.array(others)] == -8).all()
-    np.testing.assert_array_equal(O.pack_w4(q), packed)
+        n, c, b = int(rng.integers(rows)), int(rng.integers(cols // 32)), int(rng.integers(16))
+        flat = np.zeros(rows * cols // 2, dtype=np.uint8)
+        flat[(n // 16) * 16 * (cols // 2) + c * 256 + (n % 16) * 16 + b] = v
+        q = O.unpack_w4(flat.reshape(rows, cols // 2))
+        lo, hi = table[b % 4]
+        base = 32 * c + 8 * (b // 4)
+        expect = np.full((rows, cols), -8, dtype=np.int8)
+        expect[n, base + lo] = (v & 15) - 8
+        expect[n, base + hi] = (v >> 4) - 8
+        np.testing.assert_array_equal(q, expect)
+        np.testing.assert_array_equal(O.pack_w4(q).reshape(-1), flat)
+
+
+def test_scale_layout():
+    """offset(row n, group g) = (n//16)*16*G + g*16 + n%16."""
+    rows, G = 32, 3
+    s = (np.arange(rows * G, dtype=np.float64).reshape(rows, G) + 1).astype(np.float16)
+    st = O.pack_scales(s).reshape(-1)
+    for n in range(rows):
+        for g in range(G):
+            assert st[(n // 16) * 16 * G + g * 16 + n % 16] == s[n, g]
+    np.testing.assert_array_equal(O.unpack_scales(O.pack_scales(s)), s)
 
 
 def test_dequant_exact():
     g = np.random.default_rng(3)
-    q = g.integers(-8, 8, size=(4, 256)).astype(np.int8)
-    s = (g.uniform(1e-3, 1e-2, size=(4, 2))).astype(np.float16)
-    W = O.dequant(O.pack_w4(q), s)
-    for n in range(4):
+    q = g.integers(-8, 8, size=(16, 256)).astype(np.int8)
+    s = (g.uniform(1e-3, 1e-2, size=(16, 2))).astype(np.float16)
+    W = O.dequant(O.pack_w4(q), O.pack_scales(s))
+    for n in range(16):
         for c in range(0, 256, 7):
             assert Fraction(W[n, c]) == int(q[n, c]) * Fraction(float(s[n, c // 128]))
     # q*s is exact in fp32 as well (4 + 11 significant bits)
@@ -262,7 +275,7 @@ def _tiny_layer(cfg, layer=0):
         mats = []
         for m in (G.GATE, G.UP, G.DOWN):
             q, s = O.group_quantize(G.expert_master(cfg, layer, e, m))
-            mats += [O.pack_w4(q), s]
+            mats += [O.pack_w4(q), O.pack_scales(s)]
         experts.append(tuple(mats))
     return x, wr, b, experts
 

@@ -16,15 +16,21 @@ LIB_PATH = os.path.join(_PKG, "libmoe_w4.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m w4_group_quantized_amd.build` "
+        f"{LIB_PATH} is missing: build it with `python w4_group_quantized_amd/build.py` "
         "(there is no fallback implementation)")
+
+# torch bundles its own HIP runtime (same soname as /opt/rocm's).  Whichever
+# copy is loaded first serves the whole process, so load torch's before this
+# library pulls in the system one: torch allocates every buffer we are given.
+import torch  # noqa: E402,F401
 
 lib = ctypes.CDLL(LIB_PATH)
 
 MOE_RMSNORM = 1
 
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_w4_grouped_ffn",
-           "moe_unpermute_combine", "moe_w4_dequant", "moe_w4_quantize", "moe_status_str")
+           "moe_unpermute_combine", "moe_w4_dequant", "moe_w4_quantize", "moe_status_str",
+           "moe_last_hip_error")
 
 
 class MoeLayer(ctypes.Structure):
@@ -66,6 +72,7 @@ _sigs = {
     "moe_w4_dequant": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P]),
     "moe_w4_quantize": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
     "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_last_hip_error": (ctypes.c_char_p, []),
 }
 for _name, (_res, _args) in _sigs.items():
     _f = getattr(lib, _name)
@@ -76,8 +83,10 @@ for _name, (_res, _args) in _sigs.items():
 class MoeError(RuntimeError):
     def __init__(self, fn: str, status: int):
         self.status = status
-        super().__init__(f"{fn} failed: status {status} "
-                         f"({lib.moe_status_str(status).decode()})")
+        msg = f"{fn} failed: status {status} ({lib.moe_status_str(status).decode()})"
+        if status == -4:
+            msg += f": {lib.moe_last_hip_error().decode()}"
+        super().__init__(msg)
 
 
 def _ptr(t):

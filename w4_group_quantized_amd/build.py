@@ -1,6 +1,9 @@
 """Build libmoe_w4.so (HIP for gfx950) in-tree with hipcc.
 
-    python -m w4_group_quantized_amd.build
+    python w4_group_quantized_amd/build.py
+
+(run by path, not with -m: importing the package would load the library
+that is about to be replaced).
 
 Every source is compiled for gfx950 only.  Packed fp32 vector instructions are
 turned off for the device code (their scalar forms are used instead).

@@ -27,6 +27,21 @@ __device__ __forceinline__ f16x2 as_f16x2(uint32_t v) { return __builtin_bit_cas
 __device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
 __device__ __forceinline__ uint32_t as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 
+// Register-resident constants for the unpack.  GFX9 VOP3 encodings take no
+// literal constants, so with literal masks the compiler emits AND + OR; with
+// the masks in SGPRs and the fp16 1024.0 pair in a VGPR (made opaque by an
+// empty asm so they are not folded back into literals) it selects one
+// v_and_or_b32 per pair.
+struct UnpackConsts {
+  uint32_t lo, hi, magic;
+};
+__device__ __forceinline__ UnpackConsts unpack_consts() {
+  UnpackConsts c{0x000F000Fu, 0x00F000F0u, 0x64006400u};
+  asm volatile("" : "+s"(c.lo), "+s"(c.hi));
+  asm volatile("" : "+v"(c.magic));
+  return c;
+}
+
 // Eight int4 codes of one 32-bit word of the packed format -> eight fp16
 // codes q = u - 8 in column order.  Nibble p of the word holds column
 // {0,2,4,6,1,3,5,7}[p], so masking bits 0-3 and 16-19 yields columns (0,1),
@@ -35,16 +50,16 @@ __device__ __forceinline__ uint32_t as_u32(f16x2 v) { return __builtin_bit_cast(
 // 1024.0 (0x6400) gives 1024 + u exactly (fp16 spacing is 1 on [1024, 2048));
 // a nibble sitting 4 bits higher gives 1024 + 16u.  One subtraction, or one
 // fused multiply-add by 1/16, then leaves the exact small integer u - 8.
-__device__ __forceinline__ f16x8 unpack8(uint32_t w) {
-  const uint32_t kMagic = 0x64006400u;
+// Cost: 1 shift + 4 AND-OR + 4 packed fp16 ops per 8 weights.
+__device__ __forceinline__ f16x8 unpack8(uint32_t w, const UnpackConsts &k) {
   const f16x2 k1032 = {(f16)-1032.0f, (f16)-1032.0f};
   const f16x2 k16th = {(f16)0.0625f, (f16)0.0625f};
   const f16x2 k72 = {(f16)-72.0f, (f16)-72.0f};
   const uint32_t w8 = w >> 8;
-  f16x2 c01 = as_f16x2((w & 0x000F000Fu) | kMagic) + k1032;
-  f16x2 c23 = __builtin_elementwise_fma(as_f16x2((w & 0x00F000F0u) | kMagic), k16th, k72);
-  f16x2 c45 = as_f16x2((w8 & 0x000F000Fu) | kMagic) + k1032;
-  f16x2 c67 = __builtin_elementwise_fma(as_f16x2((w8 & 0x00F000F0u) | kMagic), k16th, k72);
+  f16x2 c01 = as_f16x2((w & k.lo) | k.magic) + k1032;
+  f16x2 c23 = __builtin_elementwise_fma(as_f16x2((w & k.hi) | k.magic), k16th, k72);
+  f16x2 c45 = as_f16x2((w8 & k.lo) | k.magic) + k1032;
+  f16x2 c67 = __builtin_elementwise_fma(as_f16x2((w8 & k.hi) | k.magic), k16th, k72);
   u32x4 r = {as_u32(c01), as_u32(c23), as_u32(c45), as_u32(c67)};
   return as_f16x8(r);
 }

@@ -115,12 +115,12 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       nrow[t] = nt * 64 * NT + (wid * NT + t) * 16 + r;
-      const size_t row = (size_t)e * Nrows + nrow[t];
-      qrow[t] = p.q0 + row * (K / 2);
-      srow[t] = p.s0 + row * G;
+      const size_t row0 = (size_t)e * Nrows + (nrow[t] - r);      // first row of the tile
+      qrow[t] = p.q0 + row0 * (K / 2) + lane * 16;
+      srow[t] = p.s0 + row0 * G + r;
       if (kPair) {
-        qrow[NT + t] = p.q1 + row * (K / 2);
-        srow[NT + t] = p.s1 + row * G;
+        qrow[NT + t] = p.q1 + row0 * (K / 2) + lane * 16;
+        srow[NT + t] = p.s1 + row0 * G + r;
       }
     }
     f32x4 acc[kMats * NT];

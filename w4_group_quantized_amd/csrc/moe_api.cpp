@@ -59,7 +59,18 @@ static moe_status check_ws(const moe_layer *L, int32_t T, const void *ws, size_t
   return MOE_OK;
 }
 
-static inline moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+// The HIP error behind the last MOE_EHIP returned on this thread.
+static thread_local hipError_t g_last_hip_error = hipSuccess;
+
+static inline moe_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  g_last_hip_error = e;
+  return MOE_EHIP;
+}
+
+// Errors left behind by earlier HIP calls of other code on this thread must
+// not be reported as ours: clear them before launching.
+static inline void clear_stale_hip_error() { (void)hipGetLastError(); }
 
 }  // namespace moe
 
@@ -84,6 +95,7 @@ moe_status moe_route(const moe_layer *L, const uint16_t *x, int32_t T, int32_t *
   if ((s = check_ws(L, T, ws, ws_bytes)) != MOE_OK) return s;
   const WsLayout w = ws_layout(*L, T);
   float *logits = reinterpret_cast<float *>(static_cast<char *>(ws) + w.logits);
+  clear_stale_hip_error();
   return hip_status(launch_route(*L, x, T, topk_idx, topk_w, logits, (hipStream_t)stream));
 }
 
@@ -100,6 +112,7 @@ moe_status moe_permute(const moe_layer *L, const uint16_t *x, const int32_t *top
   if ((s = check_ws(L, T, ws, ws_bytes)) != MOE_OK) return s;
   const WsLayout w = ws_layout(*L, T);
   char *base = static_cast<char *>(ws);
+  clear_stale_hip_error();
   return hip_status(launch_permute(*L, x, topk_idx, T, offsets, perm_src, inv_pos, x_perm,
                                    reinterpret_cast<int32_t *>(base + w.counts),
                                    reinterpret_cast<int32_t *>(base + w.bases),
@@ -123,6 +136,7 @@ moe_status moe_w4_grouped_ffn(const moe_layer *L, const uint16_t *x_perm, const 
   if ((s = check_ws(L, T, ws, ws_bytes)) != MOE_OK) return s;
   const WsLayout w = ws_layout(*L, T);
   char *base = static_cast<char *>(ws);
+  clear_stale_hip_error();
   return hip_status(launch_ffn(*L, x_perm, offsets, x, T, y_perm,
                                L->shared_ffn > 0 ? y_shared : nullptr,
                                reinterpret_cast<uint16_t *>(base + w.h),
@@ -142,6 +156,7 @@ moe_status moe_unpermute_combine(const moe_layer *L, const uint16_t *y_perm,
   if (y_shared && !aligned16(y_shared)) return MOE_EINVAL;
   if (flags & ~MOE_RMSNORM) return MOE_EINVAL;
   if ((flags & MOE_RMSNORM) && !(eps >= 0.0f)) return MOE_EINVAL;
+  clear_stale_hip_error();
   return hip_status(launch_combine(*L, y_perm, y_shared, inv_pos, topk_w, T, flags, eps, out,
                                    (hipStream_t)stream));
 }
@@ -149,21 +164,27 @@ moe_status moe_unpermute_combine(const moe_layer *L, const uint16_t *y_perm,
 moe_status moe_w4_dequant(const uint8_t *q, const uint16_t *s, int64_t rows, int64_t cols,
                           float *out, void *stream) {
   if (rows < 0 || cols < 0) return MOE_EINVAL;
-  if (cols % 128) return MOE_EUNSUPPORTED;
+  if (cols % 128 || rows % 16) return MOE_EUNSUPPORTED;
   if (rows == 0 || cols == 0) return MOE_OK;
   if ((rows * (cols / 8) + 255) / 256 > 0x7fffffffLL) return MOE_EUNSUPPORTED;
   if (!ok_ptr(q) || !ok_ptr(s) || !ok_ptr(out)) return MOE_EINVAL;
+  clear_stale_hip_error();
   return hip_status(launch_dequant(q, s, rows, cols, out, (hipStream_t)stream));
 }
 
 moe_status moe_w4_quantize(const uint16_t *w, int64_t rows, int64_t cols, uint8_t *q, uint16_t *s,
                            void *stream) {
   if (rows < 0 || cols < 0) return MOE_EINVAL;
-  if (cols % 128) return MOE_EUNSUPPORTED;
+  if (cols % 128 || rows % 16) return MOE_EUNSUPPORTED;
   if (rows == 0 || cols == 0) return MOE_OK;
   if ((rows * (cols / 8) + 255) / 256 > 0x7fffffffLL) return MOE_EUNSUPPORTED;
   if (!ok_ptr(w) || !ok_ptr(q) || !ok_ptr(s)) return MOE_EINVAL;
+  clear_stale_hip_error();
   return hip_status(launch_quantize(w, rows, cols, q, s, (hipStream_t)stream));
+}
+
+const char *moe_last_hip_error(void) {
+  return g_last_hip_error == hipSuccess ? "no HIP error" : hipGetErrorString(g_last_hip_error);
 }
 
 const char *moe_status_str(moe_status status) {

@@ -12,11 +12,23 @@
 
 namespace moe {
 
+// Stored layout (see the packed-weight format in moe_w4.h): 16 rows side by
+// side per 16-byte chunk of 32 columns, so one group of a 16-row tile is 1 KB
+// contiguous; scales likewise 16 rows side by side per group.
+__device__ __forceinline__ size_t word_offset(int64_t row, int64_t word, int64_t cols) {
+  // word = 8-column word index within the row; 4 words per 16-byte chunk
+  return (size_t)(row >> 4) * 16 * (cols / 2) + (size_t)(word >> 2) * 256 +
+         (size_t)(row & 15) * 16 + (size_t)(word & 3) * 4;
+}
+__device__ __forceinline__ size_t scale_offset(int64_t row, int64_t g, int64_t cols) {
+  return (size_t)(row >> 4) * 16 * (cols / 128) + (size_t)g * 16 + (size_t)(row & 15);
+}
+
 // One thread per 8 consecutive columns (one 32-bit packed word); 16 threads
-// cover one 128-column group, a wave covers 4 groups.
+// cover one 128-column group, a wave covers 4 groups of one row.
 __global__ __launch_bounds__(256) void quantize_kernel(const f16 *__restrict__ w,
                                                        int64_t rows, int64_t cols,
-                                                       uint32_t *__restrict__ q,
+                                                       uint8_t *__restrict__ q,
                                                        f16 *__restrict__ s) {
   const int64_t words_per_row = cols / 8;
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -24,10 +36,10 @@ __global__ __launch_bounds__(256) void quantize_kernel(const f16 *__restrict__ w
   // Lanes past the end still take part in the 16-lane max so that the
   // shuffles see a full group; they load nothing and store nothing.
   const bool live = t < total;
+  const int64_t row = live ? t / words_per_row : 0, word = live ? t % words_per_row : 0;
   float v[8];
   float m = 0.0f;
   if (live) {
-    const int64_t row = t / words_per_row, word = t % words_per_row;
     u32x4 raw = ld16(w + row * cols + word * 8);
     f16x8 h = as_f16x8(raw);
 #pragma unroll
@@ -52,26 +64,31 @@ __global__ __launch_bounds__(256) void quantize_kernel(const f16 *__restrict__ w
     u[i] = (uint32_t)((int)qi + 8);
   }
   // nibble p holds column {0,2,4,6,1,3,5,7}[p]
-  const uint32_t word = u[0] | (u[2] << 4) | (u[4] << 8) | (u[6] << 12) | (u[1] << 16) |
-                        (u[3] << 20) | (u[5] << 24) | (u[7] << 28);
-  q[t] = word;
-  if ((t & 15) == 0) s[t / 16] = s16;
+  const uint32_t packed = u[0] | (u[2] << 4) | (u[4] << 8) | (u[6] << 12) | (u[1] << 16) |
+                          (u[3] << 20) | (u[5] << 24) | (u[7] << 28);
+  *reinterpret_cast<uint32_t *>(q + word_offset(row, word, cols)) = packed;
+  if ((word & 15) == 0) s[scale_offset(row, word / 16, cols)] = s16;
 }
 
 // out[n][c] = q[n][c] * s[n][c/128] in fp32 (exact), decoding with the same
-// unpack8() the FFN kernels use.
+// unpack8() the FFN kernels use.  One thread per stored 32-bit word.
 __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t *__restrict__ q,
                                                       const f16 *__restrict__ s,
                                                       int64_t rows, int64_t cols,
                                                       float *__restrict__ out) {
-  const int64_t words_per_row = cols / 8;
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= rows * words_per_row) return;
-  const float sc = (float)s[t / 16];
-  const f16x8 c = unpack8(q[t]);
+  if (t >= rows * (cols / 8)) return;
+  const int64_t byte = t * 4;
+  const int64_t tile_bytes = 16 * (cols / 2);
+  const int64_t tile = byte / tile_bytes, rem = byte % tile_bytes;
+  const int64_t chunk = rem / 256, r = (rem % 256) / 16, word_in_chunk = (rem % 16) / 4;
+  const int64_t row = tile * 16 + r;
+  const int64_t col = chunk * 32 + word_in_chunk * 8;
+  const float sc = (float)s[scale_offset(row, col / 128, cols)];
+  const f16x8 c = unpack8(q[t], unpack_consts());
   f32x4 a = {(float)c[0] * sc, (float)c[1] * sc, (float)c[2] * sc, (float)c[3] * sc};
   f32x4 b = {(float)c[4] * sc, (float)c[5] * sc, (float)c[6] * sc, (float)c[7] * sc};
-  f32x4 *o = reinterpret_cast<f32x4 *>(out + t * 8);
+  f32x4 *o = reinterpret_cast<f32x4 *>(out + row * cols + col);
   o[0] = a;
   o[1] = b;
 }
@@ -81,8 +98,7 @@ hipError_t launch_quantize(const uint16_t *w, int64_t rows, int64_t cols, uint8_
   const int64_t total = rows * (cols / 8);
   const int64_t blocks = (total + 255) / 256;
   hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
-                     reinterpret_cast<const f16 *>(w), rows, cols,
-                     reinterpret_cast<uint32_t *>(q), reinterpret_cast<f16 *>(s));
+                     reinterpret_cast<const f16 *>(w), rows, cols, q, reinterpret_cast<f16 *>(s));
   return hipGetLastError();
 }
 

@@ -39,8 +39,8 @@ __device__ __forceinline__ void w4_load(W4Stage<NT, S> &st, const f16 *__restric
     const int gg = min(g + i, G - 1);   // past the end: reload the last group (never used)
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      st.q[i][t] = ld16(qrow[t] + (size_t)gg * (kGroup / 2) + kb * 16);
-      st.s[i][t] = srow[t][gg];
+      st.q[i][t] = ld16(qrow[t] + (size_t)gg * 1024);
+      st.s[i][t] = srow[t][(size_t)gg * 16];
     }
 #pragma unroll
     for (int m = 0; m < 4; ++m)
@@ -49,7 +49,7 @@ __device__ __forceinline__ void w4_load(W4Stage<NT, S> &st, const f16 *__restric
 }
 
 template <int NT, int S>
-__device__ __forceinline__ void w4_compute(const W4Stage<NT, S> &st, int ngroups,
+__device__ __forceinline__ void w4_compute(const W4Stage<NT, S> &st, int ngroups, const UnpackConsts &magic,
                                            f32x4 (&acc)[NT]) {
 #pragma unroll
   for (int i = 0; i < S; ++i) {
@@ -59,7 +59,7 @@ __device__ __forceinline__ void w4_compute(const W4Stage<NT, S> &st, int ngroups
         f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < 4; ++m)
-          tmp = mfma_16x16x32(as_f16x8(st.x[i][m]), unpack8(st.q[i][t][m]), tmp);
+          tmp = mfma_16x16x32(as_f16x8(st.x[i][m]), unpack8(st.q[i][t][m], magic), tmp);
         const float s = (float)st.s[i][t];
         acc[t] += s * tmp;
       }
@@ -70,8 +70,9 @@ __device__ __forceinline__ void w4_compute(const W4Stage<NT, S> &st, int ngroups
 // int4 weights: acc[t] += sum_g scale[t][g] * sum_{k in g} A[tok][k] * q[t][k]
 // for g in [g0, g1).  arow: this lane's activation row (always a valid row;
 // lanes whose token is past the tile read a duplicate row and their output
-// rows are discarded); qrow[t]: this lane's packed weight row of tile t;
-// srow[t]: its scales.  The loop body has no control flow, so the two stages
+// rows are discarded); qrow[t]: base of weight tile t (16 rows) + lane*16
+// bytes, so group g is at qrow[t] + g*1024; srow[t]: the tile's scales + r,
+// group g at srow[t][g*16].  The loop body has no control flow, so the two stages
 // stay in fixed registers and only the stage about to be used is waited for.
 template <int NT, int S>
 __device__ __forceinline__ void w4_tiles(const f16 *__restrict__ arow,
@@ -79,25 +80,26 @@ __device__ __forceinline__ void w4_tiles(const f16 *__restrict__ arow,
                                          const f16 *const (&srow)[NT], int kb, int g0, int g1,
                                          f32x4 (&acc)[NT]) {
   if (g0 >= g1) return;
+  const UnpackConsts magic = unpack_consts();
   W4Stage<NT, S> a, b;
   w4_load<NT, S>(a, arow, qrow, srow, kb, g0, g1);
   int g = g0;
   for (; g + 2 * S <= g1; g += 2 * S) {
     w4_load<NT, S>(b, arow, qrow, srow, kb, g + S, g1);
     sched_fence();
-    w4_compute<NT, S>(a, S, acc);
+    w4_compute<NT, S>(a, S, magic, acc);
     sched_fence();
     w4_load<NT, S>(a, arow, qrow, srow, kb, g + 2 * S, g1);
     sched_fence();
-    w4_compute<NT, S>(b, S, acc);
+    w4_compute<NT, S>(b, S, magic, acc);
     sched_fence();
   }
   const int rest = g1 - g;          // 0 <= rest < 2S groups; stage a holds group g..
   if (rest > 0) {
-    w4_compute<NT, S>(a, rest, acc);
+    w4_compute<NT, S>(a, rest, magic, acc);
     if (rest > S) {
       w4_load<NT, S>(b, arow, qrow, srow, kb, g + S, g1);
-      w4_compute<NT, S>(b, rest - S, acc);
+      w4_compute<NT, S>(b, rest - S, magic, acc);
     }
   }
 }
