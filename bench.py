@@ -2,8 +2,9 @@
 
     python bench.py [--steps K] [--warmup W] [--workload decode_fine]
 
-A step is one full layer forward (route -> permute -> grouped W4 FFN ->
-combine) over one batch of synthetic tokens already resident in HBM.  Several
+A step is one full layer forward (route + permute -> grouped W4 FFN ->
+combine, through the C entry points) over one batch of synthetic tokens
+already resident in HBM.  Several
 independently drawn weight sets are rotated so that no expert byte is served
 from the 256 MB Infinity Cache across steps.  Prints ONE JSON line.
 
@@ -191,8 +192,7 @@ def main():
         x = xs[(i // n_sets) % args.batches]
         for li, layer in enumerate(layers):
             last = li == len(layers) - 1
-            layer.route(x, bufs, T)
-            layer.permute(x, bufs, T)
+            layer.route_permute(x, bufs, T)
             if ev_pair is not None and li == 0:
                 ev_pair[0].record(stream)
             layer.ffn(x, bufs, T)
@@ -212,8 +212,7 @@ def main():
     for c in range(n_combo):
         layer = sets[c % n_sets][0]
         x = xs[(c // n_sets) % args.batches]
-        layer.route(x, bufs, T)
-        layer.permute(x, bufs, T)
+        layer.route_permute(x, bufs, T)
         torch.cuda.synchronize()
         cnt = np.diff(bufs.offsets.cpu().numpy())
         U = int((cnt > 0).sum())

@@ -37,7 +37,9 @@
  *  - Arguments are checked on the host before anything is launched; a failed
  *    check launches nothing and returns a negative moe_status.  T = 0 returns
  *    MOE_OK and launches nothing.
- *  - Two calls that share a workspace must not run concurrently.
+ *  - Two calls that share a workspace must not run concurrently.  Zero-fill a
+ *    workspace once before its first use: it holds a synchronization counter
+ *    that every call leaves at zero.
  *
  * Packed int4 weight format (this library's choice; the page stores int8
  * codes).  A matrix [out, in] (out a multiple of 16, in a multiple of 128) is
@@ -127,12 +129,14 @@ moe_status moe_route(const moe_layer *layer, const uint16_t *x, int32_t T,
 /* Permutation of the T*k (token, slot) pairs into per-expert segments.
  * Flat index f = t*k + j; segment e holds the f with topk_idx[f] = e in
  * increasing f.
- *   x         fp16 [T, H]
+ *   x         fp16 [T, H] (read only when x_perm is not NULL)
  *   topk_idx  int32 [T, k], each in [0, E)
  *   offsets   int32 [E+1] out: segment e is rows offsets[e]..offsets[e+1]-1
  *   perm_src  int32 [T*k] out: flat index f of permuted row r
  *   inv_pos   int32 [T*k] out: permuted row of flat index f
- *   x_perm    fp16 [T*k, H] out: x_perm[r] = x[perm_src[r] / k] (bit copy)
+ *   x_perm    fp16 [T*k, H] out: x_perm[r] = x[perm_src[r] / k] (bit copy),
+ *             or NULL to skip the copy (moe_w4_grouped_ffn can read the rows
+ *             of x through perm_src)
  * Indices outside [0, E) are clamped into range on the device so no access
  * leaves the buffers; such input is a caller error and gives unspecified
  * (but in-bounds) segments. */
@@ -141,21 +145,33 @@ moe_status moe_permute(const moe_layer *layer, const uint16_t *x,
                        int32_t *offsets, int32_t *perm_src, int32_t *inv_pos,
                        uint16_t *x_perm, void *ws, size_t ws_bytes, void *stream);
 
+/* moe_route followed by moe_permute, same arguments and outputs as the two
+ * calls.  For T <= 64 and T*E <= 8192 both run in one launch: the last router block to finish
+ * (a device-wide counter in the workspace) runs the softmax, top-k and the
+ * permutation, so the workspace must be zero-filled before its first use
+ * (every call leaves that counter at zero again). */
+moe_status moe_route_permute(const moe_layer *layer, const uint16_t *x, int32_t T,
+                             int32_t *topk_idx, float *topk_w, int32_t *offsets,
+                             int32_t *perm_src, int32_t *inv_pos, uint16_t *x_perm,
+                             void *ws, size_t ws_bytes, void *stream);
+
 /* Grouped SwiGLU FFN over the routed segments and the shared expert.
- * For each expert e and each row r of its segment:
- *   g = deq(gate_e) x_perm[r],  u = deq(up_e) x_perm[r]   (fp32 accumulation)
+ * For each expert e and each row r of its segment, with a = x_perm[r], or
+ * a = x[perm_src[r] / k] when x_perm is NULL:
+ *   g = deq(gate_e) a,  u = deq(up_e) a          (fp32 accumulation)
  *   h = silu(g) * u  with silu(z) = z / (1 + exp(-z)), stored as fp16
- *   y_perm[r] = deq(down_e) h                              (fp32 accumulation)
+ *   y_perm[r] = deq(down_e) h                    (fp32 accumulation)
  * and, when the layer has a shared expert, the same with its fp16 weights for
  * every token of x, into y_shared.
- *   x_perm    fp16 [T*k, H]    offsets int32 [E+1] (as written by moe_permute;
- *             offsets[0] = 0, non-decreasing, offsets[E] = T*k)
- *   x         fp16 [T, H]      (read only for the shared expert; may be NULL
- *             when shared_ffn = 0)
+ *   x         fp16 [T, H]   (needed when x_perm is NULL or shared_ffn > 0)
+ *   x_perm    fp16 [T*k, H] or NULL;  perm_src int32 [T*k] (needed when
+ *             x_perm is NULL);  offsets int32 [E+1] as written by moe_permute
+ *             (offsets[0] = 0, non-decreasing, offsets[E] = T*k)
  *   y_perm    fp16 [T*k, H] out
  *   y_shared  fp16 [T, H] out, or NULL when shared_ffn = 0 */
-moe_status moe_w4_grouped_ffn(const moe_layer *layer, const uint16_t *x_perm,
-                              const int32_t *offsets, const uint16_t *x, int32_t T,
+moe_status moe_w4_grouped_ffn(const moe_layer *layer, const uint16_t *x,
+                              const uint16_t *x_perm, const int32_t *perm_src,
+                              const int32_t *offsets, int32_t T,
                               uint16_t *y_perm, uint16_t *y_shared,
                               void *ws, size_t ws_bytes, void *stream);
 

@@ -80,11 +80,26 @@ def test_other_calls_argument_errors():
                              None) == EINVAL
     assert N.lib.moe_permute(ctypes.byref(L), FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, FAKE, 8,
                              None) == EWS
-    assert N.lib.moe_w4_grouped_ffn(ctypes.byref(layer(down_q=None)), FAKE, FAKE, FAKE, 4, FAKE,
-                                    None, FAKE, big, None) == EINVAL
+    ffn = N.lib.moe_w4_grouped_ffn
+    # (layer, x, x_perm, perm_src, offsets, T, y_perm, y_shared, ws, ws_bytes, stream)
+    assert ffn(ctypes.byref(layer(down_q=None)), FAKE, FAKE, FAKE, FAKE, 4, FAKE, None, FAKE, big,
+               None) == EINVAL
+    assert ffn(ctypes.byref(L), FAKE, None, None, FAKE, 4, FAKE, None, FAKE, big,
+               None) == EINVAL                        # no x_perm and no perm_src
+    assert ffn(ctypes.byref(L), None, None, FAKE, FAKE, 4, FAKE, None, FAKE, big,
+               None) == EINVAL                        # no x_perm and no x
     Ls = layer(shared_ffn=256)       # shared expert declared but its weights missing
-    assert N.lib.moe_w4_grouped_ffn(ctypes.byref(Ls), FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, big,
-                                    None) == EINVAL
+    assert ffn(ctypes.byref(Ls), FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, big,
+               None) == EINVAL
+    rp = N.lib.moe_route_permute
+    # (layer, x, T, idx, w, offsets, perm_src, inv_pos, x_perm, ws, ws_bytes, stream)
+    assert rp(ctypes.byref(L), FAKE, 4, FAKE, FAKE, None, FAKE, FAKE, None, FAKE, big,
+              None) == EINVAL
+    assert rp(ctypes.byref(L), FAKE, 4, FAKE, FAKE, FAKE, FAKE, FAKE, MISALIGNED, FAKE, big,
+              None) == EINVAL
+    assert rp(ctypes.byref(L), FAKE, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 64,
+              None) == EWS
+    assert rp(ctypes.byref(L), None, 0, None, None, None, None, None, None, None, 0, None) == OK
     assert N.lib.moe_unpermute_combine(ctypes.byref(L), FAKE, None, FAKE, FAKE, 4, 2, 1e-6, FAKE,
                                        None) == EINVAL                      # unknown flag
     assert N.lib.moe_unpermute_combine(ctypes.byref(L), FAKE, None, FAKE, FAKE, 4, 1, -1.0,

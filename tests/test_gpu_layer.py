@@ -23,7 +23,7 @@ def _np(t):
     return t.detach().cpu().numpy()
 
 
-def run_layer_case(cfg, T, batch=0):
+def run_layer_case(cfg, T, batch=0, separate_calls=False):
     mats, experts = quantized_experts(cfg)
     wr, b = G.router(cfg)
     shared = G.shared_expert(cfg)
@@ -31,7 +31,15 @@ def run_layer_case(cfg, T, batch=0):
     ref = O.moe_layer(x, wr, b, experts, cfg.top_k, shared=shared)
     layer = make_gpu_layer(cfg, mats, wr, b, shared)
     buf = layer.alloc(T)
-    out = layer.forward(to_dev(x), buf)
+    xd = to_dev(x)
+    if separate_calls:       # the four calls of the boundary, x_perm materialised
+        layer.route(xd, buf, T)
+        layer.permute(xd, buf, T, gather=True)
+        layer.ffn(xd, buf, T, use_x_perm=True)
+        layer.combine(buf, T)
+        out = buf.out
+    else:
+        out = layer.forward(xd, buf)
     torch.cuda.synchronize()
     diff = route_compare(_np(buf.topk_idx), ref["idx"], ref["logits"], cfg.top_k)
     if not diff.any():
@@ -43,9 +51,10 @@ def run_layer_case(cfg, T, batch=0):
     return layer, buf, x
 
 
-def test_tiny_layer_exact_config():
+@pytest.mark.parametrize("separate_calls", [False, True])
+def test_tiny_layer_exact_config(separate_calls):
     """8 experts, hidden 256, ffn 512, top-2, 16 tokens, seed 0."""
-    run_layer_case(get_config("tiny"), 16)
+    run_layer_case(get_config("tiny"), 16, separate_calls=separate_calls)
 
 
 @pytest.mark.parametrize("T", [1, 8, 13])
@@ -54,9 +63,10 @@ def test_fine_grained_shape_scaled_down(T):
     run_layer_case(cfg, T, batch=T)
 
 
-def test_prefill_like_ragged_segments():
+@pytest.mark.parametrize("separate_calls", [False, True])
+def test_prefill_like_ragged_segments(separate_calls):
     cfg = get_config("prefill", num_experts=16, hidden=256, ffn=384, top_k=4)
-    run_layer_case(cfg, 150)
+    run_layer_case(cfg, 150, separate_calls=separate_calls)
 
 
 def test_layer_is_deterministic():

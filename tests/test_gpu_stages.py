@@ -184,6 +184,34 @@ def test_permute_bitexact(T, k, E, kind):
     assert _np(buf.x_perm).tobytes() == xp_ref.tobytes()
 
 
+@pytest.mark.parametrize("name,over,T", [("tiny", {}, 16), ("decode_fine", {}, 8),
+                                         ("decode_fine", {}, 16), ("decode_fine", {}, 64),
+                                         ("decode_coarse", {}, 16), ("decode_fine", {}, 65),
+                                         ("prefill", {"tokens": 40}, 40)])
+def test_route_permute_fused(name, over, T):
+    """moe_route_permute (one launch for T <= 64) against the oracle: indices
+    exact away from near ties; offsets/perm_src/inv_pos exact when the indices
+    agree; called twice to check that the completion counter is reset."""
+    cfg = get_config(name, **over)
+    wr, b = G.router(cfg)
+    layer = _router_only_layer(cfg, wr, b)
+    buf = layer.alloc(T)
+    for rep in range(2):
+        x = G.activations(cfg, tokens=T, batch=20 + rep)
+        idx_ref, w_ref, l_ref = O.route(x, wr, b, cfg.top_k)
+        layer.route_permute(to_dev(x), buf, T, gather=True)
+        torch.cuda.synchronize()
+        idx = _np(buf.topk_idx)
+        diff = route_compare(idx, idx_ref, l_ref, cfg.top_k)
+        tol_check(_np(buf.topk_w)[~diff], w_ref[~diff], "topk_w", rel=1e-5, abs_=1e-7)
+        # the permutation must be the exact permutation of the GPU's own indices
+        off, perm_src, inv_pos = O.permute(idx, cfg.num_experts)
+        np.testing.assert_array_equal(_np(buf.offsets), off)
+        np.testing.assert_array_equal(_np(buf.perm_src), perm_src)
+        np.testing.assert_array_equal(_np(buf.inv_pos), inv_pos)
+        assert _np(buf.x_perm).tobytes() == O.gather_rows(x, perm_src, cfg.top_k).tobytes()
+
+
 # ---------------------------------------------------------------- FFN
 FFN_CASES = [
     ("tiny", {}, 16, 0),
@@ -193,8 +221,9 @@ FFN_CASES = [
 ]
 
 
+@pytest.mark.parametrize("use_x_perm", [False, True])
 @pytest.mark.parametrize("name,over,T,Fs", FFN_CASES)
-def test_ffn_teacher_forced(name, over, T, Fs):
+def test_ffn_teacher_forced(name, over, T, Fs, use_x_perm):
     cfg = get_config(name, shared_ffn=Fs, **over)
     mats, experts = quantized_experts(cfg)
     wr, b = G.router(cfg)
@@ -206,8 +235,13 @@ def test_ffn_teacher_forced(name, over, T, Fs):
     layer = make_gpu_layer(cfg, mats, wr, b, shared)
     buf = layer.alloc(T)
     buf.offsets.copy_(to_dev(off))
-    buf.x_perm.copy_(to_dev(x_perm))
-    layer.ffn(to_dev(x), buf, T)
+    if use_x_perm:
+        buf.x_perm.copy_(to_dev(x_perm))
+        buf.perm_src.fill_(-1)                    # must not be read
+    else:
+        buf.perm_src.copy_(to_dev(perm_src))
+        buf.x_perm.fill_(float("nan"))            # must not be read
+    layer.ffn(to_dev(x), buf, T, use_x_perm=use_x_perm)
     torch.cuda.synchronize()
     y_perm = _np(buf.y_perm)
     for e in range(cfg.num_experts):

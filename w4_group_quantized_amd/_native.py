@@ -28,7 +28,8 @@ lib = ctypes.CDLL(LIB_PATH)
 
 MOE_RMSNORM = 1
 
-EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_w4_grouped_ffn",
+EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_route_permute",
+           "moe_w4_grouped_ffn",
            "moe_unpermute_combine", "moe_w4_dequant", "moe_w4_quantize", "moe_status_str",
            "moe_last_hip_error")
 
@@ -66,7 +67,8 @@ _sigs = {
     "moe_workspace_size": (_SZ, [_LP, _I32]),
     "moe_route": (ctypes.c_int, [_LP, _P, _I32, _P, _P, _P, _SZ, _P]),
     "moe_permute": (ctypes.c_int, [_LP, _P, _P, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
-    "moe_w4_grouped_ffn": (ctypes.c_int, [_LP, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
+    "moe_route_permute": (ctypes.c_int, [_LP, _P, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_w4_grouped_ffn": (ctypes.c_int, [_LP, _P, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
     "moe_unpermute_combine": (ctypes.c_int, [_LP, _P, _P, _P, _P, _I32, ctypes.c_uint32,
                                              ctypes.c_float, _P, _P]),
     "moe_w4_dequant": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P]),
@@ -137,12 +139,20 @@ def moe_permute(layer, x, topk_idx, T, offsets, perm_src, inv_pos, x_perm, ws, w
                                           _ptr(x_perm), _ptr(ws), ws_bytes, _stream(stream)))
 
 
-def moe_w4_grouped_ffn(layer, x_perm, offsets, x, T, y_perm, y_shared, ws, ws_bytes,
+def moe_route_permute(layer, x, T, topk_idx, topk_w, offsets, perm_src, inv_pos, x_perm, ws,
+                      ws_bytes, stream=None):
+    _check("moe_route_permute",
+           lib.moe_route_permute(ctypes.byref(layer), _ptr(x), T, _ptr(topk_idx), _ptr(topk_w),
+                                 _ptr(offsets), _ptr(perm_src), _ptr(inv_pos), _ptr(x_perm),
+                                 _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_w4_grouped_ffn(layer, x, x_perm, perm_src, offsets, T, y_perm, y_shared, ws, ws_bytes,
                        stream=None):
     _check("moe_w4_grouped_ffn",
-           lib.moe_w4_grouped_ffn(ctypes.byref(layer), _ptr(x_perm), _ptr(offsets), _ptr(x), T,
-                                  _ptr(y_perm), _ptr(y_shared), _ptr(ws), ws_bytes,
-                                  _stream(stream)))
+           lib.moe_w4_grouped_ffn(ctypes.byref(layer), _ptr(x), _ptr(x_perm), _ptr(perm_src),
+                                  _ptr(offsets), T, _ptr(y_perm), _ptr(y_shared), _ptr(ws),
+                                  ws_bytes, _stream(stream)))
 
 
 def moe_unpermute_combine(layer, y_perm, y_shared, inv_pos, topk_w, T, flags, eps, out,

@@ -114,4 +114,90 @@ __device__ __forceinline__ int block_excl_scan(int v, int *scratch, int *total) 
   return wbase + incl - v;
 }
 
+// Routing key of one (logit, expert) candidate: the 64-bit maximum over a
+// wave picks the largest logit, ties to the lower expert index, NaN below
+// every number, and a key of 0 (empty or already chosen) below everything.
+// High word: the float's bits mapped to an unsigned order (-0 folded into +0,
+// NaN -> 0); low word: 1 << 16 | (0xFFFF - expert).
+__device__ __forceinline__ uint64_t route_key(float v, int e) {
+  v = v + 0.0f;                                   // -0 -> +0
+  uint32_t b = __float_as_uint(v);
+  uint32_t m = (v != v) ? 0u : ((b >> 31) ? ~b : (b | 0x80000000u));
+  return ((uint64_t)m << 32) | (1u << 16) | (uint32_t)(0xFFFF - e);
+}
+__device__ __forceinline__ int route_key_expert(uint64_t key) {
+  return 0xFFFF - (int)(key & 0xFFFFu);
+}
+// Cross-lane reductions on DPP row operations (no LDS round trips): within
+// each row of 16 lanes, exchange with lane^1, lane^2, the mirrored lane of the
+// half row and of the row; afterwards every lane of a row holds the row's
+// result.  The four row results are then combined on the scalar unit in row
+// order, so every lane gets the same, order-fixed result.
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;   // row_half_mirror
+constexpr int kDppMirror = 0x140;       // row_mirror
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL,
+                                                    0xF, 0xF, false));
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max_u64_step(uint64_t v) {
+  const uint32_t lo = dpp_u32<CTRL>((uint32_t)v), hi = dpp_u32<CTRL>((uint32_t)(v >> 32));
+  const uint64_t t = ((uint64_t)hi << 32) | lo;
+  return t > v ? t : v;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = dpp_max_u64_step<kDppXor1>(v);
+  v = dpp_max_u64_step<kDppXor2>(v);
+  v = dpp_max_u64_step<kDppHalfMirror>(v);
+  v = dpp_max_u64_step<kDppMirror>(v);
+  uint64_t r = 0;
+#pragma unroll
+  for (int row = 0; row < 4; ++row) {
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, row * 16);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), row * 16);
+    const uint64_t t = ((uint64_t)hi << 32) | lo;
+    r = t > r ? t : r;
+  }
+  return r;
+}
+
+// max that propagates NaN
+__device__ __forceinline__ float fmax_nan(float a, float b) {
+  return (a != a || b != b) ? __builtin_nanf("") : fmaxf(a, b);
+}
+
+__device__ __forceinline__ float wave_max_nan_dpp(float v) {
+  v = fmax_nan(v, dpp_f32<kDppXor1>(v));
+  v = fmax_nan(v, dpp_f32<kDppXor2>(v));
+  v = fmax_nan(v, dpp_f32<kDppHalfMirror>(v));
+  v = fmax_nan(v, dpp_f32<kDppMirror>(v));
+  float r = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+#pragma unroll
+  for (int row = 1; row < 4; ++row)
+    r = fmax_nan(r, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), row * 16)));
+  return r;
+}
+
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v = v + dpp_f32<kDppXor1>(v);
+  v = v + dpp_f32<kDppXor2>(v);
+  v = v + dpp_f32<kDppHalfMirror>(v);
+  v = v + dpp_f32<kDppMirror>(v);
+  float r = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+#pragma unroll
+  for (int row = 1; row < 4; ++row)
+    r = r + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), row * 16));
+  return r;
+}
+
 }  // namespace moe

@@ -33,9 +33,10 @@ namespace moe {
 constexpr int kTileM = 16;   // tokens per MFMA tile
 
 struct FfnArgs {
-  int E, H, F, Fs, T, N;            // N = T * k
+  int E, H, F, Fs, T, N, k;         // N = T * k
   const int32_t *offsets;           // [E+1]
-  const f16 *a_routed;              // phase 1: x_perm [N, H]; phase 2: h [N, F]
+  const int32_t *perm_src;          // phase 1 without x_perm: rows of x via perm_src[r] / k
+  const f16 *a_routed;              // phase 1: x_perm [N, H] or x [T, H]; phase 2: h [N, F]
   const f16 *a_shared;              // phase 1: x [T, H];      phase 2: h_shared [T, Fs]
   const uint8_t *q0, *q1;           // phase 1: gate_q, up_q;  phase 2: down_q, unused
   const f16 *s0, *s1;               // matching scales
@@ -108,7 +109,12 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
     if (seg0 < 0 || seg0 >= p.N) return;
     const int rows = min(min(kTileM, p.offsets[e + 1] - seg0), p.N - seg0);
     // token rows past the tile read a duplicate row; their outputs are dropped
-    const f16 *arow = p.a_routed + (size_t)(seg0 + min(r, rows - 1)) * K;
+    int arow_idx = seg0 + min(r, rows - 1);
+    if (p.perm_src) {            // gather straight from x: token of flat index perm_src[r]
+      arow_idx = p.perm_src[arow_idx] / p.k;
+      arow_idx = arow_idx < 0 ? 0 : (arow_idx >= p.T ? p.T - 1 : arow_idx);
+    }
+    const f16 *arow = p.a_routed + (size_t)arow_idx * K;
     const uint8_t *qrow[kMats * NT];
     const f16 *srow[kMats * NT];
     int nrow[NT];
@@ -177,9 +183,10 @@ constexpr int kNT2 = 2;   // phase 2: 128 down rows per block
 constexpr int kS1 = 1;    // groups per pipeline stage, phase 1
 constexpr int kS2 = 1;    // groups per pipeline stage, phase 2
 
-hipError_t launch_ffn(const moe_layer &L, const uint16_t *x_perm, const int32_t *offsets,
-                      const uint16_t *x, int32_t T, uint16_t *y_perm, uint16_t *y_shared,
-                      uint16_t *h, uint16_t *h_shared, hipStream_t st) {
+hipError_t launch_ffn(const moe_layer &L, const uint16_t *x, const uint16_t *x_perm,
+                      const int32_t *perm_src, const int32_t *offsets, int32_t T,
+                      uint16_t *y_perm, uint16_t *y_shared, uint16_t *h, uint16_t *h_shared,
+                      hipStream_t st) {
   const int E = L.num_experts, H = L.hidden, F = L.ffn, Fs = L.shared_ffn, k = L.top_k;
   const int N = T * k;
   // worst case number of 16-row segment tiles: every non-empty segment adds at
@@ -188,11 +195,12 @@ hipError_t launch_ffn(const moe_layer &L, const uint16_t *x_perm, const int32_t 
   const int mtiles_shared = (T + kTileM - 1) / kTileM;
 
   FfnArgs a{};
-  a.E = E; a.H = H; a.F = F; a.Fs = Fs; a.T = T; a.N = N;
+  a.E = E; a.H = H; a.F = F; a.Fs = Fs; a.T = T; a.N = N; a.k = k;
   a.offsets = offsets;
 
-  // phase 1
-  a.a_routed = reinterpret_cast<const f16 *>(x_perm);
+  // phase 1: token rows from x_perm, or from x through perm_src
+  a.perm_src = x_perm ? nullptr : perm_src;
+  a.a_routed = reinterpret_cast<const f16 *>(x_perm ? x_perm : x);
   a.a_shared = reinterpret_cast<const f16 *>(x);
   a.q0 = L.gate_q; a.q1 = L.up_q;
   a.s0 = reinterpret_cast<const f16 *>(L.gate_s);
@@ -209,6 +217,7 @@ hipError_t launch_ffn(const moe_layer &L, const uint16_t *x_perm, const int32_t 
   if (err != hipSuccess) return err;
 
   // phase 2
+  a.perm_src = nullptr;
   a.a_routed = reinterpret_cast<const f16 *>(h);
   a.a_shared = reinterpret_cast<const f16 *>(h_shared);
   a.q0 = L.down_q; a.q1 = nullptr;

@@ -11,10 +11,14 @@ namespace moe {
 
 constexpr int kPermChunk = 256;   // flat (token, slot) entries per permutation block
 constexpr int kGroupSize = 128;   // the only group size the kernels implement
+constexpr int kFusedMaxT = 64;    // route + permute in one launch up to this many tokens
+constexpr int kFusedMaxKsb = 16;  // K parts of the fused router's logits
+constexpr int kFusedMaxLogits = 8192;   // T * E held in LDS by the fused router
 
 // Byte offsets of the per-call scratch regions inside the caller's workspace.
 struct WsLayout {
-  size_t logits;    // fp32 [T, E]
+  size_t sync;      // uint32 counters; zero between calls
+  size_t logits;    // fp32 [T, E], or [kFusedMaxKsb, T, E] partials when T <= kFusedMaxT
   size_t counts;    // int32 [nchunks, E]
   size_t bases;     // int32 [nchunks, E]
   size_t h;         // fp16 [T*k, F]
@@ -29,12 +33,19 @@ hipError_t launch_dequant(const uint8_t *q, const uint16_t *s, int64_t rows, int
                           float *out, hipStream_t st);
 hipError_t launch_route(const moe_layer &L, const uint16_t *x, int32_t T, int32_t *idx,
                         float *w, float *logits, hipStream_t st);
+hipError_t launch_route_permute_fused(const moe_layer &L, const uint16_t *x, int32_t T,
+                                      int32_t *idx, float *w, int32_t *offsets,
+                                      int32_t *perm_src, int32_t *inv_pos, float *partial,
+                                      unsigned int *counter, hipStream_t st);
 hipError_t launch_permute(const moe_layer &L, const uint16_t *x, const int32_t *idx, int32_t T,
                           int32_t *offsets, int32_t *perm_src, int32_t *inv_pos,
                           uint16_t *x_perm, int32_t *counts, int32_t *bases, hipStream_t st);
-hipError_t launch_ffn(const moe_layer &L, const uint16_t *x_perm, const int32_t *offsets,
-                      const uint16_t *x, int32_t T, uint16_t *y_perm, uint16_t *y_shared,
-                      uint16_t *h, uint16_t *h_shared, hipStream_t st);
+hipError_t launch_gather(const moe_layer &L, const uint16_t *x, const int32_t *perm_src, int32_t T,
+                         uint16_t *x_perm, hipStream_t st);
+hipError_t launch_ffn(const moe_layer &L, const uint16_t *x, const uint16_t *x_perm,
+                      const int32_t *perm_src, const int32_t *offsets, int32_t T,
+                      uint16_t *y_perm, uint16_t *y_shared, uint16_t *h, uint16_t *h_shared,
+                      hipStream_t st);
 hipError_t launch_combine(const moe_layer &L, const uint16_t *y_perm, const uint16_t *y_shared,
                           const int32_t *inv_pos, const float *w, int32_t T, uint32_t flags,
                           float eps, uint16_t *out, hipStream_t st);

@@ -23,7 +23,10 @@ WsLayout ws_layout(const moe_layer &L, int32_t T) {
   const size_t N = Tz * k;
   const size_t nch = (N + kPermChunk - 1) / kPermChunk;
   size_t off = 0;
-  w.logits = off;   off += align_up(Tz * E * sizeof(float));
+  w.sync = off;     off += 256;
+  const bool fused = Tz <= (size_t)kFusedMaxT && Tz * E <= (size_t)kFusedMaxLogits;
+  const size_t nlog = fused ? (size_t)kFusedMaxKsb * Tz * E : Tz * E;
+  w.logits = off;   off += align_up(nlog * sizeof(float));
   w.counts = off;   off += align_up(nch * E * sizeof(int32_t));
   w.bases = off;    off += align_up(nch * E * sizeof(int32_t));
   w.h = off;        off += align_up(N * (size_t)L.ffn * 2);
@@ -106,9 +109,9 @@ moe_status moe_permute(const moe_layer *L, const uint16_t *x, const int32_t *top
   if ((s = check_layer(L)) != MOE_OK) return s;
   if ((s = check_tokens(L, T)) != MOE_OK) return s;
   if (T == 0) return MOE_OK;
-  if (!ok_ptr(x) || !ok_ptr(topk_idx) || !ok_ptr(offsets) || !ok_ptr(perm_src) ||
-      !ok_ptr(inv_pos) || !ok_ptr(x_perm))
+  if (!ok_ptr(topk_idx) || !ok_ptr(offsets) || !ok_ptr(perm_src) || !ok_ptr(inv_pos))
     return MOE_EINVAL;
+  if (x_perm && (!ok_ptr(x) || !aligned16(x_perm))) return MOE_EINVAL;
   if ((s = check_ws(L, T, ws, ws_bytes)) != MOE_OK) return s;
   const WsLayout w = ws_layout(*L, T);
   char *base = static_cast<char *>(ws);
@@ -119,17 +122,52 @@ moe_status moe_permute(const moe_layer *L, const uint16_t *x, const int32_t *top
                                    (hipStream_t)stream));
 }
 
-moe_status moe_w4_grouped_ffn(const moe_layer *L, const uint16_t *x_perm, const int32_t *offsets,
-                              const uint16_t *x, int32_t T, uint16_t *y_perm, uint16_t *y_shared,
-                              void *ws, size_t ws_bytes, void *stream) {
+moe_status moe_route_permute(const moe_layer *L, const uint16_t *x, int32_t T, int32_t *topk_idx,
+                             float *topk_w, int32_t *offsets, int32_t *perm_src, int32_t *inv_pos,
+                             uint16_t *x_perm, void *ws, size_t ws_bytes, void *stream) {
   moe_status s;
   if ((s = check_layer(L)) != MOE_OK) return s;
   if ((s = check_tokens(L, T)) != MOE_OK) return s;
   if (T == 0) return MOE_OK;
-  if (!ok_ptr(x_perm) || !ok_ptr(offsets) || !ok_ptr(y_perm) || !ok_ptr(L->gate_q) ||
-      !ok_ptr(L->gate_s) || !ok_ptr(L->up_q) || !ok_ptr(L->up_s) || !ok_ptr(L->down_q) ||
-      !ok_ptr(L->down_s))
+  if (!ok_ptr(L->router_w) || !ok_ptr(x) || !ok_ptr(topk_idx) || !ok_ptr(topk_w) ||
+      !ok_ptr(offsets) || !ok_ptr(perm_src) || !ok_ptr(inv_pos))
     return MOE_EINVAL;
+  if (L->router_b && !aligned16(L->router_b)) return MOE_EINVAL;
+  if (x_perm && !aligned16(x_perm)) return MOE_EINVAL;
+  if ((s = check_ws(L, T, ws, ws_bytes)) != MOE_OK) return s;
+  const WsLayout w = ws_layout(*L, T);
+  char *base = static_cast<char *>(ws);
+  hipStream_t st = (hipStream_t)stream;
+  clear_stale_hip_error();
+  if (T <= kFusedMaxT && (int64_t)T * L->num_experts <= kFusedMaxLogits) {
+    hipError_t e = launch_route_permute_fused(
+        *L, x, T, topk_idx, topk_w, offsets, perm_src, inv_pos,
+        reinterpret_cast<float *>(base + w.logits), reinterpret_cast<unsigned int *>(base + w.sync),
+        st);
+    if (e == hipSuccess && x_perm) e = launch_gather(*L, x, perm_src, T, x_perm, st);
+    return hip_status(e);
+  }
+  hipError_t e = launch_route(*L, x, T, topk_idx, topk_w,
+                              reinterpret_cast<float *>(base + w.logits), st);
+  if (e == hipSuccess)
+    e = launch_permute(*L, x, topk_idx, T, offsets, perm_src, inv_pos, x_perm,
+                       reinterpret_cast<int32_t *>(base + w.counts),
+                       reinterpret_cast<int32_t *>(base + w.bases), st);
+  return hip_status(e);
+}
+
+moe_status moe_w4_grouped_ffn(const moe_layer *L, const uint16_t *x, const uint16_t *x_perm,
+                              const int32_t *perm_src, const int32_t *offsets, int32_t T,
+                              uint16_t *y_perm, uint16_t *y_shared, void *ws, size_t ws_bytes,
+                              void *stream) {
+  moe_status s;
+  if ((s = check_layer(L)) != MOE_OK) return s;
+  if ((s = check_tokens(L, T)) != MOE_OK) return s;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(offsets) || !ok_ptr(y_perm) || !ok_ptr(L->gate_q) || !ok_ptr(L->gate_s) ||
+      !ok_ptr(L->up_q) || !ok_ptr(L->up_s) || !ok_ptr(L->down_q) || !ok_ptr(L->down_s))
+    return MOE_EINVAL;
+  if (x_perm ? !aligned16(x_perm) : (!ok_ptr(x) || !ok_ptr(perm_src))) return MOE_EINVAL;
   if (L->shared_ffn > 0 && (!ok_ptr(x) || !ok_ptr(y_shared) || !ok_ptr(L->shared_gate) ||
                             !ok_ptr(L->shared_up) || !ok_ptr(L->shared_down)))
     return MOE_EINVAL;
@@ -137,7 +175,7 @@ moe_status moe_w4_grouped_ffn(const moe_layer *L, const uint16_t *x_perm, const 
   const WsLayout w = ws_layout(*L, T);
   char *base = static_cast<char *>(ws);
   clear_stale_hip_error();
-  return hip_status(launch_ffn(*L, x_perm, offsets, x, T, y_perm,
+  return hip_status(launch_ffn(*L, x, x_perm, perm_src, offsets, T, y_perm,
                                L->shared_ffn > 0 ? y_shared : nullptr,
                                reinterpret_cast<uint16_t *>(base + w.h),
                                reinterpret_cast<uint16_t *>(base + w.h_shared),

@@ -10,7 +10,8 @@
 //   scan:    one block: per-expert totals -> offsets, per-chunk bases
 //   scatter: one wave per chunk; ranks within a wave by matching expert ids
 //            through ballots over their bits, in flat order
-//   gather:  x_perm[r] = x[perm_src[r] / k], 16-byte copies
+//   gather:  x_perm[r] = x[perm_src[r] / k], 16-byte copies (optional: the
+//            FFN can read the rows of x through perm_src instead)
 #include "common.h"
 #include "kernels.h"
 
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(256) void perm_gather_kernel(const f16 *__restrict_
 hipError_t launch_permute(const moe_layer &L, const uint16_t *x, const int32_t *idx, int32_t T,
                           int32_t *offsets, int32_t *perm_src, int32_t *inv_pos,
                           uint16_t *x_perm, int32_t *counts, int32_t *bases, hipStream_t st) {
-  const int E = L.num_experts, k = L.top_k, H = L.hidden;
+  const int E = L.num_experts, k = L.top_k;
   const int N = T * k;
   const int nchunks = (N + kPermChunk - 1) / kPermChunk;
   hipLaunchKernelGGL(perm_count_kernel, dim3(nchunks), dim3(256), 0, st, idx, N, E, counts);
@@ -118,6 +119,14 @@ hipError_t launch_permute(const moe_layer &L, const uint16_t *x, const int32_t *
   hipLaunchKernelGGL(perm_scatter_kernel, dim3(nchunks), dim3(64), 0, st, idx, N, E, bases,
                      perm_src, inv_pos);
   if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (!x_perm) return hipSuccess;
+  return launch_gather(L, x, perm_src, T, x_perm, st);
+}
+
+hipError_t launch_gather(const moe_layer &L, const uint16_t *x, const int32_t *perm_src, int32_t T,
+                         uint16_t *x_perm, hipStream_t st) {
+  const int k = L.top_k, H = L.hidden;
+  const int N = T * k;
   hipLaunchKernelGGL(perm_gather_kernel, dim3((N + 3) / 4), dim3(256), 0, st,
                      reinterpret_cast<const f16 *>(x), perm_src, N, k, T, H,
                      reinterpret_cast<f16 *>(x_perm));

@@ -1,10 +1,12 @@
-// Router: logits on the matrix cores, then softmax and top-k fused in one
-// kernel with wavefront reductions.
+// Router: logits on the matrix cores, softmax + top-k fused with wavefront
+// reductions, and (for decode-sized batches) the permutation by expert in the
+// same launch.
 //
 // Softmax over the expert logits followed by a descending partial sort for
 // the first k: zwxr.cn/news/276292 §3.2 (routing engine).  Softmax and top-k
 // fused into one kernel so the probabilities never round-trip through global
-// memory: lpnh.cn/news/2730718 §2.3.  Ties go to the lower expert index; the
+// memory: lpnh.cn/news/2730718 §2.3.  Tokens grouped by expert for one grouped
+// GEMM: xdnf.cn/news/329730 §3.2.  Ties go to the lower expert index; the
 // combine weights are the softmax probabilities of the chosen experts, not
 // renormalised.
 #include "common.h"
@@ -13,6 +15,79 @@
 
 namespace moe {
 
+// One wave: softmax over the E logits of one token and its k best experts in
+// order.  get(i) returns the logit of expert lane + 64 i (i < NPER; experts
+// past E are skipped), get_expert(e) the logit of expert e.  Each lane sorts
+// its NPER (logit, expert) keys once; every round is one wave-wide maximum
+// over the lanes' current heads, and the winning lane shifts its list.
+// Writes idx_out[0..k), w_out[0..k) and, when lds_idx is given, the indices
+// there too.
+template <int NPER, class Get, class GetE>
+__device__ __forceinline__ void wave_softmax_topk(Get get, GetE get_expert, int E, int k,
+                                                  int32_t *__restrict__ idx_out,
+                                                  float *__restrict__ w_out, int *lds_idx) {
+  const int lane = threadIdx.x & (kWave - 1);
+  float v[NPER];
+  uint64_t key[NPER];
+  float m = -__builtin_inff();
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const int e = lane + i * kWave;
+    v[i] = e < E ? get(i) : -__builtin_inff();
+    key[i] = e < E ? route_key(v[i], e) : 0ull;
+    if (e < E) m = fmax_nan(m, v[i]);
+  }
+  m = wave_max_nan_dpp(m);
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NPER; ++i)
+    if (lane + i * kWave < E) s += expf(v[i] - m);
+  s = wave_sum_dpp(s);
+  // sort this lane's keys, descending (odd-even transposition network)
+#pragma unroll
+  for (int pass = 0; pass < NPER; ++pass)
+#pragma unroll
+    for (int i = pass & 1; i + 1 < NPER; i += 2)
+      if (key[i + 1] > key[i]) {
+        const uint64_t t = key[i]; key[i] = key[i + 1]; key[i + 1] = t;
+      }
+  // k rounds; the winner of round j is uniform, lane j records it
+  int mine = 0;
+  for (int j = 0; j < k; ++j) {
+    const uint64_t best = wave_max_u64(key[0]);
+    if (lane == j) mine = route_key_expert(best);
+    if (key[0] == best) {   // the owner lane: its head won, shift its list
+#pragma unroll
+      for (int i = 0; i + 1 < NPER; ++i) key[i] = key[i + 1];
+      key[NPER - 1] = 0ull;
+    }
+  }
+  if (lane < k) {          // the k weights in parallel
+    const float ve = get_expert(mine);
+    idx_out[lane] = mine;
+    w_out[lane] = expf(ve - m) / s;
+    if (lds_idx) lds_idx[lane] = mine;
+  }
+}
+
+// Instantiate for the number of logits each lane holds (1..16, E <= 1024).
+template <class Get, class GetE>
+__device__ __forceinline__ void wave_softmax_topk_any(Get get, GetE get_expert, int E, int k,
+                                                      int32_t *idx_out, float *w_out,
+                                                      int *lds_idx) {
+  switch ((E + kWave - 1) / kWave) {
+#define MOE_TOPK_CASE(n) \
+    case n: wave_softmax_topk<n>(get, get_expert, E, k, idx_out, w_out, lds_idx); break;
+    MOE_TOPK_CASE(1) MOE_TOPK_CASE(2) MOE_TOPK_CASE(3) MOE_TOPK_CASE(4)
+    MOE_TOPK_CASE(5) MOE_TOPK_CASE(6) MOE_TOPK_CASE(7) MOE_TOPK_CASE(8)
+    MOE_TOPK_CASE(9) MOE_TOPK_CASE(10) MOE_TOPK_CASE(11) MOE_TOPK_CASE(12)
+    MOE_TOPK_CASE(13) MOE_TOPK_CASE(14) MOE_TOPK_CASE(15) MOE_TOPK_CASE(16)
+#undef MOE_TOPK_CASE
+    default: break;
+  }
+}
+
+// ------------------------------------------------------------ any batch size
 // logits[t][e] = x[t] . Wr[e] + b[e].  One block per (16-token tile,
 // 16-expert tile); its 4 waves split K and their partial sums are added in a
 // fixed order.
@@ -45,28 +120,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const f16 *__restric
   }
 }
 
-// Ranking key: numbers above NaN, NaN above empty slots; among equals the
-// lower expert index first.
-struct Cand {
-  float v;
-  int cls;   // 2 = number, 1 = NaN, 0 = empty / already chosen
-  int e;
-};
-
-__device__ __forceinline__ bool better(const Cand &a, const Cand &b) {
-  if (a.cls != b.cls) return a.cls > b.cls;
-  if (a.cls == 2 && a.v != b.v) return a.v > b.v;
-  return a.e < b.e;
-}
-
-__device__ __forceinline__ float max_nan(float a, float b) {
-  return (a != a || b != b) ? __builtin_nanf("") : fmaxf(a, b);
-}
-
-constexpr int kMaxPerLane = 16;   // E <= 1024
-
-// One wave per token: softmax over E logits, then k rounds of a wave-wide
-// arg-max.  4 tokens per 256-thread block.
+// One wave per token, 4 tokens per block.
 __global__ __launch_bounds__(256) void softmax_topk_kernel(const float *__restrict__ logits,
                                                            int T, int E, int k,
                                                            int32_t *__restrict__ idx,
@@ -75,44 +129,168 @@ __global__ __launch_bounds__(256) void softmax_topk_kernel(const float *__restri
   const int t = blockIdx.x * 4 + threadIdx.x / kWave;
   if (t >= T) return;
   const float *lt = logits + (size_t)t * E;
-  float v[kMaxPerLane];
-  float m = -__builtin_inff();
+  wave_softmax_topk_any([&](int i) { return lt[lane + i * kWave]; },
+                        [&](int e) { return lt[e]; }, E, k, idx + (size_t)t * k,
+                        w + (size_t)t * k, nullptr);
+}
+
+// ------------------------------------------------------------ decode batches
+// Route and permute in one launch.  Blocks (16-token tile, 16-expert tile,
+// K part) write partial logits; the last block to finish (device-wide
+// counter) adds the partials in K-part order plus the bias, runs softmax and
+// top-k (one wave per token), then builds the per-expert segments in LDS:
+// histogram, exclusive scan, and stable ranks by ballot-matching expert ids
+// 64 entries at a time.  It then resets the counter to 0.
+constexpr int kFusedWaves = 16;
+
+struct FusedRouteArgs {
+  const f16 *x;
+  const f16 *wr;
+  const float *bias;
+  int T, E, H, k, ksb;           // ksb: K parts across blocks
+  float *partial;                // [ksb, T, E]
+  unsigned int *counter;         // zero before the launch, zero after
+  int32_t *idx;                  // [T, k]
+  float *w;                      // [T, k]
+  int32_t *offsets;              // [E + 1]
+  int32_t *perm_src;             // [T*k]
+  int32_t *inv_pos;              // [T*k]
+};
+
+__global__ __launch_bounds__(kFusedWaves * kWave) void route_permute_kernel(FusedRouteArgs p) {
+  __shared__ float red[(kFusedWaves - 1) * 4 * kWave];
+  __shared__ int s_idx[kFusedMaxT * 32];
+  __shared__ float s_logit[kFusedMaxLogits];
+  __shared__ int s_cnt[1024];
+  __shared__ int s_scan[kFusedWaves];
+  __shared__ int s_last;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wid = tid / kWave;
+  const int r = lane & 15, kb = lane >> 4;
+  const int T = p.T, E = p.E, H = p.H, k = p.k;
+  const int G = H / kGroup;
+
+  // ---- partial logits of this block's (token tile, expert tile, K part)
+  {
+    const int etiles = (E + 15) / 16;
+    const int kp = blockIdx.x % p.ksb;
+    const int et = (blockIdx.x / p.ksb) % etiles;
+    const int mt = blockIdx.x / (p.ksb * etiles);
+    const int tok0 = mt * 16;
+    const int rows = min(16, T - tok0);
+    const f16 *arow = p.x + (size_t)(tok0 + min(r, rows - 1)) * H;
+    const int e = et * 16 + r;
+    const f16 *wrow[1] = {p.wr + (size_t)min(e, E - 1) * H};
+    const int kg0 = kp * G / p.ksb, kg1 = (kp + 1) * G / p.ksb;
+    const int n = kg1 - kg0;
+    f32x4 acc[1] = {{0.f, 0.f, 0.f, 0.f}};
+    f16_tiles<1>(arow, wrow, kb, kg0 + wid * n / kFusedWaves, kg0 + (wid + 1) * n / kFusedWaves,
+                 acc);
+    ksplit_reduce<1, kFusedWaves>(acc, red);
+    if (wid == 0 && e < E) {
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
-    const int e = lane + i * kWave;
-    v[i] = e < E ? lt[e] : -__builtin_inff();
-    if (e < E) m = max_nan(m, v[i]);
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) m = max_nan(m, __shfl_xor(m, o, kWave));
-  float s = 0.0f;
-#pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i)
-    if (lane + i * kWave < E) s += expf(v[i] - m);
-  s = wave_sum(s);
-  uint32_t taken = 0;   // bit i: entry i of this lane already chosen
-  for (int j = 0; j < k; ++j) {
-    Cand best{0.0f, 0, 0x7fffffff};
-#pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
-      const int e = lane + i * kWave;
-      if (e < E && !((taken >> i) & 1u)) {
-        Cand c{v[i], v[i] != v[i] ? 1 : 2, e};
-        if (better(c, best)) best = c;
+      for (int j = 0; j < 4; ++j) {
+        const int tok = 4 * kb + j;
+        if (tok < rows)   // written through to the device coherence point (no L2 flush)
+          __hip_atomic_store(&p.partial[((size_t)kp * T + tok0 + tok) * E + e], acc[0][j],
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
+  }
+  // ---- the last block continues.  The partials travel as agent-scope
+  // atomic stores and loads, which reach / read the device coherence point
+  // directly; waiting for this wave's stores to complete before the barrier
+  // orders them before the counter increment, so no L2 write-back or
+  // invalidate (what a full device fence costs across the XCDs) is needed.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(p.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             gridDim.x - 1;
+  __syncthreads();
+  if (!s_last) return;
+
+  // logits = sum of the K parts in order + bias, into LDS; every thread's
+  // loads are independent so they are all in flight together
+  const int TE = T * E;
+  for (int i = tid; i < TE; i += blockDim.x) {
+    const int e = i % E;
+    float part[kFusedMaxKsb];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      Cand other{__shfl_xor(best.v, o, kWave), __shfl_xor(best.cls, o, kWave),
-                 __shfl_xor(best.e, o, kWave)};
-      if (better(other, best)) best = other;
-    }
-    if ((best.e & (kWave - 1)) == lane) taken |= 1u << (best.e / kWave);
-    if (lane == 0) {
-      idx[(size_t)t * k + j] = best.e;
-      w[(size_t)t * k + j] = expf(best.v - m) / s;
+    for (int kp = 0; kp < kFusedMaxKsb; ++kp)
+      part[kp] = kp < p.ksb ? __hip_atomic_load(&p.partial[(size_t)kp * TE + i], __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT)
+                            : 0.0f;
+    float a = part[0];
+#pragma unroll
+    for (int kp = 1; kp < kFusedMaxKsb; ++kp)
+      if (kp < p.ksb) a += part[kp];
+    s_logit[i] = a + (p.bias ? p.bias[e] : 0.0f);
+  }
+  __syncthreads();
+
+  // softmax + top-k, one wave per token
+  for (int t = wid; t < T; t += kFusedWaves) {
+    const float *lt = s_logit + t * E;
+    wave_softmax_topk_any([&](int i) { return lt[lane + i * kWave]; },
+                          [&](int e) { return lt[e]; }, E, k, p.idx + (size_t)t * k,
+                          p.w + (size_t)t * k, s_idx + t * k);
+  }
+  for (int e = tid; e < E; e += blockDim.x) s_cnt[e] = 0;
+  __syncthreads();
+
+  // histogram and exclusive scan -> offsets
+  const int N = T * k;
+  for (int f = tid; f < N; f += blockDim.x) atomicAdd(&s_cnt[s_idx[f]], 1);
+  __syncthreads();
+  static_assert(kFusedWaves * kWave >= 1024, "one thread per expert");
+  const int cnt = tid < E ? s_cnt[tid] : 0;
+  int total;
+  const int run = block_excl_scan(cnt, s_scan, &total);
+  __syncthreads();   // every s_cnt read is done before it is overwritten
+  if (tid < E) {
+    p.offsets[tid] = run;
+    s_cnt[tid] = run;   // running next-row counter of segment e
+  }
+  if (tid == 0) p.offsets[E] = total;
+  __syncthreads();
+
+  // stable ranks: wave 0 walks the flat entries in order, 64 at a time
+  if (wid == 0) {
+    const uint64_t below = (1ull << lane) - 1ull;
+    for (int base = 0; base < N; base += kWave) {
+      const int f = base + lane;
+      const bool valid = f < N;
+      const int e = valid ? s_idx[f] : E;   // E marks an empty lane
+      uint64_t same = ~0ull;
+#pragma unroll
+      for (int b = 0; b < 11; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t m = __ballot(bit);
+        same &= bit ? m : ~m;
+      }
+      const int rank = __popcll(same & below);
+      const int start = valid ? s_cnt[e] : 0;
+      if (valid && (same & below) == 0ull) s_cnt[e] = start + __popcll(same);
+      if (valid) {
+        p.perm_src[start + rank] = f;
+        p.inv_pos[f] = start + rank;
+      }
     }
   }
+  if (tid == 0) __hip_atomic_store(p.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// K parts across blocks: only when there are too few expert tiles to spread
+// the router weights over enough CUs (each part is one more partial per
+// logit for the last block to add after the cross-XCD fence).
+int fused_route_ksb(const moe_layer &L) {
+  const int G = L.hidden / kGroup;
+  const int etiles = (L.num_experts + 15) / 16;
+  int ksb = 1;
+  while (ksb < kFusedMaxKsb && etiles * ksb < 64 && G / (2 * ksb) >= 8) ksb *= 2;
+  return ksb;
 }
 
 hipError_t launch_route(const moe_layer &L, const uint16_t *x, int32_t T, int32_t *idx,
@@ -126,6 +304,23 @@ hipError_t launch_route(const moe_layer &L, const uint16_t *x, int32_t T, int32_
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(softmax_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, st, logits, T, E,
                      L.top_k, idx, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_permute_fused(const moe_layer &L, const uint16_t *x, int32_t T,
+                                      int32_t *idx, float *w, int32_t *offsets,
+                                      int32_t *perm_src, int32_t *inv_pos, float *partial,
+                                      unsigned int *counter, hipStream_t st) {
+  FusedRouteArgs a{};
+  a.x = reinterpret_cast<const f16 *>(x);
+  a.wr = reinterpret_cast<const f16 *>(L.router_w);
+  a.bias = L.router_b;
+  a.T = T; a.E = L.num_experts; a.H = L.hidden; a.k = L.top_k;
+  a.ksb = fused_route_ksb(L);
+  a.partial = partial; a.counter = counter;
+  a.idx = idx; a.w = w; a.offsets = offsets; a.perm_src = perm_src; a.inv_pos = inv_pos;
+  const int blocks = ((T + 15) / 16) * ((a.E + 15) / 16) * a.ksb;
+  hipLaunchKernelGGL(route_permute_kernel, dim3(blocks), dim3(kFusedWaves * kWave), 0, st, a);
   return hipGetLastError();
 }
 

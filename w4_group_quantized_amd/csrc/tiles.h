@@ -153,9 +153,10 @@ __device__ __forceinline__ void f16_tiles(const f16 *__restrict__ arow,
   if (g < g1) f16_compute<NT>(a, acc);
 }
 
-// Sum the accumulators of the 4 waves of a block (K split 4 ways) into wave 0,
-// in the fixed order wave 0 + 1 + 2 + 3.  red: LDS of 3 * NT * 4 * 64 floats.
-template <int NT>
+// Sum the accumulators of the NW waves of a block (K split NW ways) into wave
+// 0, in the fixed order wave 0 + 1 + ... + NW-1.
+// red: LDS of (NW - 1) * NT * 4 * 64 floats.
+template <int NT, int NW = 4>
 __device__ __forceinline__ void ksplit_reduce(f32x4 (&acc)[NT], float *red) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x / kWave;
@@ -168,7 +169,7 @@ __device__ __forceinline__ void ksplit_reduce(f32x4 (&acc)[NT], float *red) {
   __syncthreads();
   if (wid == 0) {
 #pragma unroll
-    for (int w = 1; w < 4; ++w)
+    for (int w = 1; w < NW; ++w)
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll

@@ -1,8 +1,8 @@
 """Device-resident W4 MoE layer: weights, preallocated buffers, one forward.
 
 PyTorch provides device memory and streams only; every step of the layer
-runs in the HIP kernels behind the four C entry points, called in order on
-one stream with no host synchronization in between.
+runs in the HIP kernels behind the C entry points, called in order on one
+stream with no host synchronization in between.
 """
 from __future__ import annotations
 
@@ -11,11 +11,6 @@ from dataclasses import dataclass
 import torch
 
 from . import _native as N
-
-
-def _u16(t: torch.Tensor) -> torch.Tensor:
-    assert t.dtype in (torch.float16, torch.uint16, torch.int16), t.dtype
-    return t
 
 
 @dataclass
@@ -76,21 +71,27 @@ class W4MoELayer:
             y_perm=torch.empty((T * k, H), dtype=f16, device=d),
             y_shared=torch.empty((T if self.Fs else 0, H), dtype=f16, device=d),
             out=torch.empty((T, H), dtype=f16, device=d),
-            ws=torch.empty((max(self.workspace_size(T), 256),), dtype=torch.uint8, device=d),
+            # zero-filled once: it holds the fused router's completion counter
+            ws=torch.zeros((max(self.workspace_size(T), 256),), dtype=torch.uint8, device=d),
         )
 
-    # the four stages, each one C call
+    # the stages, each one C call
     def route(self, x, buf, T, stream=None):
         N.moe_route(self.desc, x, T, buf.topk_idx, buf.topk_w, buf.ws, buf.ws.numel(), stream)
 
-    def permute(self, x, buf, T, stream=None):
+    def permute(self, x, buf, T, gather=True, stream=None):
         N.moe_permute(self.desc, x, buf.topk_idx, T, buf.offsets, buf.perm_src, buf.inv_pos,
-                      buf.x_perm, buf.ws, buf.ws.numel(), stream)
+                      buf.x_perm if gather else None, buf.ws, buf.ws.numel(), stream)
 
-    def ffn(self, x, buf, T, stream=None):
-        N.moe_w4_grouped_ffn(self.desc, buf.x_perm, buf.offsets, x if self.Fs else None, T,
-                             buf.y_perm, buf.y_shared if self.Fs else None, buf.ws,
-                             buf.ws.numel(), stream)
+    def route_permute(self, x, buf, T, gather=False, stream=None):
+        N.moe_route_permute(self.desc, x, T, buf.topk_idx, buf.topk_w, buf.offsets, buf.perm_src,
+                            buf.inv_pos, buf.x_perm if gather else None, buf.ws, buf.ws.numel(),
+                            stream)
+
+    def ffn(self, x, buf, T, use_x_perm=False, stream=None):
+        N.moe_w4_grouped_ffn(self.desc, x, buf.x_perm if use_x_perm else None, buf.perm_src,
+                             buf.offsets, T, buf.y_perm, buf.y_shared if self.Fs else None,
+                             buf.ws, buf.ws.numel(), stream)
 
     def combine(self, buf, T, rmsnorm=False, eps=1e-6, out=None, stream=None):
         N.moe_unpermute_combine(self.desc, buf.y_perm, buf.y_shared if self.Fs else None,
@@ -98,13 +99,16 @@ class W4MoELayer:
                                 eps, buf.out if out is None else out, stream)
 
     def forward(self, x, buf, T=None, rmsnorm=False, eps=1e-6, out=None, stream=None):
-        """x fp16 [T, H] on the device -> buf.out (or `out`) fp16 [T, H]."""
+        """x fp16 [T, H] on the device -> buf.out (or `out`) fp16 [T, H].
+
+        Three launches-worth of calls: route + permute (one launch for small
+        batches), the grouped FFN reading token rows through perm_src, and the
+        combine."""
         T = x.shape[0] if T is None else T
         if T > buf.max_tokens:
             raise ValueError("more tokens than the buffers were allocated for")
-        self.route(x, buf, T, stream)
-        self.permute(x, buf, T, stream)
-        self.ffn(x, buf, T, stream)
+        self.route_permute(x, buf, T, stream=stream)
+        self.ffn(x, buf, T, stream=stream)
         self.combine(buf, T, rmsnorm, eps, out, stream)
         return buf.out[:T] if out is None else out
 
