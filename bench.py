@@ -242,6 +242,21 @@ def main():
     ffn_bytes = np.array([bytes_per_combo[i % n_combo] for i in range(K)], dtype=np.float64)
     achieved_gbs = float(ffn_bytes.mean() / (ffn_ms.mean() * 1e-3) / 1e9)
     tokens_per_s = T * K / (ms_total * 1e-3)
+    # algorithmic FFN FLOPs: every (token, chosen expert) pair costs 6*H*F
+    # (gate, up, down), the shared expert 6*H*Fs per token
+    ffn_flops = T * (cfg.top_k * 6.0 * cfg.hidden * cfg.ffn + 6.0 * cfg.hidden * cfg.shared_ffn)
+    achieved_tflops = float(ffn_flops / (ffn_ms.mean() * 1e-3) / 1e12)
+    if cfg.name == "prefill":
+        roofline = {"bound": "mfma", "achieved": achieved_tflops, "peak": MFMA_F16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": achieved_tflops / MFMA_F16_PEAK_TFLOPS,
+                    "traffic": None}
+    else:
+        roofline = {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None}
+    roofline.update({"kernel": "moe_w4_grouped_ffn (gate/up launch + down launch)",
+                     "ffn_us_mean": float(ffn_ms.mean() * 1e3),
+                     "ffn_bytes_mean": float(ffn_bytes.mean()), "ffn_flops": ffn_flops,
+                     "ffn_tflops": achieved_tflops, "ffn_gbs": achieved_gbs})
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -271,13 +286,7 @@ def main():
             "weights": "int4 g128 (fp16 scales), router fp16, shared expert fp16",
             "distinct_experts_per_step_mean": float(np.mean(u_per_combo)),
         },
-        "roofline": {
-            "bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
-            "kernel": "moe_w4_grouped_ffn (gate/up launch + down launch)",
-            "ffn_us_mean": float(ffn_ms.mean() * 1e3),
-            "ffn_bytes_mean": float(ffn_bytes.mean()),
-        },
+        "roofline": roofline,
         "wall_s_timed": wall,
         "cpu_baseline": cpu,
     }

@@ -90,3 +90,12 @@ def test_zero_tokens_is_a_noop():
     layer.forward(x[:0], buf, T=0)
     torch.cuda.synchronize()
     assert (_np(buf.out) == 7).all()
+
+
+@pytest.mark.parametrize("E,H,F,k,T", [(16, 256, 384, 4, 150), (8, 512, 256, 2, 700),
+                                       (32, 768, 384, 8, 300)])
+def test_prefill_kernel_path(E, H, F, k, T):
+    """Average segment >= 32 rows and H % 256 == 0: the LDS-tiled MFMA path,
+    with ragged segment tails (segments not multiples of 128 rows)."""
+    cfg = get_config("prefill", num_experts=E, hidden=H, ffn=F, top_k=k, dead_experts=1)
+    run_layer_case(cfg, T, batch=3)

@@ -178,10 +178,31 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
   }
 }
 
-constexpr int kNT1 = 1;   // phase 1: 64 gate rows + 64 up rows per block
-constexpr int kNT2 = 2;   // phase 2: 128 down rows per block
-constexpr int kS1 = 1;    // groups per pipeline stage, phase 1
-constexpr int kS2 = 1;    // groups per pipeline stage, phase 2
+#ifndef MOE_FFN_NT1
+#define MOE_FFN_NT1 2
+#endif
+#ifndef MOE_FFN_NT2
+#define MOE_FFN_NT2 4
+#endif
+#ifndef MOE_FFN_S1
+#define MOE_FFN_S1 2
+#endif
+#ifndef MOE_FFN_S2
+#define MOE_FFN_S2 1
+#endif
+constexpr int kNT1 = MOE_FFN_NT1;   // phase 1: 64*NT1 gate rows + as many up rows per block
+constexpr int kNT2 = MOE_FFN_NT2;   // phase 2: 64*NT2 down rows per block
+constexpr int kS1 = MOE_FFN_S1;     // groups per pipeline stage, phase 1
+constexpr int kS2 = MOE_FFN_S2;     // groups per pipeline stage, phase 2
+
+// Prefill mode: segments average at least this many rows, so a 128-row MFMA
+// block tile is mostly full; routed experts then run on the LDS-tiled kernel.
+constexpr int kPrefillMinAvgRows = 32;
+
+bool ffn_prefill_mode(const moe_layer &L, int32_t T) {
+  return (int64_t)T * L.top_k >= (int64_t)kPrefillMinAvgRows * L.num_experts &&
+         L.hidden % 256 == 0;
+}
 
 hipError_t launch_ffn(const moe_layer &L, const uint16_t *x, const uint16_t *x_perm,
                       const int32_t *perm_src, const int32_t *offsets, int32_t T,
@@ -189,6 +210,7 @@ hipError_t launch_ffn(const moe_layer &L, const uint16_t *x, const uint16_t *x_p
                       hipStream_t st) {
   const int E = L.num_experts, H = L.hidden, F = L.ffn, Fs = L.shared_ffn, k = L.top_k;
   const int N = T * k;
+  const bool prefill = ffn_prefill_mode(L, T);
   // worst case number of 16-row segment tiles: every non-empty segment adds at
   // most one partial tile
   const int max_tiles = (E < N ? E : N) + (N + kTileM - 1) / kTileM;
@@ -199,6 +221,12 @@ hipError_t launch_ffn(const moe_layer &L, const uint16_t *x, const uint16_t *x_p
   a.offsets = offsets;
 
   // phase 1: token rows from x_perm, or from x through perm_src
+  hipError_t err;
+  if (prefill) {
+    err = launch_ffn_prefill_phase(L, 1, x_perm ? x_perm : x, x_perm ? nullptr : perm_src,
+                                   offsets, T, h, st);
+    if (err != hipSuccess) return err;
+  }
   a.perm_src = x_perm ? nullptr : perm_src;
   a.a_routed = reinterpret_cast<const f16 *>(x_perm ? x_perm : x);
   a.a_shared = reinterpret_cast<const f16 *>(x);
@@ -209,14 +237,20 @@ hipError_t launch_ffn(const moe_layer &L, const uint16_t *x, const uint16_t *x_p
   a.w1 = reinterpret_cast<const f16 *>(L.shared_up);
   a.out_routed = reinterpret_cast<f16 *>(h);
   a.out_shared = reinterpret_cast<f16 *>(h_shared);
-  a.routed_items = max_tiles * (F / (64 * kNT1));
+  static_assert(128 % (64 * kNT1) == 0, "F is a multiple of 128");
+  a.routed_items = prefill ? 0 : max_tiles * (F / (64 * kNT1));
   int shared_items = Fs ? mtiles_shared * (Fs / 16) : 0;
-  hipLaunchKernelGGL((ffn_decode_kernel<1, kNT1, kS1>), dim3(a.routed_items + shared_items),
-                     dim3(256), 0, st, a);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  if (a.routed_items + shared_items > 0) {
+    hipLaunchKernelGGL((ffn_decode_kernel<1, kNT1, kS1>), dim3(a.routed_items + shared_items),
+                       dim3(256), 0, st, a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
 
   // phase 2
+  if (prefill) {
+    err = launch_ffn_prefill_phase(L, 2, h, nullptr, offsets, T, y_perm, st);
+    if (err != hipSuccess) return err;
+  }
   a.perm_src = nullptr;
   a.a_routed = reinterpret_cast<const f16 *>(h);
   a.a_shared = reinterpret_cast<const f16 *>(h_shared);
@@ -225,11 +259,20 @@ hipError_t launch_ffn(const moe_layer &L, const uint16_t *x, const uint16_t *x_p
   a.w0 = reinterpret_cast<const f16 *>(L.shared_down); a.w1 = nullptr;
   a.out_routed = reinterpret_cast<f16 *>(y_perm);
   a.out_shared = reinterpret_cast<f16 *>(y_shared);
-  a.routed_items = max_tiles * (H / (64 * kNT2));
+  // 64*kNT2 down rows per block when H allows it, else 128
+  const bool wide2 = H % (64 * kNT2) == 0;
+  a.routed_items = prefill ? 0 : max_tiles * (H / (64 * (wide2 ? kNT2 : 2)));
   shared_items = Fs ? mtiles_shared * (H / 16) : 0;
-  hipLaunchKernelGGL((ffn_decode_kernel<2, kNT2, kS2>), dim3(a.routed_items + shared_items),
-                     dim3(256), 0, st, a);
-  return hipGetLastError();
+  if (a.routed_items + shared_items > 0) {
+    if (wide2)
+      hipLaunchKernelGGL((ffn_decode_kernel<2, kNT2, kS2>), dim3(a.routed_items + shared_items),
+                         dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((ffn_decode_kernel<2, 2, kS2>), dim3(a.routed_items + shared_items),
+                         dim3(256), 0, st, a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 }  // namespace moe

@@ -46,6 +46,9 @@ hipError_t launch_ffn(const moe_layer &L, const uint16_t *x, const uint16_t *x_p
                       const int32_t *perm_src, const int32_t *offsets, int32_t T,
                       uint16_t *y_perm, uint16_t *y_shared, uint16_t *h, uint16_t *h_shared,
                       hipStream_t st);
+hipError_t launch_ffn_prefill_phase(const moe_layer &L, int phase, const uint16_t *a,
+                                    const int32_t *perm_src, const int32_t *offsets, int32_t T,
+                                    uint16_t *out, hipStream_t st);
 hipError_t launch_combine(const moe_layer &L, const uint16_t *y_perm, const uint16_t *y_shared,
                           const int32_t *inv_pos, const float *w, int32_t T, uint32_t flags,
                           float eps, uint16_t *out, hipStream_t st);
