@@ -291,7 +291,7 @@ def rmsnorm(y: np.ndarray, eps: float = 1e-6) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # whole layer
 # ---------------------------------------------------------------------------
-def moe_layer(x16, router_w16, router_b, experts, k: int, shared=None):
+def moe_layer(x16, router_w16, router_b, experts, k: int, shared=None, expert_ffn=None):
     """One MoE layer forward in float64, keeping every intermediate.
 
     experts: indexable by expert id, returning
@@ -300,7 +300,11 @@ def moe_layer(x16, router_w16, router_b, experts, k: int, shared=None):
              receive tokens are fetched, so a lazy provider may regenerate
              them on demand.
     shared:  None or (Wg16 [Fs,H], Wu16 [Fs,H], Wd16 [H,Fs]) fp16.
+    expert_ffn: the routed expert's FFN (default expert_ffn_w4; the C
+             reference in oracle.cref evaluates the same definition for
+             matrices too large to dequantize in numpy).
     """
+    expert_ffn = expert_ffn_w4 if expert_ffn is None else expert_ffn
     x16 = np.asarray(x16)
     T = x16.shape[0]
     E = np.asarray(router_w16).shape[0]
@@ -312,7 +316,7 @@ def moe_layer(x16, router_w16, router_b, experts, k: int, shared=None):
     for e in range(E):
         a, b = int(off[e]), int(off[e + 1])
         if b > a:
-            y_perm[a:b] = expert_ffn_w4(x_perm[a:b], *experts[e])
+            y_perm[a:b] = expert_ffn(x_perm[a:b], *experts[e])
     ys = swiglu_ffn(x16, *shared) if shared is not None else None
     out = combine(y_perm, ys, inv_pos, w, T, k)
     return dict(idx=idx, w=w, logits=logits, offsets=off, perm_src=perm_src,
