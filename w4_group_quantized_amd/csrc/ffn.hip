@@ -196,12 +196,17 @@ constexpr int kS1 = MOE_FFN_S1;     // groups per pipeline stage, phase 1
 constexpr int kS2 = MOE_FFN_S2;     // groups per pipeline stage, phase 2
 
 // Prefill mode: segments average at least this many rows, so a 128-row MFMA
-// block tile is mostly full; routed experts then run on the LDS-tiled kernel.
+// block tile is mostly full; routed experts then run on the MFMA kernel.  Its
+// buffer loads address each activation matrix and each expert's weight
+// matrix with 32-bit byte offsets.
 constexpr int kPrefillMinAvgRows = 32;
 
 bool ffn_prefill_mode(const moe_layer &L, int32_t T) {
-  return (int64_t)T * L.top_k >= (int64_t)kPrefillMinAvgRows * L.num_experts &&
-         L.hidden % 256 == 0;
+  const int64_t N = (int64_t)T * L.top_k;
+  const int64_t H = L.hidden, F = L.ffn;
+  const int64_t max_bytes = int64_t(1) << 31;
+  return N >= (int64_t)kPrefillMinAvgRows * L.num_experts && H % 256 == 0 &&
+         N * H * 2 < max_bytes && N * F * 2 < max_bytes && F * H / 2 < max_bytes;
 }
 
 hipError_t launch_ffn(const moe_layer &L, const uint16_t *x, const uint16_t *x_perm,

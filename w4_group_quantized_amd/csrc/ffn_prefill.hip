@@ -1,22 +1,31 @@
-// Grouped W4 SwiGLU FFN for prefill-sized segments: an LDS-tiled grouped GEMM
-// on v_mfma_f32_32x32x16_f16.
+// Grouped W4 SwiGLU FFN for prefill-sized segments: a grouped GEMM on
+// v_mfma_f32_32x32x16_f16 with the int4 weights dequantized in registers.
 //
 // Grouped GEMM over the selected experts in one launch per phase
 // (xdnf.cn/news/329730 §3.2, lpnh.cn/news/2730718 §2.3); in-kernel dequant of
-// the int4 expert weights, unpacked once per block tile and reused by every
-// token row of the tile (the per-token re-unpacking that xdnf.cn/news/329730
-// §3.1 reports as wasteful on its GPU does not happen here).
+// the int4 expert weights, each weight unpacked once per 128-token block tile
+// (the per-token re-unpacking that xdnf.cn/news/329730 §3.1 reports as
+// wasteful on its GPU does not happen here).
 //
 // Block tile: 128 token rows (one segment tile of one expert) x 256 weight
-// rows, K step 32.  Per K step the block loads the 256 x 32 int4 codes
-// (16 bytes per thread, one 256-byte chunk per 16-row tile of the storage
-// layout) and the 128 x 32 fp16 activations, dequantizes the codes with their
-// group scale into fp16 (RN16(q*s)) and writes both into one of two LDS
-// buffers; the 4 waves (2 x 2) each multiply a 64 x 128 sub-tile with 8
-// 32x32 accumulators while the next K step's global loads are in flight.
-// Phase 1 orders the 256 B rows as [gate f0..63 | up f0..63 | gate f64..127
-// | up f64..127] so each wave holds matching gate and up columns and applies
-// silu(g) * u in registers.
+// rows, K step 64, 4 waves.  The activation tile goes through LDS: each K
+// step's 128 x 64 fp16 tile is copied by direct global->LDS loads into one of
+// three stage buffers, two steps ahead of its use.  The weights do not touch
+// LDS: wave w owns 64 weight rows and loads their int4 codes straight into
+// registers (16 bytes per lane per 32 rows per K step, also two steps ahead),
+// unpacks them with the group scale folded in (RN16(q*s)) and feeds them as
+// the B operand, so every weight is read from memory and unpacked exactly
+// once per block.  Each wave multiplies all 128 token rows by its 64 weight
+// rows: 4 x 2 accumulators of 32 x 32.
+//
+// Phase 1 gives wave w gate rows and up rows of the same 32 ffn columns, so
+// silu(g) * u is formed in registers.
+//
+// LDS layout of one stage: 128 rows of 128 bytes (64 halfs); the eight 16-byte
+// pieces of row r are stored XOR-swizzled (piece p at position p ^ (r % 8)),
+// which keeps both the direct loads (1 KB contiguous per wave instruction)
+// and the MFMA operand reads (32 rows x 16 bytes per half wave) free of bank
+// conflicts.
 #include "common.h"
 #include "kernels.h"
 
@@ -26,8 +35,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kPM = 128;          // token rows per block tile
 constexpr int kPN = 256;          // weight rows per block tile
-constexpr int kPK = 32;           // K per step
-constexpr int kPLda = kPK + 8;    // LDS row stride in halfs (padding against bank conflicts)
+constexpr int kPK = 64;           // K per step
+constexpr int kPStage = kPM * kPK;  // halfs per stage
 
 struct PrefillArgs {
   int E, H, F, T, N, k;
@@ -78,15 +87,124 @@ __device__ bool locate_tile128(const int32_t *__restrict__ off, int E, int slot,
   return s_res[0] >= 0;
 }
 
+// All LDS operations of this wave are done; meet the other waves of the
+// block.  The "memory" clobber keeps the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer over `bytes` bytes at `base` (gfx9 descriptor: stride 0, plain
+// dword data format).  Loads through it take a 32-bit per-lane byte offset
+// plus a wave-uniform one in an SGPR; offsets past `bytes` read zeros.
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ f16 bload_f16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(f16, __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0));
+}
+
+// Per-lane byte offsets of one block tile (step 0) and LDS offsets.
+struct PrefillOperands {
+  uint32_t a_off[4];          // activation pieces in the activation buffer
+  int a_dst;                  // this lane's first piece in a stage (halfs)
+  int a_rd[4];                // operand read offset in a stage per k16 sub-step (halfs)
+  uint32_t b_off[2];          // code chunk per N-tile in its code buffer
+  uint32_t s_off[2];          // group-0 scale per N-tile in its scale buffer
+  int nsteps;
+};
+
+// The K loop.  Step s: meet at the barrier (stage s % 2 is complete), issue
+// the loads of the activation pieces of step s + 1 and of the code chunks and
+// scales of step s + 2 (clamped to the last step; surplus loads are never
+// used), run 4 k16 sub-steps of 8 MFMAs on LDS stage s % 2, then store the
+// step s + 1 pieces into the other stage.  Code/scale registers rotate with
+// period 3, hence the loop unrolled by 3.
+__device__ __forceinline__ void prefill_gemm(f16 *sA, rsrc_t a_rs, rsrc_t b_rs0, rsrc_t b_rs1,
+                                             rsrc_t s_rs0, rsrc_t s_rs1,
+                                             const PrefillOperands &o, f32x16 (&acc)[4][2]) {
+  u32x4 ra[4];                      // activation pieces of the next step
+  u32x4 rb0[2], rb1[2], rb2[2];     // code chunks of the three steps in flight
+  f16 rs0[2], rs1[2], rs2[2];       // their group scales
+  const int nsteps = o.nsteps;
+  auto load_a = [&](int step) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ra[j] = bload16(a_rs, o.a_off[j], step * (kPK * 2));
+  };
+  auto load_b = [&](int step, u32x4 (&rb)[2], f16 (&rs)[2]) {
+    rb[0] = bload16(b_rs0, o.b_off[0], step * 512);
+    rb[1] = bload16(b_rs1, o.b_off[1], step * 512);
+    rs[0] = bload_f16(s_rs0, o.s_off[0], (step >> 1) * 32);
+    rs[1] = bload_f16(s_rs1, o.s_off[1], (step >> 1) * 32);
+  };
+  auto store_a = [&](int step) {
+    f16 *dst = sA + (step & 1) * kPStage + o.a_dst;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4 *>(dst + j * 8 * kPK) = ra[j];
+  };
+
+  const UnpackConsts kc = unpack_consts();
+  auto body = [&](int step, const u32x4 (&rb)[2], const f16 (&rs)[2], u32x4 (&rb_ahead)[2],
+                  f16 (&rs_ahead)[2]) {
+    lds_barrier();      // stage step % 2 is complete; stage (step+1) % 2 is free
+    load_a(min(step + 1, nsteps - 1));
+    load_b(min(step + 2, nsteps - 1), rb_ahead, rs_ahead);
+    __builtin_amdgcn_sched_barrier(0);   // keep the loads at the top of the step
+    const f16 *as = sA + (step & 1) * kPStage;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      f16x8 bf[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const f16x8 q = unpack8(rb[j][w], kc);
+        const f16x2 sc = {rs[j], rs[j]};
+        u32x4 v;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const f16x2 pr = {q[2 * t], q[2 * t + 1]};
+          v[t] = as_u32(pr * sc);                    // RN16(q * s)
+        }
+        bf[j] = as_f16x8(v);
+      }
+      f16x8 af[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        af[i] = *reinterpret_cast<const f16x8 *>(as + i * 32 * kPK + o.a_rd[w]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_32x32x16(af[i], bf[j], acc[i][j]);
+    }
+    if (step + 1 < nsteps) store_a(step + 1);
+  };
+
+  load_a(0);
+  load_b(0, rb0, rs0);
+  load_b(min(1, nsteps - 1), rb1, rs1);
+  store_a(0);
+  for (int s0 = 0;; s0 += 3) {
+    body(s0, rb0, rs0, rb2, rs2);
+    if (s0 + 1 >= nsteps) break;
+    body(s0 + 1, rb1, rs1, rb0, rs0);
+    if (s0 + 2 >= nsteps) break;
+    body(s0 + 2, rb2, rs2, rb1, rs1);
+    if (s0 + 3 >= nsteps) break;
+  }
+}
+
 template <int PHASE>
 __global__ __launch_bounds__(256, 2) void ffn_prefill_kernel(PrefillArgs p) {
   constexpr bool kPair = PHASE == 1;
-  __shared__ __attribute__((aligned(16))) f16 sA[2][kPM * kPLda];
-  __shared__ __attribute__((aligned(16))) f16 sB[2][kPN * kPLda];
+  __shared__ __attribute__((aligned(1024))) f16 sA[2 * kPStage];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wid = tid / kWave;
-  const int wm = wid >> 1, wn = wid & 1;          // 2 x 2 waves: 64 rows x 128 cols each
+  const int wv = tid / kWave;
+  const int h = lane >> 5, l32 = lane & 31;
   const int K = kPair ? p.H : p.F;
   const int Nrows = kPair ? p.F : p.H;            // rows of one weight matrix
   const int G = K / kGroup;
@@ -99,124 +217,79 @@ __global__ __launch_bounds__(256, 2) void ffn_prefill_kernel(PrefillArgs p) {
   const int slot = logical / p.ntiles, nt = logical % p.ntiles;
   int e, mt;
   if (!locate_tile128(p.offsets, p.E, slot, &e, &mt)) return;
+  e = __builtin_amdgcn_readfirstlane(e);      // block-uniform: buffer bases go in SGPRs
+  mt = __builtin_amdgcn_readfirstlane(mt);
   const int seg0 = p.offsets[e] + mt * kPM;
   if (seg0 < 0 || seg0 >= p.N) return;
   const int rows = min(min(kPM, p.offsets[e + 1] - seg0), p.N - seg0);
 
-  // ---- loader assignments
-  // A: thread -> token row tid/2, 16 halfs at k offset (tid&1)*16
-  const int a_row = tid >> 1, a_k = (tid & 1) * 16;
-  int a_src = seg0 + min(a_row, rows - 1);
-  if (p.perm_src) {
-    a_src = p.perm_src[a_src] / p.k;
-    a_src = a_src < 0 ? 0 : (a_src >= p.T ? p.T - 1 : a_src);
-  }
-  const f16 *a_ptr = p.a + (size_t)a_src * K + a_k;
-  // B: thread -> 16-row storage tile tt = tid/16, row r = tid%16; 16 bytes
-  // (32 codes) of chunk (4g + step) per K step
-  const int tt = tid >> 4, br = tid & 15;
-  int b_lds_row, w_row;
-  const uint8_t *qbase;
-  const f16 *sbase;
-  if (kPair) {
-    const int mat = (tt >> 2) & 1;                 // 0 gate, 1 up
-    const int ftile = (tt >> 3) * 4 + (tt & 3);    // 16-row tile among the 128 f values
-    w_row = nt * 128 + ftile * 16;                 // first row of the storage tile
-    b_lds_row = ((tt >> 3) * 128) + mat * 64 + (tt & 3) * 16 + br;
-    qbase = mat ? p.q1 : p.q0;
-    sbase = mat ? p.s1 : p.s0;
-  } else {
-    w_row = nt * kPN + tt * 16;
-    b_lds_row = tt * 16 + br;
-    qbase = p.q0;
-    sbase = p.s0;
-  }
-  const size_t mat_row0 = (size_t)e * Nrows + w_row;
-  const uint8_t *b_ptr = qbase + mat_row0 * (K / 2) + br * 16;   // + chunk * 256
-  const f16 *s_ptr = sbase + mat_row0 * G + br;                   // + g * 16
-
-  const UnpackConsts kc = unpack_consts();
-  const int nsteps = K / kPK;
-
-  u32x4 ra0, ra1, rb;
-  f16 rs;
-  auto gload = [&](int step) {
-    const int k0 = step * kPK;
-    ra0 = ld16(a_ptr + k0);
-    ra1 = ld16(a_ptr + k0 + 8);
-    rb = ld16(b_ptr + (size_t)step * 256);     // chunk index = step (4 chunks per group)
-    rs = s_ptr[(size_t)(step >> 2) * 16];
-  };
-  auto lstore = [&](int buf) {
-    *reinterpret_cast<u32x4 *>(&sA[buf][a_row * kPLda + a_k]) = ra0;
-    *reinterpret_cast<u32x4 *>(&sA[buf][a_row * kPLda + a_k + 8]) = ra1;
-    const f16x2 sc = {rs, rs};
-    f16 *dst = &sB[buf][b_lds_row * kPLda];
+  PrefillOperands o;
+  o.nsteps = K / kPK;
+  // ---- activation pieces: piece j of wave wv's lane i is stored at row
+  // 32*wv + 8*j + i/8, position i%8 of a stage (the wave's 64 lanes fill
+  // 1 KB contiguously), which holds logical piece (i%8) ^ (i/8).  Rows past
+  // the segment repeat its last row (their outputs are never stored).
+  const int a_rows = p.perm_src ? p.T : p.N;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      f16x8 c = unpack8(rb[w], kc);
-      u32x4 o;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f16x2 pr = {c[2 * j], c[2 * j + 1]};
-        o[j] = as_u32(pr * sc);                    // RN16(q * s)
-      }
-      *reinterpret_cast<u32x4 *>(dst + w * 8) = o;
+  for (int j = 0; j < 4; ++j) {
+    const int r = 32 * wv + 8 * j + (lane >> 3);
+    int src = seg0 + min(r, rows - 1);
+    if (p.perm_src) {
+      src = p.perm_src[src] / p.k;
+      src = src < 0 ? 0 : (src >= p.T ? p.T - 1 : src);
     }
-  };
-
-  f32x16 acc[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){};
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  const int lrow = lane & 31, lk = (lane >> 5) * 8;
-  for (int step = 0; step < nsteps; ++step) {
-    const int buf = step & 1;
-    if (step + 1 < nsteps) gload(step + 1);
-#pragma unroll
-    for (int ks = 0; ks < kPK; ks += 16) {
-      f16x8 af[2], bf[4];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        af[i] = *reinterpret_cast<const f16x8 *>(
-            &sA[buf][(wm * 64 + i * 32 + lrow) * kPLda + ks + lk]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bf[j] = *reinterpret_cast<const f16x8 *>(
-            &sB[buf][(wn * 128 + j * 32 + lrow) * kPLda + ks + lk]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_32x32x16(af[i], bf[j], acc[i][j]);
-    }
-    if (step + 1 < nsteps) lstore(buf ^ 1);
-    __syncthreads();
+    o.a_off[j] = ((uint32_t)src * K + ((lane & 7) ^ (lane >> 3)) * 8) * 2;
   }
+  o.a_dst = 32 * wv * kPK + lane * 8;
+  const rsrc_t a_rs = make_rsrc(p.a, (uint32_t)a_rows * K * 2);
+
+  // ---- operand reads: for k16 sub-step w, lane l supplies row 32*i + l%32 at
+  // logical piece 4*(l/32) + w, i.e. k = 32*(l/32) + 8*w .. +7 of the step
+#pragma unroll
+  for (int w = 0; w < 4; ++w) o.a_rd[w] = l32 * kPK + (((4 * h + w) ^ (lane & 7)) * 8);
+
+  // ---- weights: N-tile j of wave wv is 32 weight rows of one matrix of
+  // expert e; per step lane l loads the 16-byte chunk 2*step + l/32 of row
+  // l%32, whose word w holds the same k = 32*(l/32) + 8*w .. +7 of the step
+  // as the activation operand.
+  const size_t mat_codes = (size_t)Nrows * (K / 2), mat_scales = (size_t)Nrows * G;
+  const uint8_t *qb0 = p.q0 + (size_t)e * mat_codes;
+  const uint8_t *qb1 = (kPair ? p.q1 : p.q0) + (size_t)e * mat_codes;
+  const f16 *sb0 = p.s0 + (size_t)e * mat_scales;
+  const f16 *sb1 = (kPair ? p.s1 : p.s0) + (size_t)e * mat_scales;
+  const rsrc_t b_rs0 = make_rsrc(qb0, (uint32_t)mat_codes);
+  const rsrc_t b_rs1 = make_rsrc(qb1, (uint32_t)mat_codes);
+  const rsrc_t s_rs0 = make_rsrc(sb0, (uint32_t)(mat_scales * 2));
+  const rsrc_t s_rs1 = make_rsrc(sb1, (uint32_t)(mat_scales * 2));
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = kPair ? nt * 128 + wv * 32 + l32 : nt * kPN + wv * 64 + j * 32 + l32;
+    o.b_off[j] = (uint32_t)(n >> 4) * 8 * K + h * 256 + (n & 15) * 16;
+    o.s_off[j] = ((uint32_t)(n >> 4) * 16 * G + (n & 15)) * 2;
+  }
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = (f32x16){};
+  prefill_gemm(sA, a_rs, b_rs0, b_rs1, s_rs0, s_rs1, o, acc);
 
   // ---- epilogue: D register r of lane l is row 8*(r/4) + 4*(l/32) + r%4,
   // column l%32 of its 32x32 tile
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int m = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      const int m = i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
       if (m >= rows) continue;
       f16 *orow = p.out + (size_t)(seg0 + m) * Nrows;
       if (kPair) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const float g = acc[i][j][r], u = acc[i][j + 2][r];
-          const int f = nt * 128 + wn * 64 + j * 32 + (lane & 31);
-          orow[f] = (f16)(g / (1.0f + expf(-g)) * u);
-        }
+        const float g = acc[i][0][r], u = acc[i][1][r];
+        orow[nt * 128 + wv * 32 + l32] = (f16)(g / (1.0f + expf(-g)) * u);
       } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) orow[nt * kPN + wn * 128 + j * 32 + (lane & 31)] = (f16)acc[i][j][r];
+        for (int j = 0; j < 2; ++j) orow[nt * kPN + wv * 64 + j * 32 + l32] = (f16)acc[i][j][r];
       }
     }
   }
