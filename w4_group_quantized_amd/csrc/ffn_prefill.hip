@@ -9,23 +9,28 @@
 //
 // Block tile: 128 token rows (one segment tile of one expert) x 256 weight
 // rows, K step 64, 4 waves.  The activation tile goes through LDS: each K
-// step's 128 x 64 fp16 tile is copied by direct global->LDS loads into one of
-// three stage buffers, two steps ahead of its use.  The weights do not touch
-// LDS: wave w owns 64 weight rows and loads their int4 codes straight into
-// registers (16 bytes per lane per 32 rows per K step, also two steps ahead),
+// step's 128 x 64 fp16 tile is loaded into registers one step ahead and
+// stored into one of two LDS stages.  The weights do not touch LDS: wave w
+// owns 64 weight rows and loads their int4 codes straight into registers
+// (16 bytes per lane per 32 rows per K step, two steps ahead),
 // unpacks them with the group scale folded in (RN16(q*s)) and feeds them as
-// the B operand, so every weight is read from memory and unpacked exactly
-// once per block.  Each wave multiplies all 128 token rows by its 64 weight
-// rows: 4 x 2 accumulators of 32 x 32.
+// the MFMA's A operand, so every weight is read from memory and unpacked
+// exactly once per block.  Each wave multiplies its 64 weight rows by all 128
+// token rows: 4 x 2 accumulators of 32 x 32, holding the output transposed,
+// which gives each lane 4 consecutive output columns of a token row per
+// store.
 //
 // Phase 1 gives wave w gate rows and up rows of the same 32 ffn columns, so
 // silu(g) * u is formed in registers.
 //
 // LDS layout of one stage: 128 rows of 128 bytes (64 halfs); the eight 16-byte
-// pieces of row r are stored XOR-swizzled (piece p at position p ^ (r % 8)),
-// which keeps both the direct loads (1 KB contiguous per wave instruction)
-// and the MFMA operand reads (32 rows x 16 bytes per half wave) free of bank
-// conflicts.
+// pieces of row r are stored XOR-swizzled, piece p at position p ^ sw(r) with
+// sw(r) = (r % 8) ^ ((r / 8) % 2).  The stores are 1 KB contiguous per wave
+// instruction; for the MFMA operand reads (16 bytes of 16 consecutive rows
+// per quarter wave) the swizzle spreads any 8 consecutive rows, and the 8
+// even and the 8 odd rows of any 16, over distinct 16-byte bank groups, so
+// they are free of bank conflicts whether the LDS serves 8 or 16 lanes of a
+// 16-byte read per cycle.
 #include "common.h"
 #include "kernels.h"
 
@@ -47,18 +52,28 @@ struct PrefillArgs {
   const f16 *s0, *s1;
   f16 *out;                   // phase 1: h [N, F]; phase 2: y_perm [N, H]
   int ntiles;                 // weight-row tiles per segment tile
-  int nblocks;                // grid size (a multiple of 8)
 };
 
 __device__ __forceinline__ f32x16 mfma_32x32x16(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-// Which expert and which 128-row tile of its segment is segment tile `slot`?
-__device__ bool locate_tile128(const int32_t *__restrict__ off, int E, int slot, int *e_out,
-                               int *mt_out) {
+// The block's tile.  The routed rows of each expert are split into 128-row
+// segment tiles; the (segment tile, weight-row tile) pairs are numbered in
+// order and each XCD gets a contiguous run of that numbering of equal length
+// (the hardware deals consecutive blocks round-robin over the 8 XCDs), so
+// the blocks that share a segment tile's activations share an L2 and every
+// XCD has the same amount of work.  Returns false (for the whole block) for
+// blocks beyond the real number of pairs.
+struct TileInfo {
+  int e;          // expert
+  int seg0;       // first permuted row of the segment tile
+  int seg_end;    // end of the expert's segment
+  int nt;         // weight-row tile
+};
+__device__ bool locate_tile(const int32_t *__restrict__ off, int E, int ntiles, TileInfo *t) {
   __shared__ int s_scan[4];
-  __shared__ int s_res[2];
+  __shared__ int s_res[3];
   const int tid = threadIdx.x;
   int o[5];
 #pragma unroll
@@ -71,20 +86,27 @@ __device__ bool locate_tile128(const int32_t *__restrict__ off, int E, int slot,
   }
   int total;
   int run = block_excl_scan(sum, s_scan, &total);
-  if (tid == 0) s_res[0] = -1;
-  __syncthreads();
+  const int nvalid = total * ntiles;
+  const int per_xcd = (nvalid + 7) / 8;
+  const int idx = blockIdx.x / 8;
+  const int logical = (blockIdx.x % 8) * per_xcd + idx;
+  if (idx >= per_xcd || logical >= nvalid) return false;
+  const int slot = logical / ntiles;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (slot >= run && slot < run + c[i]) {
       s_res[0] = 4 * tid + i;
-      s_res[1] = slot - run;
+      s_res[1] = o[i] + (slot - run) * kPM;
+      s_res[2] = o[i + 1];
     }
     run += c[i];
   }
   __syncthreads();
-  *e_out = s_res[0];
-  *mt_out = s_res[1];
-  return s_res[0] >= 0;
+  t->e = __builtin_amdgcn_readfirstlane(s_res[0]);   // block-uniform: bases go in SGPRs
+  t->seg0 = __builtin_amdgcn_readfirstlane(s_res[1]);
+  t->seg_end = __builtin_amdgcn_readfirstlane(s_res[2]);
+  t->nt = logical % ntiles;
+  return true;
 }
 
 // All LDS operations of this wave are done; meet the other waves of the
@@ -178,7 +200,7 @@ __device__ __forceinline__ void prefill_gemm(f16 *sA, rsrc_t a_rs, rsrc_t b_rs0,
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_32x32x16(af[i], bf[j], acc[i][j]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_32x32x16(bf[j], af[i], acc[i][j]);
     }
     if (step + 1 < nsteps) store_a(step + 1);
   };
@@ -209,25 +231,17 @@ __global__ __launch_bounds__(256, 2) void ffn_prefill_kernel(PrefillArgs p) {
   const int Nrows = kPair ? p.F : p.H;            // rows of one weight matrix
   const int G = K / kGroup;
 
-  // XCD-aware order: hardware round-robins consecutive blocks over the 8
-  // XCDs; give each XCD a contiguous run of logical tiles so the blocks that
-  // share a segment tile's activations share an L2.
-  const int per_xcd = p.nblocks / 8;
-  const int logical = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  const int slot = logical / p.ntiles, nt = logical % p.ntiles;
-  int e, mt;
-  if (!locate_tile128(p.offsets, p.E, slot, &e, &mt)) return;
-  e = __builtin_amdgcn_readfirstlane(e);      // block-uniform: buffer bases go in SGPRs
-  mt = __builtin_amdgcn_readfirstlane(mt);
-  const int seg0 = p.offsets[e] + mt * kPM;
+  TileInfo ti;
+  if (!locate_tile(p.offsets, p.E, p.ntiles, &ti)) return;
+  const int e = ti.e, seg0 = ti.seg0, nt = ti.nt;
   if (seg0 < 0 || seg0 >= p.N) return;
-  const int rows = min(min(kPM, p.offsets[e + 1] - seg0), p.N - seg0);
+  const int rows = min(min(kPM, ti.seg_end - seg0), p.N - seg0);
 
   PrefillOperands o;
   o.nsteps = K / kPK;
   // ---- activation pieces: piece j of wave wv's lane i is stored at row
-  // 32*wv + 8*j + i/8, position i%8 of a stage (the wave's 64 lanes fill
-  // 1 KB contiguously), which holds logical piece (i%8) ^ (i/8).  Rows past
+  // r = 32*wv + 8*j + i/8, position i%8 of a stage (the wave's 64 lanes fill
+  // 1 KB contiguously), which holds logical piece (i%8) ^ sw(r).  Rows past
   // the segment repeat its last row (their outputs are never stored).
   const int a_rows = p.perm_src ? p.T : p.N;
 #pragma unroll
@@ -238,7 +252,7 @@ __global__ __launch_bounds__(256, 2) void ffn_prefill_kernel(PrefillArgs p) {
       src = p.perm_src[src] / p.k;
       src = src < 0 ? 0 : (src >= p.T ? p.T - 1 : src);
     }
-    o.a_off[j] = ((uint32_t)src * K + ((lane & 7) ^ (lane >> 3)) * 8) * 2;
+    o.a_off[j] = ((uint32_t)src * K + ((lane & 7) ^ (lane >> 3) ^ (j & 1)) * 8) * 2;
   }
   o.a_dst = 32 * wv * kPK + lane * 8;
   const rsrc_t a_rs = make_rsrc(p.a, (uint32_t)a_rows * K * 2);
@@ -246,7 +260,8 @@ __global__ __launch_bounds__(256, 2) void ffn_prefill_kernel(PrefillArgs p) {
   // ---- operand reads: for k16 sub-step w, lane l supplies row 32*i + l%32 at
   // logical piece 4*(l/32) + w, i.e. k = 32*(l/32) + 8*w .. +7 of the step
 #pragma unroll
-  for (int w = 0; w < 4; ++w) o.a_rd[w] = l32 * kPK + (((4 * h + w) ^ (lane & 7)) * 8);
+  for (int w = 0; w < 4; ++w)
+    o.a_rd[w] = l32 * kPK + (((4 * h + w) ^ (lane & 7) ^ ((lane >> 3) & 1)) * 8);
 
   // ---- weights: N-tile j of wave wv is 32 weight rows of one matrix of
   // expert e; per step lane l loads the 16-byte chunk 2*step + l/32 of row
@@ -275,21 +290,35 @@ __global__ __launch_bounds__(256, 2) void ffn_prefill_kernel(PrefillArgs p) {
     for (int j = 0; j < 2; ++j) acc[i][j] = (f32x16){};
   prefill_gemm(sA, a_rs, b_rs0, b_rs1, s_rs0, s_rs1, o, acc);
 
-  // ---- epilogue: D register r of lane l is row 8*(r/4) + 4*(l/32) + r%4,
-  // column l%32 of its 32x32 tile
+  // ---- epilogue.  The weights are the MFMA's A operand, so accumulator
+  // acc[i][j] holds the transposed 32 x 32 tile: register r of lane l is
+  // weight row 8*(r/4) + 4*(l/32) + r%4 of N-tile j and token row l%32 of
+  // M-tile i.  Registers 4q .. 4q+3 are 4 consecutive output columns of one
+  // token row: one 8-byte store.
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    const int m = i * 32 + l32;
+    if (m >= rows) continue;
+    f16 *orow = p.out + (size_t)(seg0 + m) * Nrows;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-      if (m >= rows) continue;
-      f16 *orow = p.out + (size_t)(seg0 + m) * Nrows;
+    for (int q = 0; q < 4; ++q) {
+      f16 v[4];
       if (kPair) {
-        const float g = acc[i][0][r], u = acc[i][1][r];
-        orow[nt * 128 + wv * 32 + l32] = (f16)(g / (1.0f + expf(-g)) * u);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float g = acc[i][0][4 * q + t], u = acc[i][1][4 * q + t];
+          v[t] = (f16)(g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u);   // silu(g) * u
+        }
+        *reinterpret_cast<uint2 *>(orow + nt * 128 + wv * 32 + 8 * q + 4 * h) =
+            __builtin_bit_cast(uint2, v);
       } else {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) orow[nt * kPN + wv * 64 + j * 32 + l32] = (f16)acc[i][j][r];
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) v[t] = (f16)acc[i][j][4 * q + t];
+          *reinterpret_cast<uint2 *>(orow + nt * kPN + wv * 64 + j * 32 + 8 * q + 4 * h) =
+              __builtin_bit_cast(uint2, v);
+        }
       }
     }
   }
@@ -318,7 +347,6 @@ hipError_t launch_ffn_prefill_phase(const moe_layer &L, int phase, const uint16_
   const int max_tiles = (E < N ? E : N) + (N + kPM - 1) / kPM;
   int blocks = max_tiles * p.ntiles;
   blocks = (blocks + 7) / 8 * 8;
-  p.nblocks = blocks;
   if (phase == 1)
     hipLaunchKernelGGL(ffn_prefill_kernel<1>, dim3(blocks), dim3(256), 0, st, p);
   else
