@@ -146,15 +146,20 @@ struct PrefillOperands {
 // scales of step s + 2 (clamped to the last step; surplus loads are never
 // used), run 4 k16 sub-steps of 8 MFMAs on LDS stage s % 2, then store the
 // step s + 1 pieces into the other stage.  Code/scale registers rotate with
-// period 3, hence the loop unrolled by 3.
+// period 3, hence the loop unrolled by 3.  MI (1..4) is the number of 32-row
+// M-tiles holding real rows: the last tile of a segment skips the MFMAs and
+// activation loads of its empty M-tiles (wave w loads the rows of M-tile w).
+template <int MI>
 __device__ __forceinline__ void prefill_gemm(f16 *sA, rsrc_t a_rs, rsrc_t b_rs0, rsrc_t b_rs1,
                                              rsrc_t s_rs0, rsrc_t s_rs1,
-                                             const PrefillOperands &o, f32x16 (&acc)[4][2]) {
+                                             const PrefillOperands &o, bool a_loader,
+                                             f32x16 (&acc)[MI][2]) {
   u32x4 ra[4];                      // activation pieces of the next step
   u32x4 rb0[2], rb1[2], rb2[2];     // code chunks of the three steps in flight
   f16 rs0[2], rs1[2], rs2[2];       // their group scales
   const int nsteps = o.nsteps;
   auto load_a = [&](int step) {
+    if (!a_loader) return;
 #pragma unroll
     for (int j = 0; j < 4; ++j) ra[j] = bload16(a_rs, o.a_off[j], step * (kPK * 2));
   };
@@ -165,6 +170,7 @@ __device__ __forceinline__ void prefill_gemm(f16 *sA, rsrc_t a_rs, rsrc_t b_rs0,
     rs[1] = bload_f16(s_rs1, o.s_off[1], (step >> 1) * 32);
   };
   auto store_a = [&](int step) {
+    if (!a_loader) return;
     f16 *dst = sA + (step & 1) * kPStage + o.a_dst;
 #pragma unroll
     for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4 *>(dst + j * 8 * kPK) = ra[j];
@@ -193,12 +199,12 @@ __device__ __forceinline__ void prefill_gemm(f16 *sA, rsrc_t a_rs, rsrc_t b_rs0,
         }
         bf[j] = as_f16x8(v);
       }
-      f16x8 af[4];
+      f16x8 af[MI];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < MI; ++i)
         af[i] = *reinterpret_cast<const f16x8 *>(as + i * 32 * kPK + o.a_rd[w]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma_32x32x16(bf[j], af[i], acc[i][j]);
     }
@@ -216,6 +222,58 @@ __device__ __forceinline__ void prefill_gemm(f16 *sA, rsrc_t a_rs, rsrc_t b_rs0,
     if (s0 + 2 >= nsteps) break;
     body(s0 + 2, rb2, rs2, rb1, rs1);
     if (s0 + 3 >= nsteps) break;
+  }
+}
+
+// Accumulate one block tile with MI live M-tiles and store it.
+template <int PHASE, int MI>
+__device__ __forceinline__ void prefill_tile(const PrefillArgs &p, f16 *sA, rsrc_t a_rs,
+                                             rsrc_t b_rs0, rsrc_t b_rs1, rsrc_t s_rs0,
+                                             rsrc_t s_rs1, const PrefillOperands &o, int seg0,
+                                             int rows, int nt) {
+  constexpr bool kPair = PHASE == 1;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int Nrows = kPair ? p.F : p.H;
+  f32x16 acc[MI][2];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = (f32x16){};
+  prefill_gemm<MI>(sA, a_rs, b_rs0, b_rs1, s_rs0, s_rs1, o, wv < MI, acc);
+
+  // ---- epilogue.  The weights are the MFMA's A operand, so accumulator
+  // acc[i][j] holds the transposed 32 x 32 tile: register r of lane l is
+  // weight row 8*(r/4) + 4*(l/32) + r%4 of N-tile j and token row l%32 of
+  // M-tile i.  Registers 4q .. 4q+3 are 4 consecutive output columns of one
+  // token row: one 8-byte store.
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int m = i * 32 + l32;
+    if (m >= rows) continue;
+    f16 *orow = p.out + (size_t)(seg0 + m) * Nrows;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f16 v[4];
+      if (kPair) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float g = acc[i][0][4 * q + t], u = acc[i][1][4 * q + t];
+          v[t] = (f16)(g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u);   // silu(g) * u
+        }
+        *reinterpret_cast<uint2 *>(orow + nt * 128 + wv * 32 + 8 * q + 4 * h) =
+            __builtin_bit_cast(uint2, v);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) v[t] = (f16)acc[i][j][4 * q + t];
+          *reinterpret_cast<uint2 *>(orow + nt * kPN + wv * 64 + j * 32 + 8 * q + 4 * h) =
+              __builtin_bit_cast(uint2, v);
+        }
+      }
+    }
   }
 }
 
@@ -283,45 +341,15 @@ __global__ __launch_bounds__(256, 2) void ffn_prefill_kernel(PrefillArgs p) {
     o.s_off[j] = ((uint32_t)(n >> 4) * 16 * G + (n & 15)) * 2;
   }
 
-  f32x16 acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = (f32x16){};
-  prefill_gemm(sA, a_rs, b_rs0, b_rs1, s_rs0, s_rs1, o, acc);
-
-  // ---- epilogue.  The weights are the MFMA's A operand, so accumulator
-  // acc[i][j] holds the transposed 32 x 32 tile: register r of lane l is
-  // weight row 8*(r/4) + 4*(l/32) + r%4 of N-tile j and token row l%32 of
-  // M-tile i.  Registers 4q .. 4q+3 are 4 consecutive output columns of one
-  // token row: one 8-byte store.
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = i * 32 + l32;
-    if (m >= rows) continue;
-    f16 *orow = p.out + (size_t)(seg0 + m) * Nrows;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      f16 v[4];
-      if (kPair) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const float g = acc[i][0][4 * q + t], u = acc[i][1][4 * q + t];
-          v[t] = (f16)(g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u);   // silu(g) * u
-        }
-        *reinterpret_cast<uint2 *>(orow + nt * 128 + wv * 32 + 8 * q + 4 * h) =
-            __builtin_bit_cast(uint2, v);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-#pragma unroll
-          for (int t = 0; t < 4; ++t) v[t] = (f16)acc[i][j][4 * q + t];
-          *reinterpret_cast<uint2 *>(orow + nt * kPN + wv * 64 + j * 32 + 8 * q + 4 * h) =
-              __builtin_bit_cast(uint2, v);
-        }
-      }
-    }
-  }
+  const int mi = (rows + 31) / 32;
+  if (mi >= 4)
+    prefill_tile<PHASE, 4>(p, sA, a_rs, b_rs0, b_rs1, s_rs0, s_rs1, o, seg0, rows, nt);
+  else if (mi == 3)
+    prefill_tile<PHASE, 3>(p, sA, a_rs, b_rs0, b_rs1, s_rs0, s_rs1, o, seg0, rows, nt);
+  else if (mi == 2)
+    prefill_tile<PHASE, 2>(p, sA, a_rs, b_rs0, b_rs1, s_rs0, s_rs1, o, seg0, rows, nt);
+  else
+    prefill_tile<PHASE, 1>(p, sA, a_rs, b_rs0, b_rs1, s_rs0, s_rs1, o, seg0, rows, nt);
 }
 
 hipError_t launch_ffn_prefill_phase(const moe_layer &L, int phase, const uint16_t *a,
