@@ -79,6 +79,8 @@ ROUTE_CASES = [
     ("decode_fine", {}, 37),
     ("decode_coarse", {}, 16),
     ("prefill", {}, 300),
+    ("decode_fine", {}, 333),      # 32-token x 128-expert tiles: 3 expert tiles, last one partial
+    ("tiny", {}, 257),             # same tiles with 8 experts and a ragged token tail
 ]
 
 
@@ -155,6 +157,9 @@ PERM_CASES = [
     (50, 1, 6, "one_expert"),
     (7, 5, 5, "k_eq_E"),
     (1000, 4, 1024, "random"),
+    (8192, 8, 128, "random"),      # prefill size: 256 chunks split over 8 scan threads per expert
+    (5000, 3, 3, "random"),        # 256 scan threads per expert
+    (600, 1, 1, "random"),        # a single expert
 ]
 
 

@@ -12,6 +12,7 @@ namespace moe {
 constexpr int kPermChunk = 256;   // flat (token, slot) entries per permutation block
 constexpr int kGroupSize = 128;   // the only group size the kernels implement
 constexpr int kFusedMaxT = 64;    // route + permute in one launch up to this many tokens
+constexpr int kRouterWideMinT = 256;   // 32-token x 128-expert router tiles from this many tokens
 constexpr int kFusedMaxKsb = 16;  // K parts of the fused router's logits
 constexpr int kFusedMaxLogits = 8192;   // T * E held in LDS by the fused router
 

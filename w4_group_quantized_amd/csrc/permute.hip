@@ -7,7 +7,8 @@
 // increasing f, which makes offsets, perm_src and inv_pos unique.
 //
 //   count:   one block per chunk of kPermChunk entries, LDS histogram
-//   scan:    one block: per-expert totals -> offsets, per-chunk bases
+//   scan:    one block: per-expert totals -> offsets, per-chunk bases, the
+//            chunks of each expert split over 1024 / E threads
 //   scatter: one wave per chunk; ranks within a wave by matching expert ids
 //            through ballots over their bits, in flat order
 //   gather:  x_perm[r] = x[perm_src[r] / k], 16-byte copies (optional: the
@@ -33,27 +34,51 @@ __global__ __launch_bounds__(256) void perm_count_kernel(const int32_t *__restri
     counts[(size_t)blockIdx.x * E + e] = hist[e];
 }
 
-// blockDim.x = 1024 >= E
+// One block of 1024 threads.  Thread (p, e) = (tid / Ep, tid % Ep), Ep the
+// power of two >= E: the P = 1024 / Ep threads of expert e each sum the
+// counts of a contiguous range of chunks; their partial sums give each
+// thread the expert's total and the count before its range, the totals are
+// scanned over experts (offsets), and each thread then writes the running
+// bases of its chunks.
 __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t *__restrict__ counts,
-                                                         int nchunks, int E, int N,
+                                                         int nchunks, int E, int Ep,
                                                          int32_t *__restrict__ offsets,
                                                          int32_t *__restrict__ bases) {
+  __shared__ int part[1024];
+  __shared__ int s_off[kMaxExperts];
   __shared__ int scratch[16];
-  const int e = threadIdx.x;
-  int tot = 0;
+  const int tid = threadIdx.x;
+  const int P = 1024 / Ep;
+  const int e = tid % Ep, pp = tid / Ep;
+  const int c0 = (int)((int64_t)pp * nchunks / P), c1 = (int)((int64_t)(pp + 1) * nchunks / P);
+  int sum = 0;
   if (e < E)
-    for (int c = 0; c < nchunks; ++c) tot += counts[(size_t)c * E + e];
+    for (int c = c0; c < c1; ++c) sum += counts[(size_t)c * E + e];
+  part[tid] = sum;
+  __syncthreads();
+  int pre = 0, tot = 0;
+  if (e < E)
+    for (int q = 0; q < P; ++q) {
+      const int v = part[q * Ep + e];
+      pre += q < pp ? v : 0;
+      tot += v;
+    }
   int total;
-  const int excl = block_excl_scan(tot, scratch, &total);
-  if (e < E) {
+  const int excl = block_excl_scan(pp == 0 && e < E ? tot : 0, scratch, &total);
+  if (pp == 0 && e < E) {
+    s_off[e] = excl;
     offsets[e] = excl;
-    int run = excl;
-    for (int c = 0; c < nchunks; ++c) {
+  }
+  if (tid == 0) offsets[E] = total;
+  __syncthreads();
+  if (e < E) {
+    int run = s_off[e] + pre;
+    for (int c = c0; c < c1; ++c) {
+      const int v = counts[(size_t)c * E + e];
       bases[(size_t)c * E + e] = run;
-      run += counts[(size_t)c * E + e];
+      run += v;
     }
   }
-  if (e == 0) offsets[E] = total;
 }
 
 // One wave per chunk.
@@ -113,8 +138,10 @@ hipError_t launch_permute(const moe_layer &L, const uint16_t *x, const int32_t *
   hipLaunchKernelGGL(perm_count_kernel, dim3(nchunks), dim3(256), 0, st, idx, N, E, counts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, st, counts, nchunks, E, N, offsets,
-                     bases);
+  int Ep = 1;
+  while (Ep < E) Ep *= 2;
+  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, st, counts, nchunks, E, Ep,
+                     offsets, bases);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(perm_scatter_kernel, dim3(nchunks), dim3(64), 0, st, idx, N, E, bases,
                      perm_src, inv_pos);

@@ -120,6 +120,80 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const f16 *__restric
   }
 }
 
+// Prefill-sized batches: one block per 32 tokens x 128 experts; wave w owns
+// experts 32w .. 32w+31 of the block's expert tile and runs the whole K on
+// v_mfma_f32_32x32x16_f16 with both operands loaded straight from global
+// memory (the block's waves share the token rows through the caches), so x
+// is read from memory once instead of once per 16-expert tile.
+//
+// K is walked in 64-wide chunks; lane (row l%32, half l/32) loads the 64
+// contiguous bytes k = 32*(l/32) .. +31 of the chunk for its token row and
+// its expert row, and MFMA s of the chunk contracts piece s of both (k =
+// 8s .. 8s+7 and 32+8s .. 32+8s+7).  Four accumulators (one per piece) are
+// summed in a fixed order at the end.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+struct RouterChunk {
+  u32x4 x[4], w[4];
+};
+
+__global__ __launch_bounds__(256) void router_logits_wide_kernel(const f16 *__restrict__ x,
+                                                                 const f16 *__restrict__ wr,
+                                                                 const float *__restrict__ bias,
+                                                                 int T, int E, int H,
+                                                                 float *__restrict__ logits) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  const int etiles = (E + 127) / 128;
+  const int tok0 = (blockIdx.x / etiles) * 32;
+  const int e0 = (blockIdx.x % etiles) * 128 + wv * 32;
+  if (e0 >= E) return;
+  const int l32 = lane & 31, kh = lane >> 5;
+  // surplus token rows and expert rows repeat the last one; never stored
+  const f16 *xr = x + (size_t)min(tok0 + l32, T - 1) * H + kh * 32;
+  const f16 *wrr = wr + (size_t)min(e0 + l32, E - 1) * H + kh * 32;
+  const int C = H / 64;
+  auto load = [&](RouterChunk &c, int ci) {
+    const size_t k = (size_t)min(ci, C - 1) * 64;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      c.x[s] = ld16(xr + k + 8 * s);
+      c.w[s] = ld16(wrr + k + 8 * s);
+    }
+  };
+  f32x16 acc[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) acc[s] = (f32x16){};
+  auto compute = [&](const RouterChunk &c) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(c.x[s]), as_f16x8(c.w[s]), acc[s],
+                                                     0, 0, 0);
+  };
+  RouterChunk a, b;
+  load(a, 0);
+  int ci = 0;
+  for (; ci + 2 <= C; ci += 2) {
+    load(b, ci + 1);
+    sched_fence();
+    compute(a);
+    sched_fence();
+    load(a, ci + 2);
+    sched_fence();
+    compute(b);
+    sched_fence();
+  }
+  if (ci < C) compute(a);
+  // D register r of lane l: token row 8*(r/4) + 4*(l/32) + r%4, expert l%32
+  const int e = e0 + l32;
+  if (e >= E) return;
+  const float bb = bias ? bias[e] : 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int tok = tok0 + 8 * (r >> 2) + 4 * kh + (r & 3);
+    if (tok < T) logits[(size_t)tok * E + e] = ((acc[0][r] + acc[1][r]) + (acc[2][r] + acc[3][r])) + bb;
+  }
+}
+
 // One wave per token, 4 tokens per block.
 __global__ __launch_bounds__(256) void softmax_topk_kernel(const float *__restrict__ logits,
                                                            int T, int E, int k,
@@ -296,10 +370,17 @@ int fused_route_ksb(const moe_layer &L) {
 hipError_t launch_route(const moe_layer &L, const uint16_t *x, int32_t T, int32_t *idx,
                         float *w, float *logits, hipStream_t st) {
   const int E = L.num_experts, H = L.hidden;
-  const int blocks = ((T + 15) / 16) * ((E + 15) / 16);
-  hipLaunchKernelGGL(router_logits_kernel, dim3(blocks), dim3(256), 0, st,
-                     reinterpret_cast<const f16 *>(x),
-                     reinterpret_cast<const f16 *>(L.router_w), L.router_b, T, E, H, logits);
+  if (T >= kRouterWideMinT) {
+    const int blocks = ((T + 31) / 32) * ((E + 127) / 128);
+    hipLaunchKernelGGL(router_logits_wide_kernel, dim3(blocks), dim3(256), 0, st,
+                       reinterpret_cast<const f16 *>(x),
+                       reinterpret_cast<const f16 *>(L.router_w), L.router_b, T, E, H, logits);
+  } else {
+    const int blocks = ((T + 15) / 16) * ((E + 15) / 16);
+    hipLaunchKernelGGL(router_logits_kernel, dim3(blocks), dim3(256), 0, st,
+                       reinterpret_cast<const f16 *>(x),
+                       reinterpret_cast<const f16 *>(L.router_w), L.router_b, T, E, H, logits);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(softmax_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, st, logits, T, E,
