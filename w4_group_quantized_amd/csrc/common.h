@@ -64,6 +64,21 @@ __device__ __forceinline__ f16x8 unpack8(uint32_t w, const UnpackConsts &k) {
   return as_f16x8(r);
 }
 
+// Raw buffer over `bytes` bytes at `base` (gfx9 descriptor: stride 0, plain
+// dword data format).  Loads through it take a 32-bit per-lane byte offset
+// plus a wave-uniform one in an SGPR; offsets past `bytes` read zeros and
+// stores there are dropped.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ f16 bload_f16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(f16, __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0));
+}
+
 __device__ __forceinline__ u32x4 ldg16(const void *p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }

@@ -14,7 +14,9 @@
 // The phases are separate launches because phase 2 of an expert needs every
 // column of h for its rows.
 //
-// Work items (one 256-thread block each):
+// Work items (one 256-thread block each; the shared-expert items come first,
+// so they start with the first wave of blocks instead of waiting for slots
+// behind the routed ones):
 //   routed item = (segment tile, n-tile): a segment tile is 16 consecutive rows
 //     of one expert's segment; an n-tile is 64*NT weight rows; each of the 4
 //     waves streams 16*NT rows over the whole K range.
@@ -43,7 +45,8 @@ struct FfnArgs {
   const f16 *w0, *w1;               // shared expert fp16 weights (phase 2: w0 only)
   f16 *out_routed;                  // phase 1: h [N, F];      phase 2: y_perm [N, H]
   f16 *out_shared;                  // phase 1: h_shared;      phase 2: y_shared
-  int routed_items;                 // worst-case number of routed items
+  int shared_items;                 // shared-expert items (blocks 0 .. shared_items-1)
+  int routed_items;                 // worst-case number of routed items (the blocks after)
 };
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
@@ -99,9 +102,10 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
   const int G = K / kGroup;
   __shared__ float red[3 * 2 * 4 * kWave];
 
-  if ((int)blockIdx.x < p.routed_items) {
+  if ((int)blockIdx.x >= p.shared_items) {
+    const int item = blockIdx.x - p.shared_items;
     const int ntiles = Nrows / (64 * NT);
-    const int slot = blockIdx.x / ntiles, nt = blockIdx.x % ntiles;
+    const int slot = item / ntiles, nt = item % ntiles;
     int e, mt;
     if (!locate_tile(p.offsets, p.E, slot, &e, &mt)) return;
     const int seg0 = p.offsets[e] + mt * kTileM;
@@ -150,7 +154,7 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
   const int Ks = kPair ? p.H : p.Fs;
   const int Ns = kPair ? p.Fs : p.H;
   const int Gs = Ks / kGroup;
-  const int sitem = blockIdx.x - p.routed_items;
+  const int sitem = blockIdx.x;
   const int sntiles = Ns / 16;
   const int mt = sitem / sntiles, nt = sitem % sntiles;
   const int tok0 = mt * kTileM;
@@ -179,7 +183,7 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
 }
 
 #ifndef MOE_FFN_NT1
-#define MOE_FFN_NT1 2
+#define MOE_FFN_NT1 1
 #endif
 #ifndef MOE_FFN_NT2
 #define MOE_FFN_NT2 4
@@ -244,9 +248,9 @@ hipError_t launch_ffn(const moe_layer &L, const uint16_t *x, const uint16_t *x_p
   a.out_shared = reinterpret_cast<f16 *>(h_shared);
   static_assert(128 % (64 * kNT1) == 0, "F is a multiple of 128");
   a.routed_items = prefill ? 0 : max_tiles * (F / (64 * kNT1));
-  int shared_items = Fs ? mtiles_shared * (Fs / 16) : 0;
-  if (a.routed_items + shared_items > 0) {
-    hipLaunchKernelGGL((ffn_decode_kernel<1, kNT1, kS1>), dim3(a.routed_items + shared_items),
+  a.shared_items = Fs ? mtiles_shared * (Fs / 16) : 0;
+  if (a.routed_items + a.shared_items > 0) {
+    hipLaunchKernelGGL((ffn_decode_kernel<1, kNT1, kS1>), dim3(a.routed_items + a.shared_items),
                        dim3(256), 0, st, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
@@ -267,13 +271,13 @@ hipError_t launch_ffn(const moe_layer &L, const uint16_t *x, const uint16_t *x_p
   // 64*kNT2 down rows per block when H allows it, else 128
   const bool wide2 = H % (64 * kNT2) == 0;
   a.routed_items = prefill ? 0 : max_tiles * (H / (64 * (wide2 ? kNT2 : 2)));
-  shared_items = Fs ? mtiles_shared * (H / 16) : 0;
-  if (a.routed_items + shared_items > 0) {
+  a.shared_items = Fs ? mtiles_shared * (H / 16) : 0;
+  if (a.routed_items + a.shared_items > 0) {
     if (wide2)
-      hipLaunchKernelGGL((ffn_decode_kernel<2, kNT2, kS2>), dim3(a.routed_items + shared_items),
+      hipLaunchKernelGGL((ffn_decode_kernel<2, kNT2, kS2>), dim3(a.routed_items + a.shared_items),
                          dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((ffn_decode_kernel<2, 2, kS2>), dim3(a.routed_items + shared_items),
+      hipLaunchKernelGGL((ffn_decode_kernel<2, 2, kS2>), dim3(a.routed_items + a.shared_items),
                          dim3(256), 0, st, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }

@@ -116,21 +116,6 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-// Raw buffer over `bytes` bytes at `base` (gfx9 descriptor: stride 0, plain
-// dword data format).  Loads through it take a 32-bit per-lane byte offset
-// plus a wave-uniform one in an SGPR; offsets past `bytes` read zeros.
-__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
-__device__ __forceinline__ f16 bload_f16(rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(f16, __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0));
-}
-
 // Per-lane byte offsets of one block tile (step 0) and LDS offsets.
 struct PrefillOperands {
   uint32_t a_off[4];          // activation pieces in the activation buffer
