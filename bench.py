@@ -8,11 +8,16 @@ already resident in HBM.  Several
 independently drawn weight sets are rotated so that no expert byte is served
 from the 256 MB Infinity Cache across steps.  Prints ONE JSON line.
 
-`roofline` is for the dominant stage, the grouped FFN (its two launches,
-gate/up then down): algorithmic bytes = distinct experts with tokens in the
-step x bytes per expert (packed int4 + fp16 scales) + the fp16 shared expert,
-divided by the stage's average duration measured with HIP events on the
-launch stream inside the timed region.
+`roofline` is for the dominant stage, the grouped FFN (one
+moe_w4_grouped_ffn call: two launches, gate/up then down): decode: algorithmic
+bytes = distinct experts with tokens in the step x bytes per expert (packed
+int4 + fp16 scales) + the fp16 shared expert; prefill: algorithmic FLOPs =
+6*H*F per (token, chosen expert) pair; divided by the stage's average
+duration measured with HIP events on the launch stream inside the timed
+region.  `traffic` is the HBM bytes per call measured by rocprofv3 counters
+(profiles/traffic_<workload>.json, taken with --copy-calibration-mib and
+turned into bytes with --summarize-traffic), or null when the FFN sources
+have changed since.
 
 `cpu_baseline` times the float64 oracle (test infrastructure, run only in
 this leg) on a bounded sample of the same workload on the host cores.
@@ -47,10 +52,90 @@ def parse():
                     choices=["decode_fine", "decode_coarse", "prefill", "decode_stack", "tiny"])
     ap.add_argument("--weight-sets", type=int, default=0, help="0 = workload default")
     ap.add_argument("--batches", type=int, default=4, help="distinct token batches rotated")
-    ap.add_argument("--graph", action="store_true", help="replay the steps from a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the timed region, copy this many MiB 3 times (a plain copy "
+                         "kernel of known size, the reference for PMC byte counters)")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, "
+                         "WRITE_SIZE) of a run with --copy-calibration-mib into "
+                         "profiles/traffic_<workload>.json")
     return ap.parse_args()
+
+
+# ---------------------------------------------------------------- HBM traffic
+# Measured HBM bytes of the FFN come from rocprofv3 counter runs; they are
+# valid only for the kernel sources they were taken with.
+FFN_SOURCES = ("w4_group_quantized_amd/csrc/ffn.hip", "w4_group_quantized_amd/csrc/ffn_prefill.hip",
+               "w4_group_quantized_amd/csrc/tiles.h", "w4_group_quantized_amd/csrc/common.h")
+FFN_KERNELS = ("ffn_decode_kernel", "ffn_prefill_kernel")
+
+
+def ffn_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in FFN_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _pmc_rows(path, counter):
+    """(kernel name, value) per dispatch of one counter in a rocprofv3 CSV."""
+    import csv
+    out = []
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] == counter:
+                out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return out
+
+
+def summarize_traffic(workload, fetch_csv, write_csv, copy_mib):
+    """FFN HBM bytes per moe_w4_grouped_ffn call from FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch), each scaled by bytes/counter of the plain copy."""
+    res = {"workload": workload, "source_sha256": ffn_source_hash(), "copy_mib": copy_mib}
+    known = copy_mib * 1024 * 1024
+    for key, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        rows = _pmc_rows(path, counter)
+        # the calibration copies are the HIP runtime's device-to-device copy
+        # kernel (torch copies contiguous same-dtype tensors with it); they are
+        # the three largest dispatches of that kernel in the run
+        copies = sorted(v for n, v in rows if "copybuffer" in n.lower())
+        if len(copies) < 3:
+            raise SystemExit(f"{path}: calibration copy dispatches not found")
+        copy_kib = float(np.median(copies[-3:]))
+        factor = known / (copy_kib * 1024.0)
+        per_kernel = {}
+        for n, v in rows:
+            for k in FFN_KERNELS:
+                if k in n:
+                    per_kernel.setdefault(n, []).append(v)
+        if not per_kernel:
+            raise SystemExit(f"{path}: no FFN dispatch found")
+        call_kib = sum(float(np.mean(v)) for v in per_kernel.values())
+        res[key] = {"counter": counter, "copy_counter_kib": copy_kib, "bytes_per_counter_byte": factor,
+                    "ffn_kib_per_call": call_kib, "ffn_bytes_per_call": call_kib * 1024.0 * factor,
+                    "dispatches": {n: len(v) for n, v in per_kernel.items()}}
+    res["traffic_bytes_per_call"] = res["fetch"]["ffn_bytes_per_call"] + res["write"]["ffn_bytes_per_call"]
+    out = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    with open(out, "w") as fh:
+        json.dump(res, fh, indent=1)
+    print(json.dumps(res))
+
+
+def measured_traffic(workload):
+    """HBM bytes per FFN call measured for the current kernel sources, else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    try:
+        with open(path) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != ffn_source_hash():
+        return None
+    return float(t["traffic_bytes_per_call"])
 
 
 # ---------------------------------------------------------------- device weights
@@ -160,6 +245,10 @@ def cpu_baseline(cfg, budget_s):
 # ---------------------------------------------------------------- main
 def main():
     args = parse()
+    if args.summarize_traffic:
+        summarize_traffic(args.workload, args.summarize_traffic[0], args.summarize_traffic[1],
+                          args.copy_calibration_mib)
+        return
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
@@ -246,17 +335,28 @@ def main():
     # (gate, up, down), the shared expert 6*H*Fs per token
     ffn_flops = T * (cfg.top_k * 6.0 * cfg.hidden * cfg.ffn + 6.0 * cfg.hidden * cfg.shared_ffn)
     achieved_tflops = float(ffn_flops / (ffn_ms.mean() * 1e-3) / 1e12)
+    traffic = measured_traffic(cfg.name)
     if cfg.name == "prefill":
         roofline = {"bound": "mfma", "achieved": achieved_tflops, "peak": MFMA_F16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": achieved_tflops / MFMA_F16_PEAK_TFLOPS,
-                    "traffic": None}
+                    "traffic": traffic}
     else:
         roofline = {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None}
+                    "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic}
     roofline.update({"kernel": "moe_w4_grouped_ffn (gate/up launch + down launch)",
                      "ffn_us_mean": float(ffn_ms.mean() * 1e3),
                      "ffn_bytes_mean": float(ffn_bytes.mean()), "ffn_flops": ffn_flops,
                      "ffn_tflops": achieved_tflops, "ffn_gbs": achieved_gbs})
+
+    if args.copy_calibration_mib:
+        # a plain copy of known size for the PMC byte counters (not timed)
+        n = args.copy_calibration_mib * 1024 * 1024 // 2
+        src = torch.empty(n, dtype=torch.float16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
