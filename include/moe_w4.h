@@ -165,7 +165,8 @@ moe_status moe_route_permute(const moe_layer *layer, const uint16_t *x, int32_t 
  * every token of x, into y_shared.
  *   x         fp16 [T, H]   (needed when x_perm is NULL or shared_ffn > 0)
  *   x_perm    fp16 [T*k, H] or NULL;  perm_src int32 [T*k] (needed when
- *             x_perm is NULL);  offsets int32 [E+1] as written by moe_permute
+ *             x_perm is NULL; then T*H*2 must be below 2^31, else
+ *             MOE_EUNSUPPORTED);  offsets int32 [E+1] as written by moe_permute
  *             (offsets[0] = 0, non-decreasing, offsets[E] = T*k)
  *   y_perm    fp16 [T*k, H] out
  *   y_shared  fp16 [T, H] out, or NULL when shared_ffn = 0 */

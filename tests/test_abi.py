@@ -88,6 +88,9 @@ def test_other_calls_argument_errors():
                None) == EINVAL                        # no x_perm and no perm_src
     assert ffn(ctypes.byref(L), None, None, FAKE, FAKE, 4, FAKE, None, FAKE, big,
                None) == EINVAL                        # no x_perm and no x
+    T_far = (1 << 31) // (2 * L.hidden)   # gathering from x needs T*H*2 < 2^31
+    assert ffn(ctypes.byref(L), FAKE, None, FAKE, FAKE, T_far, FAKE, None, FAKE, big,
+               None) == EUNSUP
     Ls = layer(shared_ffn=256)       # shared expert declared but its weights missing
     assert ffn(ctypes.byref(Ls), FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, big,
                None) == EINVAL

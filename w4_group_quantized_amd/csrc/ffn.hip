@@ -112,13 +112,15 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
     // offsets come from device memory: keep every row inside [0, N)
     if (seg0 < 0 || seg0 >= p.N) return;
     const int rows = min(min(kTileM, p.offsets[e + 1] - seg0), p.N - seg0);
-    // token rows past the tile read a duplicate row; their outputs are dropped
-    int arow_idx = seg0 + min(r, rows - 1);
+    // lanes of token rows past the tile read zeros; their outputs are dropped
+    const bool live = r < rows;
+    int tok = min(r, rows - 1);
     if (p.perm_src) {            // gather straight from x: token of flat index perm_src[r]
-      arow_idx = p.perm_src[arow_idx] / p.k;
-      arow_idx = arow_idx < 0 ? 0 : (arow_idx >= p.T ? p.T - 1 : arow_idx);
+      tok = p.perm_src[seg0 + tok] / p.k;
+      tok = tok < 0 ? 0 : (tok >= p.T ? p.T - 1 : tok);
     }
-    const f16 *arow = p.a_routed + (size_t)arow_idx * K;
+    const ARows arow = p.perm_src ? ARows(p.a_routed, p.T, K, tok, live, kb)
+                                  : ARows(p.a_routed + (size_t)seg0 * K, rows, K, tok, live, kb);
     const uint8_t *qrow[kMats * NT];
     const f16 *srow[kMats * NT];
     int nrow[NT];
@@ -136,7 +138,7 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
     f32x4 acc[kMats * NT];
 #pragma unroll
     for (int t = 0; t < kMats * NT; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    w4_tiles<kMats * NT, S>(arow, qrow, srow, kb, 0, G, acc);
+    w4_tiles<kMats * NT, S>(arow, qrow, srow, 0, G, acc);
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -160,7 +162,7 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
   const int tok0 = mt * kTileM;
   if (tok0 >= p.T) return;
   const int rows = min(kTileM, p.T - tok0);
-  const f16 *arow = p.a_shared + (size_t)(tok0 + min(r, rows - 1)) * Ks;
+  const ARows arow(p.a_shared + (size_t)tok0 * Ks, rows, Ks, r, r < rows, kb);
   const int nrow = nt * 16 + r;
   const f16 *wrow[kMats];
   wrow[0] = p.w0 + (size_t)nrow * Ks;

@@ -168,6 +168,8 @@ moe_status moe_w4_grouped_ffn(const moe_layer *L, const uint16_t *x, const uint1
       !ok_ptr(L->up_q) || !ok_ptr(L->up_s) || !ok_ptr(L->down_q) || !ok_ptr(L->down_s))
     return MOE_EINVAL;
   if (x_perm ? !aligned16(x_perm) : (!ok_ptr(x) || !ok_ptr(perm_src))) return MOE_EINVAL;
+  // gathering rows straight from x addresses it with 32-bit byte offsets
+  if (!x_perm && (int64_t)T * L->hidden * 2 >= ((int64_t)1 << 31)) return MOE_EUNSUPPORTED;
   if (L->shared_ffn > 0 && (!ok_ptr(x) || !ok_ptr(y_shared) || !ok_ptr(L->shared_gate) ||
                             !ok_ptr(L->shared_up) || !ok_ptr(L->shared_down)))
     return MOE_EINVAL;

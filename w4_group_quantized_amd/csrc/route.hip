@@ -104,7 +104,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const f16 *__restric
   const int mt = blockIdx.x / etiles, et = blockIdx.x % etiles;
   const int tok0 = mt * 16;
   const int rows = min(16, T - tok0);
-  const f16 *arow = x + (size_t)(tok0 + min(r, rows - 1)) * H;   // surplus rows: duplicates, dropped
+  const ARows arow(x + (size_t)tok0 * H, rows, H, r, r < rows, kb);   // surplus rows read zeros
   const int e = et * 16 + r;
   const f16 *wrow[1] = {wr + (size_t)min(e, E - 1) * H};
   f32x4 acc[1] = {{0.f, 0.f, 0.f, 0.f}};
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(kFusedWaves * kWave) void route_permute_kernel(Fuse
     const int mt = blockIdx.x / (p.ksb * etiles);
     const int tok0 = mt * 16;
     const int rows = min(16, T - tok0);
-    const f16 *arow = p.x + (size_t)(tok0 + min(r, rows - 1)) * H;
+    const ARows arow(p.x + (size_t)tok0 * H, rows, H, r, r < rows, kb);
     const int e = et * 16 + r;
     const f16 *wrow[1] = {p.wr + (size_t)min(e, E - 1) * H};
     const int kg0 = kp * G / p.ksb, kg1 = (kp + 1) * G / p.ksb;

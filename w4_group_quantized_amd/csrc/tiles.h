@@ -21,6 +21,26 @@ namespace moe {
 
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// The A operand rows of one tile: lane (r, kb) reads the 32 consecutive
+// columns [32*kb, 32*kb + 32) of each 128-wide group of its token row through
+// a raw buffer.  Lanes whose row is past the tile hold an offset beyond the
+// buffer, so their loads return zeros without a memory access (their output
+// rows are discarded).
+struct ARows {
+  rsrc_t rs;
+  uint32_t voff;   // row byte offset + 64 * kb, or kPadOffset
+  static constexpr uint32_t kPadOffset = 0x80000000u;
+  // rows [0, nrows) of a [*, K] fp16 matrix at `base`, this lane's row `row`
+  // (nrows * K * 2 < 2^31)
+  __device__ __forceinline__ ARows(const f16 *base, int nrows, int K, int row, bool live, int kb)
+      : rs(make_rsrc(base, (uint32_t)nrows * (uint32_t)K * 2u)),
+        voff(live ? (uint32_t)row * (uint32_t)K * 2u + 64u * kb : kPadOffset) {}
+  // 8 halfs at column 128*g + 32*kb + 8*m
+  __device__ __forceinline__ u32x4 load(int g, int m) const {
+    return bload16(rs, voff + 16u * m, (uint32_t)g * 256u);
+  }
+};
+
 // One pipeline stage of the int4 path: S groups of activations, weights and
 // scales for NT weight tiles.
 template <int NT, int S>
@@ -31,9 +51,9 @@ struct W4Stage {
 };
 
 template <int NT, int S>
-__device__ __forceinline__ void w4_load(W4Stage<NT, S> &st, const f16 *__restrict__ arow,
+__device__ __forceinline__ void w4_load(W4Stage<NT, S> &st, const ARows &a,
                                         const uint8_t *const (&qrow)[NT],
-                                        const f16 *const (&srow)[NT], int kb, int g, int G) {
+                                        const f16 *const (&srow)[NT], int g, int G) {
 #pragma unroll
   for (int i = 0; i < S; ++i) {
     const int gg = min(g + i, G - 1);   // past the end: reload the last group (never used)
@@ -43,8 +63,7 @@ __device__ __forceinline__ void w4_load(W4Stage<NT, S> &st, const f16 *__restric
       st.s[i][t] = srow[t][(size_t)gg * 16];
     }
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-      st.x[i][m] = ld16(arow + (size_t)gg * kGroup + kb * 32 + m * 8);
+    for (int m = 0; m < 4; ++m) st.x[i][m] = a.load(gg, m);
   }
 }
 
@@ -68,28 +87,27 @@ __device__ __forceinline__ void w4_compute(const W4Stage<NT, S> &st, int ngroups
 }
 
 // int4 weights: acc[t] += sum_g scale[t][g] * sum_{k in g} A[tok][k] * q[t][k]
-// for g in [g0, g1).  arow: this lane's activation row (always a valid row;
-// lanes whose token is past the tile read a duplicate row and their output
-// rows are discarded); qrow[t]: base of weight tile t (16 rows) + lane*16
+// for g in [g0, g1).  arow: this lane's activation row (zeros for lanes
+// whose token is past the tile); qrow[t]: base of weight tile t (16 rows) + lane*16
 // bytes, so group g is at qrow[t] + g*1024; srow[t]: the tile's scales + r,
 // group g at srow[t][g*16].  The loop body has no control flow, so the two stages
 // stay in fixed registers and only the stage about to be used is waited for.
 template <int NT, int S>
-__device__ __forceinline__ void w4_tiles(const f16 *__restrict__ arow,
+__device__ __forceinline__ void w4_tiles(const ARows &arow,
                                          const uint8_t *const (&qrow)[NT],
-                                         const f16 *const (&srow)[NT], int kb, int g0, int g1,
+                                         const f16 *const (&srow)[NT], int g0, int g1,
                                          f32x4 (&acc)[NT]) {
   if (g0 >= g1) return;
   const UnpackConsts magic = unpack_consts();
   W4Stage<NT, S> a, b;
-  w4_load<NT, S>(a, arow, qrow, srow, kb, g0, g1);
+  w4_load<NT, S>(a, arow, qrow, srow, g0, g1);
   int g = g0;
   for (; g + 2 * S <= g1; g += 2 * S) {
-    w4_load<NT, S>(b, arow, qrow, srow, kb, g + S, g1);
+    w4_load<NT, S>(b, arow, qrow, srow, g + S, g1);
     sched_fence();
     w4_compute<NT, S>(a, S, magic, acc);
     sched_fence();
-    w4_load<NT, S>(a, arow, qrow, srow, kb, g + 2 * S, g1);
+    w4_load<NT, S>(a, arow, qrow, srow, g + 2 * S, g1);
     sched_fence();
     w4_compute<NT, S>(b, S, magic, acc);
     sched_fence();
@@ -98,7 +116,7 @@ __device__ __forceinline__ void w4_tiles(const f16 *__restrict__ arow,
   if (rest > 0) {
     w4_compute<NT, S>(a, rest, magic, acc);
     if (rest > S) {
-      w4_load<NT, S>(b, arow, qrow, srow, kb, g + S, g1);
+      w4_load<NT, S>(b, arow, qrow, srow, g + S, g1);
       w4_compute<NT, S>(b, rest - S, magic, acc);
     }
   }
@@ -112,13 +130,13 @@ struct F16Stage {
 };
 
 template <int NT>
-__device__ __forceinline__ void f16_load(F16Stage<NT> &st, const f16 *__restrict__ arow,
+__device__ __forceinline__ void f16_load(F16Stage<NT> &st, const ARows &arow,
                                          const f16 *const (&wrow)[NT], int kb, int g, int G) {
   const int gg = min(g, G - 1);
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const size_t k = (size_t)gg * kGroup + kb * 32 + m * 8;
-    st.x[m] = ld16(arow + k);
+    st.x[m] = arow.load(gg, m);
 #pragma unroll
     for (int t = 0; t < NT; ++t) st.w[t][m] = ld16(wrow[t] + k);
   }
@@ -133,7 +151,7 @@ __device__ __forceinline__ void f16_compute(const F16Stage<NT> &st, f32x4 (&acc)
 }
 
 template <int NT>
-__device__ __forceinline__ void f16_tiles(const f16 *__restrict__ arow,
+__device__ __forceinline__ void f16_tiles(const ARows &arow,
                                           const f16 *const (&wrow)[NT], int kb, int g0, int g1,
                                           f32x4 (&acc)[NT]) {
   if (g0 >= g1) return;
