@@ -82,6 +82,14 @@ __device__ __forceinline__ f16 bload_f16(rsrc_t r, uint32_t voff, uint32_t soff)
 __device__ __forceinline__ u32x4 ldg16(const void *p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }
+// All LDS operations of this wave are done; meet the other waves of the
+// block.  Vector-memory loads stay in flight (no vmcnt wait, which
+// __syncthreads would add); the "memory" clobber keeps the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ u32x4 ld16(const void *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }

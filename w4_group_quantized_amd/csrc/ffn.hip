@@ -33,6 +33,11 @@
 namespace moe {
 
 constexpr int kTileM = 16;   // tokens per MFMA tile
+// Token rows of a routed tile are staged in LDS when they take at most this
+// many bytes (each of the 256 threads moves kStagePieces 16-byte pieces).
+constexpr int kStagePieces = 8;
+constexpr int kActLdsBytes = kStagePieces * 256 * 16;
+constexpr int kActLdsVec = (kActLdsBytes + kTileM * 16) / 16;   // + row padding
 
 struct FfnArgs {
   int E, H, F, Fs, T, N, k;         // N = T * k
@@ -101,6 +106,7 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
   const int Nrows = kPair ? p.F : p.H;         // out_features of this phase
   const int G = K / kGroup;
   __shared__ float red[3 * 2 * 4 * kWave];
+  __shared__ u32x4 s_act[kActLdsVec];
 
   if ((int)blockIdx.x >= p.shared_items) {
     const int item = blockIdx.x - p.shared_items;
@@ -112,15 +118,6 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
     // offsets come from device memory: keep every row inside [0, N)
     if (seg0 < 0 || seg0 >= p.N) return;
     const int rows = min(min(kTileM, p.offsets[e + 1] - seg0), p.N - seg0);
-    // lanes of token rows past the tile read zeros; their outputs are dropped
-    const bool live = r < rows;
-    int tok = min(r, rows - 1);
-    if (p.perm_src) {            // gather straight from x: token of flat index perm_src[r]
-      tok = p.perm_src[seg0 + tok] / p.k;
-      tok = tok < 0 ? 0 : (tok >= p.T ? p.T - 1 : tok);
-    }
-    const ARows arow = p.perm_src ? ARows(p.a_routed, p.T, K, tok, live, kb)
-                                  : ARows(p.a_routed + (size_t)seg0 * K, rows, K, tok, live, kb);
     const uint8_t *qrow[kMats * NT];
     const f16 *srow[kMats * NT];
     int nrow[NT];
@@ -138,7 +135,64 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
     f32x4 acc[kMats * NT];
 #pragma unroll
     for (int t = 0; t < kMats * NT; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    w4_tiles<kMats * NT, S>(arow, qrow, srow, 0, G, acc);
+    const int KB = K * 2;                 // bytes per activation row
+    if (rows * KB <= kActLdsBytes) {      // block-uniform
+      // Stage the tile's token rows in LDS once for the four waves: the
+      // loads go out before the first weight stage, the LDS writes after it,
+      // so the weights are already in flight while the rows arrive.
+      const int ppr = KB / 16;            // 16-byte pieces per row
+      const int npieces = rows * ppr;
+      const int stride = KB + 16;         // padded: rows start 4 banks apart
+      const int tid = threadIdx.x;
+      rsrc_t rs;
+      uint32_t voff[kStagePieces];
+      if (p.perm_src) {                   // gather straight from x
+        rs = make_rsrc(p.a_routed, (uint32_t)p.T * (uint32_t)KB);
+#pragma unroll
+        for (int j = 0; j < kStagePieces; ++j) {
+          const int i = j * 256 + tid;
+          const int row = min(i / ppr, rows - 1);
+          int tok = p.perm_src[seg0 + row] / p.k;
+          tok = tok < 0 ? 0 : (tok >= p.T ? p.T - 1 : tok);
+          voff[j] = i < npieces ? (uint32_t)tok * KB + (uint32_t)(i - row * ppr) * 16u
+                                : ARows::kPadOffset;
+        }
+      } else {                            // rows seg0 .. seg0+rows-1 are contiguous
+        rs = make_rsrc(p.a_routed + (size_t)seg0 * K, (uint32_t)rows * (uint32_t)KB);
+#pragma unroll
+        for (int j = 0; j < kStagePieces; ++j) {
+          const int i = j * 256 + tid;
+          voff[j] = i < npieces ? (uint32_t)i * 16u : ARows::kPadOffset;
+        }
+      }
+      u32x4 stg[kStagePieces];
+#pragma unroll
+      for (int j = 0; j < kStagePieces; ++j) stg[j] = bload16(rs, voff[j], 0);
+      const ALds<kActLdsVec> al(s_act, min(r, rows - 1), stride, kb);
+      w4_tiles<kMats * NT, S>(al, qrow, srow, 0, G, acc, [&] {
+#pragma unroll
+        for (int j = 0; j < kStagePieces; ++j) {
+          const int i = j * 256 + tid;
+          if (i < npieces) {
+            const int row = i / ppr;
+            s_act[(row * stride + (i - row * ppr) * 16) / 16] = stg[j];
+          }
+        }
+        lds_barrier();
+      });
+    } else {
+      // lanes of token rows past the tile read zeros; their outputs are dropped
+      const bool live = r < rows;
+      int tok = min(r, rows - 1);
+      if (p.perm_src) {          // gather straight from x: token of flat index perm_src[r]
+        tok = p.perm_src[seg0 + tok] / p.k;
+        tok = tok < 0 ? 0 : (tok >= p.T ? p.T - 1 : tok);
+      }
+      const ARows arow = p.perm_src
+                             ? ARows(p.a_routed, p.T, K, tok, live, kb)
+                             : ARows(p.a_routed + (size_t)seg0 * K, rows, K, tok, live, kb);
+      w4_tiles<kMats * NT, S>(arow, qrow, srow, 0, G, acc);
+    }
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -201,6 +255,10 @@ constexpr int kNT2 = MOE_FFN_NT2;   // phase 2: 64*NT2 down rows per block
 constexpr int kS1 = MOE_FFN_S1;     // groups per pipeline stage, phase 1
 constexpr int kS2 = MOE_FFN_S2;     // groups per pipeline stage, phase 2
 
+// Phase 1 streams two gate and two up tiles per wave once segments average
+// at least this many rows.
+constexpr int kWide1MinAvgRows = 2;
+
 // Prefill mode: segments average at least this many rows, so a 128-row MFMA
 // block tile is mostly full; routed experts then run on the MFMA kernel.  Its
 // buffer loads address each activation matrix and each expert's weight
@@ -249,11 +307,18 @@ hipError_t launch_ffn(const moe_layer &L, const uint16_t *x, const uint16_t *x_p
   a.out_routed = reinterpret_cast<f16 *>(h);
   a.out_shared = reinterpret_cast<f16 *>(h_shared);
   static_assert(128 % (64 * kNT1) == 0, "F is a multiple of 128");
-  a.routed_items = prefill ? 0 : max_tiles * (F / (64 * kNT1));
+  // segments of several rows on average: two gate and two up tiles per wave,
+  // so each activation load serves twice the weight bytes
+  const bool wide1 = N >= kWide1MinAvgRows * E;
+  a.routed_items = prefill ? 0 : max_tiles * (F / (wide1 ? 128 : 64 * kNT1));
   a.shared_items = Fs ? mtiles_shared * (Fs / 16) : 0;
   if (a.routed_items + a.shared_items > 0) {
-    hipLaunchKernelGGL((ffn_decode_kernel<1, kNT1, kS1>), dim3(a.routed_items + a.shared_items),
-                       dim3(256), 0, st, a);
+    if (wide1)
+      hipLaunchKernelGGL((ffn_decode_kernel<1, 2, 1>), dim3(a.routed_items + a.shared_items),
+                         dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((ffn_decode_kernel<1, kNT1, kS1>), dim3(a.routed_items + a.shared_items),
+                         dim3(256), 0, st, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
 

@@ -109,12 +109,6 @@ __device__ bool locate_tile(const int32_t *__restrict__ off, int E, int ntiles, 
   return true;
 }
 
-// All LDS operations of this wave are done; meet the other waves of the
-// block.  The "memory" clobber keeps the compiler from moving memory
-// accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 // Per-lane byte offsets of one block tile (step 0) and LDS offsets.
 struct PrefillOperands {

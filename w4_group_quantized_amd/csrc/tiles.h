@@ -35,10 +35,24 @@ struct ARows {
   __device__ __forceinline__ ARows(const f16 *base, int nrows, int K, int row, bool live, int kb)
       : rs(make_rsrc(base, (uint32_t)nrows * (uint32_t)K * 2u)),
         voff(live ? (uint32_t)row * (uint32_t)K * 2u + 64u * kb : kPadOffset) {}
+  static constexpr bool kDeferred = false;   // loaded with the weights of its stage
   // 8 halfs at column 128*g + 32*kb + 8*m
   __device__ __forceinline__ u32x4 load(int g, int m) const {
     return bload16(rs, voff + 16u * m, (uint32_t)g * 256u);
   }
+};
+
+// The same A operand rows staged in LDS by the block (row stride `stride`
+// bytes): read right before the MFMAs that use them.  Lanes past the tile
+// read the last live row (their output rows are discarded).
+template <int LDS_VEC>
+struct ALds {
+  const u32x4 (&lds)[LDS_VEC];
+  uint32_t idx;    // this lane's row start + 64 * kb, in 16-byte units
+  static constexpr bool kDeferred = true;
+  __device__ __forceinline__ ALds(const u32x4 (&l)[LDS_VEC], int row, int stride, int kb)
+      : lds(l), idx((uint32_t)(row * stride + 64 * kb) / 16u) {}
+  __device__ __forceinline__ u32x4 load(int g, int m) const { return lds[idx + 16 * g + m]; }
 };
 
 // One pipeline stage of the int4 path: S groups of activations, weights and
@@ -50,8 +64,8 @@ struct W4Stage {
   f16 s[S][NT];
 };
 
-template <int NT, int S>
-__device__ __forceinline__ void w4_load(W4Stage<NT, S> &st, const ARows &a,
+template <int NT, int S, class A>
+__device__ __forceinline__ void w4_load(W4Stage<NT, S> &st, const A &a,
                                         const uint8_t *const (&qrow)[NT],
                                         const f16 *const (&srow)[NT], int g, int G) {
 #pragma unroll
@@ -62,23 +76,28 @@ __device__ __forceinline__ void w4_load(W4Stage<NT, S> &st, const ARows &a,
       st.q[i][t] = ld16(qrow[t] + (size_t)gg * 1024);
       st.s[i][t] = srow[t][(size_t)gg * 16];
     }
+    if (!A::kDeferred) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) st.x[i][m] = a.load(gg, m);
+      for (int m = 0; m < 4; ++m) st.x[i][m] = a.load(gg, m);
+    }
   }
 }
 
-template <int NT, int S>
-__device__ __forceinline__ void w4_compute(const W4Stage<NT, S> &st, int ngroups, const UnpackConsts &magic,
-                                           f32x4 (&acc)[NT]) {
+template <int NT, int S, class A>
+__device__ __forceinline__ void w4_compute(const W4Stage<NT, S> &st, const A &a, int g, int ngroups,
+                                           const UnpackConsts &magic, f32x4 (&acc)[NT]) {
 #pragma unroll
   for (int i = 0; i < S; ++i) {
     if (i < ngroups) {
+      u32x4 x[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) x[m] = A::kDeferred ? a.load(g + i, m) : st.x[i][m];
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < 4; ++m)
-          tmp = mfma_16x16x32(as_f16x8(st.x[i][m]), unpack8(st.q[i][t][m], magic), tmp);
+          tmp = mfma_16x16x32(as_f16x8(x[m]), unpack8(st.q[i][t][m], magic), tmp);
         const float s = (float)st.s[i][t];
         acc[t] += s * tmp;
       }
@@ -87,37 +106,42 @@ __device__ __forceinline__ void w4_compute(const W4Stage<NT, S> &st, int ngroups
 }
 
 // int4 weights: acc[t] += sum_g scale[t][g] * sum_{k in g} A[tok][k] * q[t][k]
-// for g in [g0, g1).  arow: this lane's activation row (zeros for lanes
-// whose token is past the tile); qrow[t]: base of weight tile t (16 rows) + lane*16
-// bytes, so group g is at qrow[t] + g*1024; srow[t]: the tile's scales + r,
-// group g at srow[t][g*16].  The loop body has no control flow, so the two stages
-// stay in fixed registers and only the stage about to be used is waited for.
-template <int NT, int S>
-__device__ __forceinline__ void w4_tiles(const ARows &arow,
-                                         const uint8_t *const (&qrow)[NT],
+// for g in [g0, g1).  arow: this lane's activation rows (ARows or ALds);
+// qrow[t]: base of weight tile t (16 rows) + lane*16 bytes, so group g is at
+// qrow[t] + g*1024; srow[t]: the tile's scales + r, group g at srow[t][g*16].
+// after_first() runs once the first stage's loads are issued (the block can
+// stage its activations there while they are in flight).  The loop body has
+// no control flow, so the two stages stay in fixed registers and only the
+// stage about to be used is waited for.
+struct NoOp {
+  __device__ __forceinline__ void operator()() const {}
+};
+template <int NT, int S, class A, class F = NoOp>
+__device__ __forceinline__ void w4_tiles(const A &arow, const uint8_t *const (&qrow)[NT],
                                          const f16 *const (&srow)[NT], int g0, int g1,
-                                         f32x4 (&acc)[NT]) {
+                                         f32x4 (&acc)[NT], F after_first = F()) {
   if (g0 >= g1) return;
   const UnpackConsts magic = unpack_consts();
   W4Stage<NT, S> a, b;
   w4_load<NT, S>(a, arow, qrow, srow, g0, g1);
+  after_first();
   int g = g0;
   for (; g + 2 * S <= g1; g += 2 * S) {
     w4_load<NT, S>(b, arow, qrow, srow, g + S, g1);
     sched_fence();
-    w4_compute<NT, S>(a, S, magic, acc);
+    w4_compute<NT, S>(a, arow, g, S, magic, acc);
     sched_fence();
     w4_load<NT, S>(a, arow, qrow, srow, g + 2 * S, g1);
     sched_fence();
-    w4_compute<NT, S>(b, S, magic, acc);
+    w4_compute<NT, S>(b, arow, g + S, S, magic, acc);
     sched_fence();
   }
   const int rest = g1 - g;          // 0 <= rest < 2S groups; stage a holds group g..
   if (rest > 0) {
-    w4_compute<NT, S>(a, rest, magic, acc);
+    w4_compute<NT, S>(a, arow, g, rest, magic, acc);
     if (rest > S) {
       w4_load<NT, S>(b, arow, qrow, srow, g + S, g1);
-      w4_compute<NT, S>(b, rest - S, magic, acc);
+      w4_compute<NT, S>(b, arow, g + S, rest - S, magic, acc);
     }
   }
 }
