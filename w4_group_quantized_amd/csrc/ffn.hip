@@ -19,7 +19,9 @@
 // behind the routed ones):
 //   routed item = (segment tile, n-tile): a segment tile is 16 consecutive rows
 //     of one expert's segment; an n-tile is 64*NT weight rows; each of the 4
-//     waves streams 16*NT rows over the whole K range.
+//     waves streams 16*NT rows over the whole K range.  When the tile's live
+//     token rows fit in 32 KB the block stages them in LDS once and the waves
+//     read their MFMA operands from there.
 //   shared item = (16-token tile, 16 weight rows); the 4 waves split K 4 ways,
 //     so that a wave moves as many bytes as a routed wave (fp16 weights are 4x
 //     the bytes of int4).
@@ -238,26 +240,13 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
   }
 }
 
-#ifndef MOE_FFN_NT1
-#define MOE_FFN_NT1 1
-#endif
-#ifndef MOE_FFN_NT2
-#define MOE_FFN_NT2 4
-#endif
-#ifndef MOE_FFN_S1
-#define MOE_FFN_S1 2
-#endif
-#ifndef MOE_FFN_S2
-#define MOE_FFN_S2 1
-#endif
-constexpr int kNT1 = MOE_FFN_NT1;   // phase 1: 64*NT1 gate rows + as many up rows per block
-constexpr int kNT2 = MOE_FFN_NT2;   // phase 2: 64*NT2 down rows per block
-constexpr int kS1 = MOE_FFN_S1;     // groups per pipeline stage, phase 1
-constexpr int kS2 = MOE_FFN_S2;     // groups per pipeline stage, phase 2
-
-// Phase 1 streams two gate and two up tiles per wave once segments average
-// at least this many rows.
-constexpr int kWide1MinAvgRows = 2;
+// Tile shapes per phase.  Rows per block = 64 * NT (each wave streams NT
+// 16-row tiles of each matrix); S = quantization groups per pipeline stage.
+// Small segments (under kWideMinAvgRows rows per expert on average, so the
+// token rows come from LDS): gate/up NT 1, S 2; down NT 2, S 2.  Segments of
+// several rows: NT 2, S 1 for gate/up and NT 4, S 1 for down, so that each
+// activation load serves more weight bytes.
+constexpr int kWideMinAvgRows = 2;
 
 // Prefill mode: segments average at least this many rows, so a 128-row MFMA
 // block tile is mostly full; routed experts then run on the MFMA kernel.  Its
@@ -306,18 +295,15 @@ hipError_t launch_ffn(const moe_layer &L, const uint16_t *x, const uint16_t *x_p
   a.w1 = reinterpret_cast<const f16 *>(L.shared_up);
   a.out_routed = reinterpret_cast<f16 *>(h);
   a.out_shared = reinterpret_cast<f16 *>(h_shared);
-  static_assert(128 % (64 * kNT1) == 0, "F is a multiple of 128");
-  // segments of several rows on average: two gate and two up tiles per wave,
-  // so each activation load serves twice the weight bytes
-  const bool wide1 = N >= kWide1MinAvgRows * E;
-  a.routed_items = prefill ? 0 : max_tiles * (F / (wide1 ? 128 : 64 * kNT1));
+  const bool wide = N >= kWideMinAvgRows * E;
+  a.routed_items = prefill ? 0 : max_tiles * (F / (wide ? 128 : 64));   // F % 128 == 0
   a.shared_items = Fs ? mtiles_shared * (Fs / 16) : 0;
   if (a.routed_items + a.shared_items > 0) {
-    if (wide1)
+    if (wide)
       hipLaunchKernelGGL((ffn_decode_kernel<1, 2, 1>), dim3(a.routed_items + a.shared_items),
                          dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((ffn_decode_kernel<1, kNT1, kS1>), dim3(a.routed_items + a.shared_items),
+      hipLaunchKernelGGL((ffn_decode_kernel<1, 1, 2>), dim3(a.routed_items + a.shared_items),
                          dim3(256), 0, st, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
@@ -335,16 +321,15 @@ hipError_t launch_ffn(const moe_layer &L, const uint16_t *x, const uint16_t *x_p
   a.w0 = reinterpret_cast<const f16 *>(L.shared_down); a.w1 = nullptr;
   a.out_routed = reinterpret_cast<f16 *>(y_perm);
   a.out_shared = reinterpret_cast<f16 *>(y_shared);
-  // 64*kNT2 down rows per block when H allows it, else 128
-  const bool wide2 = H % (64 * kNT2) == 0;
-  a.routed_items = prefill ? 0 : max_tiles * (H / (64 * (wide2 ? kNT2 : 2)));
+  const bool wide2 = wide && H % 256 == 0;
+  a.routed_items = prefill ? 0 : max_tiles * (H / (wide2 ? 256 : 128));   // H % 128 == 0
   a.shared_items = Fs ? mtiles_shared * (H / 16) : 0;
   if (a.routed_items + a.shared_items > 0) {
     if (wide2)
-      hipLaunchKernelGGL((ffn_decode_kernel<2, kNT2, kS2>), dim3(a.routed_items + a.shared_items),
+      hipLaunchKernelGGL((ffn_decode_kernel<2, 4, 1>), dim3(a.routed_items + a.shared_items),
                          dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((ffn_decode_kernel<2, 2, kS2>), dim3(a.routed_items + a.shared_items),
+      hipLaunchKernelGGL((ffn_decode_kernel<2, 2, 2>), dim3(a.routed_items + a.shared_items),
                          dim3(256), 0, st, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
