@@ -13,8 +13,10 @@ moe_w4_grouped_ffn call: two launches, gate/up then down): decode: algorithmic
 bytes = distinct experts with tokens in the step x bytes per expert (packed
 int4 + fp16 scales) + the fp16 shared expert; prefill: algorithmic FLOPs =
 6*H*F per (token, chosen expert) pair; divided by the stage's average
-duration measured with HIP events on the launch stream inside the timed
-region.  `traffic` is the HBM bytes per call measured by rocprofv3 counters
+duration: K FFN calls with the steps' weight sets, batches and routing, run
+back to back on the launch stream between one pair of HIP events (so no
+event-processing gaps land on the kernels).  `ffn_us_in_step` is the same
+stage timed with events around it inside every step of the timed region.  `traffic` is the HBM bytes per call measured by rocprofv3 counters
 (profiles/traffic_<workload>.json, taken with --copy-calibration-mib and
 turned into bytes with --summarize-traffic), or null when the FFN sources
 have changed since.
@@ -25,6 +27,7 @@ this leg) on a bounded sample of the same workload on the host cores.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import platform
@@ -327,14 +330,40 @@ def main():
     wall = time.perf_counter() - wall0
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / K
-    ffn_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    ffn_ms_in_step = np.array([a.elapsed_time(b) for a, b in evs])
+
+    # The FFN stage alone: the same K calls (same weight sets, batches and
+    # routing as the steps) back to back between one pair of events, so that
+    # the per-call figure carries no event-processing gaps.
+    ffn_bufs = []
+    for c in range(n_combo):   # own routing per combination; outputs and workspace shared
+        b = dataclasses.replace(bufs, topk_idx=torch.empty_like(bufs.topk_idx),
+                                topk_w=torch.empty_like(bufs.topk_w),
+                                offsets=torch.empty_like(bufs.offsets),
+                                perm_src=torch.empty_like(bufs.perm_src),
+                                inv_pos=torch.empty_like(bufs.inv_pos))
+        sets[c % n_sets][0].route_permute(xs[(c // n_sets) % args.batches], b, T)
+        ffn_bufs.append(b)
+    for i in range(min(args.warmup, n_combo)):
+        sets[i % n_sets][0].ffn(xs[(i // n_sets) % args.batches], ffn_bufs[i % n_combo], T)
+    f_start = torch.cuda.Event(enable_timing=True)
+    f_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    f_start.record(stream)
+    for i in range(K):
+        c = i % n_combo
+        sets[c % n_sets][0].ffn(xs[(c // n_sets) % args.batches], ffn_bufs[c], T)
+    f_end.record(stream)
+    torch.cuda.synchronize()
+    ffn_ms_mean = f_start.elapsed_time(f_end) / K
+    del ffn_bufs
     ffn_bytes = np.array([bytes_per_combo[i % n_combo] for i in range(K)], dtype=np.float64)
-    achieved_gbs = float(ffn_bytes.mean() / (ffn_ms.mean() * 1e-3) / 1e9)
+    achieved_gbs = float(ffn_bytes.mean() / (ffn_ms_mean * 1e-3) / 1e9)
     tokens_per_s = T * K / (ms_total * 1e-3)
     # algorithmic FFN FLOPs: every (token, chosen expert) pair costs 6*H*F
     # (gate, up, down), the shared expert 6*H*Fs per token
     ffn_flops = T * (cfg.top_k * 6.0 * cfg.hidden * cfg.ffn + 6.0 * cfg.hidden * cfg.shared_ffn)
-    achieved_tflops = float(ffn_flops / (ffn_ms.mean() * 1e-3) / 1e12)
+    achieved_tflops = float(ffn_flops / (ffn_ms_mean * 1e-3) / 1e12)
     traffic = measured_traffic(cfg.name)
     if cfg.name == "prefill":
         roofline = {"bound": "mfma", "achieved": achieved_tflops, "peak": MFMA_F16_PEAK_TFLOPS,
@@ -344,7 +373,8 @@ def main():
         roofline = {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic}
     roofline.update({"kernel": "moe_w4_grouped_ffn (gate/up launch + down launch)",
-                     "ffn_us_mean": float(ffn_ms.mean() * 1e3),
+                     "ffn_us_mean": float(ffn_ms_mean * 1e3),
+                     "ffn_us_in_step": float(ffn_ms_in_step.mean() * 1e3),
                      "ffn_bytes_mean": float(ffn_bytes.mean()), "ffn_flops": ffn_flops,
                      "ffn_tflops": achieved_tflops, "ffn_gbs": achieved_gbs})
 
