@@ -219,22 +219,32 @@ def test_route_permute_fused(name, over, T):
 
 # ---------------------------------------------------------------- FFN
 FFN_CASES = [
-    ("tiny", {}, 16, 0),
-    ("tiny", {"num_experts": 4, "top_k": 4}, 21, 0),                    # >16 rows per segment
-    ("tiny", {"num_experts": 12, "hidden": 512, "ffn": 384, "top_k": 3}, 9, 256),
-    ("tiny", {"num_experts": 6, "hidden": 384, "ffn": 256, "top_k": 2}, 70, 128),
+    ("tiny", {}, 16, 0, False),
+    ("tiny", {"num_experts": 4, "top_k": 4}, 21, 0, False),             # >16 rows per segment
+    ("tiny", {"num_experts": 12, "hidden": 512, "ffn": 384, "top_k": 3}, 9, 256, False),
+    ("tiny", {"num_experts": 6, "hidden": 384, "ffn": 256, "top_k": 2}, 70, 128, False),
+    # several rows per expert on average (the wider tile shapes); 16-row tiles
+    # of 4 KB rows (64 KB: streamed from memory) next to 4-row ones (staged)
+    ("tiny", {"num_experts": 4, "hidden": 2048, "ffn": 512, "top_k": 2}, 40, 256, False),
+    # under two rows per expert on average, but every token also picks expert
+    # 0: one 7-row tile of 8 KB rows (56 KB: streamed) among 1-row tiles
+    ("tiny", {"num_experts": 8, "hidden": 4096, "ffn": 128, "top_k": 2}, 7, 128, True),
 ]
 
 
 @pytest.mark.parametrize("use_x_perm", [False, True])
-@pytest.mark.parametrize("name,over,T,Fs", FFN_CASES)
-def test_ffn_teacher_forced(name, over, T, Fs, use_x_perm):
+@pytest.mark.parametrize("name,over,T,Fs,skew", FFN_CASES)
+def test_ffn_teacher_forced(name, over, T, Fs, skew, use_x_perm):
     cfg = get_config(name, shared_ffn=Fs, **over)
     mats, experts = quantized_experts(cfg)
     wr, b = G.router(cfg)
     x = G.activations(cfg, tokens=T, batch=5)
     shared = G.shared_expert(cfg) if Fs else None
-    idx, w, l = O.route(x, wr, b, cfg.top_k)
+    if skew:                     # token t -> experts 0 and 1 + t % (E - 1)
+        idx = np.stack([np.zeros(T, np.int32), 1 + np.arange(T, dtype=np.int32) %
+                        (cfg.num_experts - 1)], axis=1)
+    else:
+        idx, w, l = O.route(x, wr, b, cfg.top_k)
     off, perm_src, inv_pos = O.permute(idx, cfg.num_experts)
     x_perm = O.gather_rows(x, perm_src, cfg.top_k)
     layer = make_gpu_layer(cfg, mats, wr, b, shared)
