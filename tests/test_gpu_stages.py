@@ -271,7 +271,8 @@ def test_ffn_teacher_forced(name, over, T, Fs, skew, use_x_perm):
 # ---------------------------------------------------------------- combine
 @pytest.mark.parametrize("rms", [False, True])
 @pytest.mark.parametrize("T,k,H,with_shared", [(16, 2, 256, False), (9, 8, 4096, True),
-                                               (3, 32, 384, True)])
+                                               (3, 32, 384, True), (5, 8, 6144, True),
+                                               (4, 3, 12416, False), (2, 4, 20480, True)])
 def test_combine(T, k, H, with_shared, rms):
     g = np.random.default_rng(T + k)
     N = T * k
