@@ -12,7 +12,7 @@
 // step's 128 x 64 fp16 tile is loaded into registers one step ahead and
 // stored into one of two LDS stages.  The weights do not touch LDS: wave w
 // owns 64 weight rows and loads their int4 codes straight into registers
-// (16 bytes per lane per 32 rows per K step, two steps ahead),
+// (16 bytes per lane per 32 rows per K step, three steps ahead),
 // unpacks them with the group scale folded in (RN16(q*s)) and feeds them as
 // the MFMA's A operand, so every weight is read from memory and unpacked
 // exactly once per block.  Each wave multiplies its 64 weight rows by all 128
@@ -42,6 +42,7 @@ constexpr int kPM = 128;          // token rows per block tile
 constexpr int kPN = 256;          // weight rows per block tile
 constexpr int kPK = 64;           // K per step
 constexpr int kPStage = kPM * kPK;  // halfs per stage
+constexpr int kPAhead = 3;        // weight codes and scales are loaded this many steps ahead
 
 struct PrefillArgs {
   int E, H, F, T, N, k;
@@ -122,31 +123,33 @@ struct PrefillOperands {
 
 // The K loop.  Step s: meet at the barrier (stage s % 2 is complete), issue
 // the loads of the activation pieces of step s + 1 and of the code chunks and
-// scales of step s + 2 (clamped to the last step; surplus loads are never
+// scales of step s + D (clamped to the last step; surplus loads are never
 // used), run 4 k16 sub-steps of 8 MFMAs on LDS stage s % 2, then store the
 // step s + 1 pieces into the other stage.  Code/scale registers rotate with
-// period 3, hence the loop unrolled by 3.  MI (1..4) is the number of 32-row
-// M-tiles holding real rows: the last tile of a segment skips the MFMAs and
-// activation loads of its empty M-tiles (wave w loads the rows of M-tile w).
-template <int MI>
+// period D + 1, hence the loop unrolled by D + 1.  MI (1..4) is the number of
+// 32-row M-tiles holding real rows: the last tile of a segment skips the
+// MFMAs and activation loads of its empty M-tiles (wave w loads the rows of
+// M-tile w).
+template <int MI, int D>
 __device__ __forceinline__ void prefill_gemm(f16 *sA, rsrc_t a_rs, rsrc_t b_rs0, rsrc_t b_rs1,
                                              rsrc_t s_rs0, rsrc_t s_rs1,
                                              const PrefillOperands &o, bool a_loader,
                                              f32x16 (&acc)[MI][2]) {
+  constexpr int NS = D + 1;         // code/scale register stages: steps v .. v+D
   u32x4 ra[4];                      // activation pieces of the next step
-  u32x4 rb0[2], rb1[2], rb2[2];     // code chunks of the three steps in flight
-  f16 rs0[2], rs1[2], rs2[2];       // their group scales
+  u32x4 rb[NS][2];                  // code chunks of the steps in flight
+  f16 rs[NS][2];                    // their group scales
   const int nsteps = o.nsteps;
   auto load_a = [&](int step) {
     if (!a_loader) return;
 #pragma unroll
     for (int j = 0; j < 4; ++j) ra[j] = bload16(a_rs, o.a_off[j], step * (kPK * 2));
   };
-  auto load_b = [&](int step, u32x4 (&rb)[2], f16 (&rs)[2]) {
-    rb[0] = bload16(b_rs0, o.b_off[0], step * 512);
-    rb[1] = bload16(b_rs1, o.b_off[1], step * 512);
-    rs[0] = bload_f16(s_rs0, o.s_off[0], (step >> 1) * 32);
-    rs[1] = bload_f16(s_rs1, o.s_off[1], (step >> 1) * 32);
+  auto load_b = [&](int step, int u) {
+    rb[u][0] = bload16(b_rs0, o.b_off[0], step * 512);
+    rb[u][1] = bload16(b_rs1, o.b_off[1], step * 512);
+    rs[u][0] = bload_f16(s_rs0, o.s_off[0], (step >> 1) * 32);
+    rs[u][1] = bload_f16(s_rs1, o.s_off[1], (step >> 1) * 32);
   };
   auto store_a = [&](int step) {
     if (!a_loader) return;
@@ -156,11 +159,12 @@ __device__ __forceinline__ void prefill_gemm(f16 *sA, rsrc_t a_rs, rsrc_t b_rs0,
   };
 
   const UnpackConsts kc = unpack_consts();
-  auto body = [&](int step, const u32x4 (&rb)[2], const f16 (&rs)[2], u32x4 (&rb_ahead)[2],
-                  f16 (&rs_ahead)[2]) {
+  // step `step` uses register stage u; the codes of step + D go to stage
+  // (u + D) % NS, which held those of step - 1
+  auto body = [&](int step, int u) {
     lds_barrier();      // stage step % 2 is complete; stage (step+1) % 2 is free
     load_a(min(step + 1, nsteps - 1));
-    load_b(min(step + 2, nsteps - 1), rb_ahead, rs_ahead);
+    load_b(min(step + D, nsteps - 1), (u + D) % NS);
     __builtin_amdgcn_sched_barrier(0);   // keep the loads at the top of the step
     const f16 *as = sA + (step & 1) * kPStage;
 #pragma unroll
@@ -168,8 +172,8 @@ __device__ __forceinline__ void prefill_gemm(f16 *sA, rsrc_t a_rs, rsrc_t b_rs0,
       f16x8 bf[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const f16x8 q = unpack8(rb[j][w], kc);
-        const f16x2 sc = {rs[j], rs[j]};
+        const f16x8 q = unpack8(rb[u][j][w], kc);
+        const f16x2 sc = {rs[u][j], rs[u][j]};
         u32x4 v;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -191,16 +195,19 @@ __device__ __forceinline__ void prefill_gemm(f16 *sA, rsrc_t a_rs, rsrc_t b_rs0,
   };
 
   load_a(0);
-  load_b(0, rb0, rs0);
-  load_b(min(1, nsteps - 1), rb1, rs1);
+#pragma unroll
+  for (int u = 0; u < D; ++u) load_b(min(u, nsteps - 1), u);
   store_a(0);
-  for (int s0 = 0;; s0 += 3) {
-    body(s0, rb0, rs0, rb2, rs2);
-    if (s0 + 1 >= nsteps) break;
-    body(s0 + 1, rb1, rs1, rb0, rs0);
-    if (s0 + 2 >= nsteps) break;
-    body(s0 + 2, rb2, rs2, rb1, rs1);
-    if (s0 + 3 >= nsteps) break;
+  for (int s0 = 0;; s0 += NS) {
+    bool done = false;
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      if (!done) {
+        body(s0 + u, u);
+        done = s0 + u + 1 >= nsteps;
+      }
+    }
+    if (done) break;
   }
 }
 
@@ -220,7 +227,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &p, f16 *sA, rsrc
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = (f32x16){};
-  prefill_gemm<MI>(sA, a_rs, b_rs0, b_rs1, s_rs0, s_rs1, o, wv < MI, acc);
+  prefill_gemm<MI, kPAhead>(sA, a_rs, b_rs0, b_rs1, s_rs0, s_rs1, o, wv < MI, acc);
 
   // ---- epilogue.  The weights are the MFMA's A operand, so accumulator
   // acc[i][j] holds the transposed 32 x 32 tile: register r of lane l is
