@@ -69,6 +69,9 @@ __device__ __forceinline__ f16x8 unpack8(uint32_t w, const UnpackConsts &k) {
 // plus a wave-uniform one in an SGPR; offsets past `bytes` read zeros and
 // stores there are dropped.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
+// cache-policy operand of the buffer intrinsics: sc1, the device coherence
+// point (what agent-scope atomic loads use on this target)
+constexpr int kBufCoherent = 16;
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
 }
@@ -191,6 +194,17 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     const uint64_t t = ((uint64_t)hi << 32) | lo;
     r = t > r ? t : r;
   }
+  return r;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<kDppXor1>(v));
+  v = max(v, dpp_u32<kDppXor2>(v));
+  v = max(v, dpp_u32<kDppHalfMirror>(v));
+  v = max(v, dpp_u32<kDppMirror>(v));
+  uint32_t r = __builtin_amdgcn_readlane(v, 0);
+#pragma unroll
+  for (int row = 1; row < 4; ++row) r = max(r, (uint32_t)__builtin_amdgcn_readlane(v, row * 16));
   return r;
 }
 

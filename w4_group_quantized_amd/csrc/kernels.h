@@ -19,7 +19,8 @@ constexpr int kFusedMaxLogits = 8192;   // T * E held in LDS by the fused router
 // Byte offsets of the per-call scratch regions inside the caller's workspace.
 struct WsLayout {
   size_t sync;      // uint32 counters; zero between calls
-  size_t logits;    // fp32 [T, E], or [kFusedMaxKsb, T, E] partials when T <= kFusedMaxT
+  size_t logits;    // fp32 [T, E], or kFusedMaxKsb partials [T, E] when T <= kFusedMaxT,
+                    // each padded to a multiple of 4 floats
   size_t counts;    // int32 [nchunks, E]
   size_t bases;     // int32 [nchunks, E]
   size_t h;         // fp16 [T*k, F]

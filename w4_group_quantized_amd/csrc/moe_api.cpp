@@ -25,7 +25,8 @@ WsLayout ws_layout(const moe_layer &L, int32_t T) {
   size_t off = 0;
   w.sync = off;     off += 256;
   const bool fused = Tz <= (size_t)kFusedMaxT && Tz * E <= (size_t)kFusedMaxLogits;
-  const size_t nlog = fused ? (size_t)kFusedMaxKsb * Tz * E : Tz * E;
+  // the fused router's K parts each padded to a multiple of 4 logits
+  const size_t nlog = fused ? (size_t)kFusedMaxKsb * ((Tz * E + 3) & ~(size_t)3) : Tz * E;
   w.logits = off;   off += align_up(nlog * sizeof(float));
   w.counts = off;   off += align_up(nch * E * sizeof(int32_t));
   w.bases = off;    off += align_up(nch * E * sizeof(int32_t));

@@ -9,6 +9,8 @@
 // GEMM: xdnf.cn/news/329730 §3.2.  Ties go to the lower expert index; the
 // combine weights are the softmax probabilities of the chosen experts, not
 // renormalised.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "tiles.h"
@@ -51,10 +53,22 @@ __device__ __forceinline__ void wave_softmax_topk(Get get, GetE get_expert, int 
       if (key[i + 1] > key[i]) {
         const uint64_t t = key[i]; key[i] = key[i + 1]; key[i + 1] = t;
       }
-  // k rounds; the winner of round j is uniform, lane j records it
+  // k rounds; the winner of round j is uniform, lane j records it.  The
+  // winner is the largest head key: its value-order word alone decides
+  // unless several heads share it (equal logits, NaN or empty heads), and
+  // then the full 64-bit comparison does.
   int mine = 0;
   for (int j = 0; j < k; ++j) {
-    const uint64_t best = wave_max_u64(key[0]);
+    const uint32_t hi = (uint32_t)(key[0] >> 32);
+    const uint32_t mhi = wave_max_u32(hi);
+    const uint64_t tied = __ballot(hi == mhi);
+    uint64_t best;
+    if (__popcll(tied) == 1) {   // wave-uniform
+      const int owner = __ffsll((long long)tied) - 1;
+      best = ((uint64_t)mhi << 32) | (uint32_t)__builtin_amdgcn_readlane((uint32_t)key[0], owner);
+    } else {
+      best = wave_max_u64(key[0]);
+    }
     if (lane == j) mine = route_key_expert(best);
     if (key[0] == best) {   // the owner lane: its head won, shift its list
 #pragma unroll
@@ -244,6 +258,7 @@ __global__ __launch_bounds__(kFusedWaves * kWave) void route_permute_kernel(Fuse
   const int r = lane & 15, kb = lane >> 4;
   const int T = p.T, E = p.E, H = p.H, k = p.k;
   const int G = H / kGroup;
+  const int TE = T * E, TEp = (TE + 3) & ~3;   // logits per K part, padded
 
   // ---- partial logits of this block's (token tile, expert tile, K part)
   {
@@ -267,7 +282,7 @@ __global__ __launch_bounds__(kFusedWaves * kWave) void route_permute_kernel(Fuse
       for (int j = 0; j < 4; ++j) {
         const int tok = 4 * kb + j;
         if (tok < rows)   // written through to the device coherence point (no L2 flush)
-          __hip_atomic_store(&p.partial[((size_t)kp * T + tok0 + tok) * E + e], acc[0][j],
+          __hip_atomic_store(&p.partial[(size_t)kp * TEp + (size_t)(tok0 + tok) * E + e], acc[0][j],
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
@@ -287,20 +302,46 @@ __global__ __launch_bounds__(kFusedWaves * kWave) void route_permute_kernel(Fuse
 
   // logits = sum of the K parts in order + bias, into LDS; every thread's
   // loads are independent so they are all in flight together
-  const int TE = T * E;
-  for (int i = tid; i < TE; i += blockDim.x) {
-    const int e = i % E;
-    float part[kFusedMaxKsb];
+  {
+    // four logits per thread and K part: 16-byte loads that read the device
+    // coherence point (sc1), like the agent-scope atomic loads they replace
+    const rsrc_t prs = make_rsrc(p.partial, (uint32_t)(p.ksb * TEp) * 4u);
+    auto sum_parts = [&](auto nparts_tag, auto nvec_tag) {
+      constexpr int NP = decltype(nparts_tag)::value;   // K parts held at once
+      constexpr int NV = decltype(nvec_tag)::value;     // vectors per thread at once
+      for (int base = 0; base < TEp / 4; base += NV * kFusedWaves * kWave) {
+        f32x4 part[NV][NP];
 #pragma unroll
-    for (int kp = 0; kp < kFusedMaxKsb; ++kp)
-      part[kp] = kp < p.ksb ? __hip_atomic_load(&p.partial[(size_t)kp * TE + i], __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT)
-                            : 0.0f;
-    float a = part[0];
+        for (int u = 0; u < NV; ++u) {   // every load of the round before any sum
+          const int i4 = base + tid + u * kFusedWaves * kWave;
 #pragma unroll
-    for (int kp = 1; kp < kFusedMaxKsb; ++kp)
-      if (kp < p.ksb) a += part[kp];
-    s_logit[i] = a + (p.bias ? p.bias[e] : 0.0f);
+          for (int kp = 0; kp < NP; ++kp)
+            if (kp < p.ksb && i4 < TEp / 4)
+              part[u][kp] = __builtin_bit_cast(
+                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                             prs, (uint32_t)(kp * TEp + 4 * i4) * 4u, 0, kBufCoherent));
+        }
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+          const int i4 = base + tid + u * kFusedWaves * kWave;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int i = 4 * i4 + c;
+            if (i < TE) {
+              float a = part[u][0][c];
+#pragma unroll
+              for (int kp = 1; kp < NP; ++kp)
+                if (kp < p.ksb) a += part[u][kp][c];
+              s_logit[i] = a + (p.bias ? p.bias[i % E] : 0.0f);
+            }
+          }
+        }
+      }
+    };
+    if (p.ksb <= 4)     // two vectors per thread: up to 8192 logits in one round trip
+      sum_parts(std::integral_constant<int, 4>(), std::integral_constant<int, 2>());
+    else
+      sum_parts(std::integral_constant<int, kFusedMaxKsb>(), std::integral_constant<int, 1>());
   }
   __syncthreads();
 
