@@ -99,3 +99,30 @@ def test_prefill_kernel_path(E, H, F, k, T):
     with ragged segment tails (segments not multiples of 128 rows)."""
     cfg = get_config("prefill", num_experts=E, hidden=H, ffn=F, top_k=k, dead_experts=1)
     run_layer_case(cfg, T, batch=3)
+
+
+def test_one_workspace_for_calls_of_different_sizes():
+    """Buffers and workspace allocated once for the largest call, then calls of
+    growing and shrinking T in turn: the fused router (T <= 64), the
+    separate router and permutation, and the MFMA prefill path (T >= 128 here)
+    must each find what they need, with no state left over from the calls
+    before."""
+    cfg = get_config("prefill", num_experts=16, hidden=256, ffn=384, top_k=4, shared_ffn=128)
+    mats, experts = quantized_experts(cfg)
+    wr, b = G.router(cfg)
+    shared = G.shared_expert(cfg)
+    layer = make_gpu_layer(cfg, mats, wr, b, shared)
+    buf = layer.alloc(700)
+    for T in (13, 1, 700, 8, 64, 65, 0, 150, 5):
+        x = G.activations(cfg, tokens=max(T, 1), batch=T)[:T]
+        out = layer.forward(to_dev(x), buf, T=T)
+        torch.cuda.synchronize()
+        if T == 0:
+            continue
+        ref = O.moe_layer(x, wr, b, experts, cfg.top_k, shared=shared)
+        diff = route_compare(_np(buf.topk_idx)[:T], ref["idx"], ref["logits"], cfg.top_k)
+        if not diff.any():
+            np.testing.assert_array_equal(_np(buf.offsets), ref["offsets"])
+            np.testing.assert_array_equal(_np(buf.perm_src)[:T * cfg.top_k], ref["perm_src"])
+        ok = ~diff
+        tol_check(_np(out)[ok], ref["out"][ok], f"T={T} out")
