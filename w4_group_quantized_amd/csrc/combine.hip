@@ -72,10 +72,115 @@ __global__ __launch_bounds__(256) void combine_kernel(const f16 *__restrict__ y_
   }
 }
 
+// Without the norm the columns are independent: one 64-thread block per
+// (token, 512 columns), so a small batch spreads over many CUs.
+__global__ __launch_bounds__(64) void combine_cols_kernel(const f16 *__restrict__ y_perm,
+                                                          const f16 *__restrict__ ys,
+                                                          const int32_t *__restrict__ inv_pos,
+                                                          const float *__restrict__ w, int k,
+                                                          int H, int N, f16 *__restrict__ out) {
+  const int chunks = (H + 511) / 512;
+  const int t = blockIdx.x / chunks;
+  const int c = (blockIdx.x % chunks) * 512 + threadIdx.x * 8;
+  if (c >= H) return;
+  float v[8];
+  if (ys) {
+    const f16x8 a = as_f16x8(ld16(ys + (size_t)t * H + c));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (float)a[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+  }
+  for (int j = 0; j < k; ++j) {
+    int r = inv_pos[(size_t)t * k + j];
+    r = r < 0 ? 0 : (r >= N ? N - 1 : r);
+    const float wj = w[(size_t)t * k + j];
+    const f16x8 y = as_f16x8(ld16(y_perm + (size_t)r * H + c));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = fmaf(wj, (float)y[i], v[i]);
+  }
+  f16x8 o;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = (f16)v[i];
+  *reinterpret_cast<f16x8 *>(out + (size_t)t * H + c) = o;
+}
+
+// With the norm, rows of up to 8192 columns: one block per token, one thread
+// per 8 columns, the combined row kept in registers (formed once).
+__global__ __launch_bounds__(1024) void combine_norm_kernel(const f16 *__restrict__ y_perm,
+                                                            const f16 *__restrict__ ys,
+                                                            const int32_t *__restrict__ inv_pos,
+                                                            const float *__restrict__ w, int k,
+                                                            int H, int N, float eps,
+                                                            f16 *__restrict__ out) {
+  __shared__ int s_row[kMaxK];
+  __shared__ float s_w[kMaxK];
+  __shared__ float s_red[16];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (tid < k) {
+    int r = inv_pos[(size_t)t * k + tid];
+    s_row[tid] = r < 0 ? 0 : (r >= N ? N - 1 : r);
+    s_w[tid] = w[(size_t)t * k + tid];
+  }
+  const int c = tid * 8;
+  const bool live = c < H;
+  float v[8];
+  if (ys && live) {
+    const f16x8 a = as_f16x8(ld16(ys + (size_t)t * H + c));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (float)a[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+  }
+  __syncthreads();
+  if (live) {
+    for (int j = 0; j < k; ++j) {
+      const f16x8 y = as_f16x8(ld16(y_perm + (size_t)s_row[j] * H + c));
+      const float wj = s_w[j];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = fmaf(wj, (float)y[i], v[i]);
+    }
+  }
+  float ss = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ss = fmaf(v[i], v[i], ss);
+  ss = wave_sum(ss);
+  const int nw = blockDim.x / kWave;
+  if ((tid & (kWave - 1)) == 0) s_red[tid / kWave] = ss;
+  __syncthreads();
+  float tot = 0.0f;
+  for (int i = 0; i < nw; ++i) tot += s_red[i];        // fixed order
+  const float scale = 1.0f / sqrtf(tot / (float)H + eps);
+  if (live) {
+    f16x8 o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = (f16)(v[i] * scale);
+    *reinterpret_cast<f16x8 *>(out + (size_t)t * H + c) = o;
+  }
+}
+
 hipError_t launch_combine(const moe_layer &L, const uint16_t *y_perm, const uint16_t *y_shared,
                           const int32_t *inv_pos, const float *w, int32_t T, uint32_t flags,
                           float eps, uint16_t *out, hipStream_t st) {
   const int k = L.top_k, H = L.hidden;
+  if (!(flags & MOE_RMSNORM)) {
+    hipLaunchKernelGGL(combine_cols_kernel, dim3(T * ((H + 511) / 512)), dim3(64), 0, st,
+                       reinterpret_cast<const f16 *>(y_perm),
+                       reinterpret_cast<const f16 *>(y_shared), inv_pos, w, k, H, T * k,
+                       reinterpret_cast<f16 *>(out));
+    return hipGetLastError();
+  }
+  if (H <= 8192) {
+    const int threads = ((H / 8 + kWave - 1) / kWave) * kWave;
+    hipLaunchKernelGGL(combine_norm_kernel, dim3(T), dim3(threads), 0, st,
+                       reinterpret_cast<const f16 *>(y_perm),
+                       reinterpret_cast<const f16 *>(y_shared), inv_pos, w, k, H, T * k, eps,
+                       reinterpret_cast<f16 *>(out));
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(256), 0, st,
                      reinterpret_cast<const f16 *>(y_perm), reinterpret_cast<const f16 *>(y_shared),
                      inv_pos, w, k, H, T * k, (flags & MOE_RMSNORM) ? 1 : 0, eps,
