@@ -69,6 +69,14 @@ def test_prefill_like_ragged_segments(separate_calls):
     run_layer_case(cfg, 150, separate_calls=separate_calls)
 
 
+def test_largest_expert_count_and_top_k():
+    """1024 experts, top-32, 4 tokens: the tile lookups over 1024 segments and
+    32 rows of y_perm per token in the combine."""
+    cfg = get_config("decode_fine", num_experts=1024, hidden=256, ffn=128, top_k=32,
+                     shared_ffn=128)
+    run_layer_case(cfg, 4, batch=9)
+
+
 def test_layer_is_deterministic():
     cfg = get_config("decode_fine", num_experts=32, hidden=384, ffn=256, shared_ffn=128)
     layer, buf, x = run_layer_case(cfg, 11)

@@ -81,6 +81,8 @@ ROUTE_CASES = [
     ("prefill", {}, 300),
     ("decode_fine", {}, 333),      # 32-token x 128-expert tiles: 3 expert tiles, last one partial
     ("tiny", {}, 257),             # same tiles with 8 experts and a ragged token tail
+    ("tiny", {"num_experts": 1024, "top_k": 32, "hidden": 512}, 6),   # largest E and k
+    ("tiny", {"num_experts": 1000, "top_k": 7}, 300),                 # wide tiles, E % 128 != 0
 ]
 
 
@@ -192,7 +194,9 @@ def test_permute_bitexact(T, k, E, kind):
 @pytest.mark.parametrize("name,over,T", [("tiny", {}, 16), ("decode_fine", {}, 8),
                                          ("decode_fine", {}, 16), ("decode_fine", {}, 64),
                                          ("decode_coarse", {}, 16), ("decode_fine", {}, 65),
-                                         ("prefill", {"tokens": 40}, 40)])
+                                         ("prefill", {"tokens": 40}, 40),
+                                         ("tiny", {"num_experts": 1024, "top_k": 32,
+                                                   "hidden": 512}, 8)])   # T*E at the LDS limit
 def test_route_permute_fused(name, over, T):
     """moe_route_permute (one launch for T <= 64) against the oracle: indices
     exact away from near ties; offsets/perm_src/inv_pos exact when the indices
