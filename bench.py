@@ -2,9 +2,9 @@
 
     python bench.py [--steps K] [--warmup W] [--workload decode_fine]
 
-A step is one full layer forward (route + permute -> grouped W4 FFN ->
-combine, through the C entry points) over one batch of synthetic tokens
-already resident in HBM.  Several
+A step is one full layer forward (moe_layer_forward: route + permute ->
+grouped W4 FFN -> combine) over one batch of synthetic tokens already
+resident in HBM.  Several
 independently drawn weight sets are rotated so that no expert byte is served
 from the 256 MB Infinity Cache across steps.  Prints ONE JSON line.
 
@@ -15,8 +15,8 @@ int4 + fp16 scales) + the fp16 shared expert; prefill: algorithmic FLOPs =
 6*H*F per (token, chosen expert) pair; divided by the stage's average
 duration: K FFN calls with the steps' weight sets, batches and routing, run
 back to back on the launch stream between one pair of HIP events (so no
-event-processing gaps land on the kernels).  `ffn_us_in_step` is the same
-stage timed with events around it inside every step of the timed region.  `traffic` is the HBM bytes per call measured by rocprofv3 counters
+event-processing gaps land on the kernels).  `traffic` is the HBM bytes per
+call measured by rocprofv3 counters
 (profiles/traffic_<workload>.json, taken with --copy-calibration-mib and
 turned into bytes with --summarize-traffic), or null when the FFN sources
 have changed since.
@@ -85,36 +85,36 @@ def ffn_source_hash():
 
 
 def _pmc_rows(path, counter):
-    """(kernel name, value) per dispatch of one counter in a rocprofv3 CSV."""
+    """(kernel name, grid size, value) per dispatch of one counter in a
+    rocprofv3 CSV."""
     import csv
     out = []
     with open(path) as fh:
         for r in csv.DictReader(fh):
             if r["Counter_Name"] == counter:
-                out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+                out.append((r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"])))
     return out
 
 
-def summarize_traffic(workload, fetch_csv, write_csv, copy_mib):
+def traffic_from_csv(fetch_csv, write_csv, copy_mib):
     """FFN HBM bytes per moe_w4_grouped_ffn call from FETCH_SIZE and WRITE_SIZE
     (KiB per dispatch), each scaled by bytes/counter of the plain copy."""
-    res = {"workload": workload, "source_sha256": ffn_source_hash(), "copy_mib": copy_mib}
+    res = {"copy_mib": copy_mib}
     known = copy_mib * 1024 * 1024
     for key, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
         rows = _pmc_rows(path, counter)
         # the calibration copies are the HIP runtime's device-to-device copy
         # kernel (torch copies contiguous same-dtype tensors with it); they are
         # the three largest dispatches of that kernel in the run
-        copies = sorted(v for n, v in rows if "copybuffer" in n.lower())
+        copies = sorted(v for n, _, v in rows if "copybuffer" in n.lower())
         if len(copies) < 3:
             raise SystemExit(f"{path}: calibration copy dispatches not found")
         copy_kib = float(np.median(copies[-3:]))
         factor = known / (copy_kib * 1024.0)
         per_kernel = {}
-        for n, v in rows:
-            for k in FFN_KERNELS:
-                if k in n:
-                    per_kernel.setdefault(n, []).append(v)
+        for n, _, v in rows:
+            if any(k in n for k in FFN_KERNELS):
+                per_kernel.setdefault(n, []).append(v)
         if not per_kernel:
             raise SystemExit(f"{path}: no FFN dispatch found")
         call_kib = sum(float(np.mean(v)) for v in per_kernel.values())
@@ -122,6 +122,13 @@ def summarize_traffic(workload, fetch_csv, write_csv, copy_mib):
                     "ffn_kib_per_call": call_kib, "ffn_bytes_per_call": call_kib * 1024.0 * factor,
                     "dispatches": {n: len(v) for n, v in per_kernel.items()}}
     res["traffic_bytes_per_call"] = res["fetch"]["ffn_bytes_per_call"] + res["write"]["ffn_bytes_per_call"]
+    return res
+
+
+def summarize_traffic(workload, fetch_csv, write_csv, copy_mib):
+    """Write profiles/traffic_<workload>.json for the current FFN sources."""
+    res = {"workload": workload, "source_sha256": ffn_source_hash()}
+    res.update(traffic_from_csv(fetch_csv, write_csv, copy_mib))
     out = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     with open(out, "w") as fh:
         json.dump(res, fh, indent=1)
@@ -279,22 +286,15 @@ def main():
 
     n_combo = n_sets * args.batches
 
-    def step(i, ev_pair=None):
+    def step(i):
         layers = sets[i % n_sets]
         x = xs[(i // n_sets) % args.batches]
         for li, layer in enumerate(layers):
-            last = li == len(layers) - 1
-            layer.route_permute(x, bufs, T)
-            if ev_pair is not None and li == 0:
-                ev_pair[0].record(stream)
-            layer.ffn(x, bufs, T)
-            if ev_pair is not None and li == 0:
-                ev_pair[1].record(stream)
-            if last:
-                layer.combine(bufs, T, rmsnorm=layers_per_step > 1, eps=cfg.rms_eps)
+            if li == len(layers) - 1:
+                layer.forward(x, bufs, T, rmsnorm=layers_per_step > 1, eps=cfg.rms_eps)
             else:
                 nxt = act[li % 2]
-                layer.combine(bufs, T, rmsnorm=True, eps=cfg.rms_eps, out=nxt)
+                layer.forward(x, bufs, T, rmsnorm=True, eps=cfg.rms_eps, out=nxt)
                 x = nxt
 
     # algorithmic bytes of the FFN stage per (weight set, batch) combination,
@@ -316,21 +316,18 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(K)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
     for i in range(K):
-        step(i, evs[i])
+        step(i)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / K
-    ffn_ms_in_step = np.array([a.elapsed_time(b) for a, b in evs])
 
     # The FFN stage alone: the same K calls (same weight sets, batches and
     # routing as the steps) back to back between one pair of events, so that
@@ -374,7 +371,6 @@ def main():
                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic}
     roofline.update({"kernel": "moe_w4_grouped_ffn (gate/up launch + down launch)",
                      "ffn_us_mean": float(ffn_ms_mean * 1e3),
-                     "ffn_us_in_step": float(ffn_ms_in_step.mean() * 1e3),
                      "ffn_bytes_mean": float(ffn_bytes.mean()), "ffn_flops": ffn_flops,
                      "ffn_tflops": achieved_tflops, "ffn_gbs": achieved_gbs})
 

@@ -189,6 +189,26 @@ moe_status moe_unpermute_combine(const moe_layer *layer, const uint16_t *y_perm,
                                  const float *topk_w, int32_t T, uint32_t flags,
                                  float eps, uint16_t *out, void *stream);
 
+/* One whole layer forward in one call: moe_route_permute,
+ * moe_w4_grouped_ffn and moe_unpermute_combine run in that order on `stream`
+ * with these arguments, and every output is bitwise what those three calls
+ * give (fewer host calls per layer; per-launch overhead is the concern of
+ * xdnf.cn/news/329730 §3.2, grouped GEMM and CUDA Graph).
+ *   x, T, topk_idx, topk_w, offsets, perm_src, inv_pos, x_perm  as in
+ *        moe_route_permute (x_perm may be NULL; then T*H*2 must be below
+ *        2^31, else MOE_EUNSUPPORTED)
+ *   y_perm, y_shared  as in moe_w4_grouped_ffn (y_shared NULL when
+ *        shared_ffn = 0; ignored then)
+ *   flags, eps, out   as in moe_unpermute_combine, with y_shared as its
+ *        shared term
+ * All arguments are checked before the first launch. */
+moe_status moe_layer_forward(const moe_layer *layer, const uint16_t *x, int32_t T,
+                             int32_t *topk_idx, float *topk_w, int32_t *offsets,
+                             int32_t *perm_src, int32_t *inv_pos, uint16_t *x_perm,
+                             uint16_t *y_perm, uint16_t *y_shared, uint32_t flags,
+                             float eps, uint16_t *out, void *ws, size_t ws_bytes,
+                             void *stream);
+
 /* Test hook: out[n][c] = q[n][c] * s[n][c/128] in fp32 (exact, row-major
  * [rows, cols]) for one matrix in the packed format above; rows multiple of
  * 16, cols multiple of 128 (MOE_EUNSUPPORTED otherwise). */

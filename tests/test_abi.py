@@ -114,6 +114,41 @@ def test_other_calls_argument_errors():
     assert N.lib.moe_w4_quantize(None, 0, 256, None, None, None) == OK     # empty: no-op
 
 
+def test_layer_forward_argument_errors():
+    """The whole-layer call checks every stage's arguments before launching."""
+    L = layer()
+    big = 1 << 30
+    fwd = N.lib.moe_layer_forward
+    # (layer, x, T, idx, w, offsets, perm_src, inv_pos, x_perm, y_perm, y_shared, flags, eps,
+    #  out, ws, ws_bytes, stream)
+    args = [ctypes.byref(L), FAKE, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 0, 1e-6,
+            FAKE, FAKE, big, None]
+
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return fwd(*a)
+
+    assert call(a1=None) == EINVAL                      # no x
+    assert call(a3=MISALIGNED) == EINVAL                # topk_idx misaligned
+    assert call(a6=None) == EINVAL                      # no perm_src
+    assert call(a8=MISALIGNED) == EINVAL                # x_perm misaligned
+    assert call(a9=None) == EINVAL                      # no y_perm
+    assert call(a11=2) == EINVAL                        # unknown flag
+    assert call(a11=1, a12=-1.0) == EINVAL              # negative eps
+    assert call(a13=None) == EINVAL                     # no out
+    assert call(a15=64) == EWS
+    assert call(a0=ctypes.byref(layer(top_k=9))) == EUNSUP
+    assert call(a2=(1 << 31) // (2 * L.hidden)) == EUNSUP   # gather from x needs T*H*2 < 2^31
+    Ls = layer(shared_ffn=256)
+    assert call(a0=ctypes.byref(Ls), a10=FAKE) == EINVAL   # shared weights missing
+    Ls2 = layer(shared_ffn=256, shared_gate=FAKE, shared_up=FAKE, shared_down=FAKE)
+    assert call(a0=ctypes.byref(Ls2)) == EINVAL            # shared expert but no y_shared
+    assert call(a2=0, a1=None, a3=None, a4=None, a5=None, a6=None, a7=None, a9=None,
+                a13=None, a14=None, a15=0) == OK            # T = 0: no-op
+
+
 def test_status_strings():
     for s in (OK, EINVAL, EUNSUP, EWS, -4):
         assert N.moe_status_str(s)

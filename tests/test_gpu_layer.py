@@ -134,3 +134,64 @@ def test_one_workspace_for_calls_of_different_sizes():
             np.testing.assert_array_equal(_np(buf.perm_src)[:T * cfg.top_k], ref["perm_src"])
         ok = ~diff
         tol_check(_np(out)[ok], ref["out"][ok], f"T={T} out")
+
+
+@pytest.mark.parametrize("E,H,F,Fs,k,T,gather", [
+    (48, 512, 256, 256, 8, 8, False),     # one-launch router
+    (48, 384, 256, 384, 4, 40, False),    # three token tiles
+    (32, 256, 128, 0, 2, 5, False),       # no shared expert
+    (16, 256, 384, 128, 4, 64, True),     # the largest one-launch batch, x_perm written
+    (16, 256, 384, 128, 4, 150, False),   # separate router and permutation launches
+    (16, 256, 384, 128, 4, 150, True),
+    (128, 1024, 256, 512, 8, 64, False),  # T*E = 8192 logits: the one-launch limit
+])
+def test_forward_matches_staged_calls(E, H, F, Fs, k, T, gather):
+    """moe_layer_forward against moe_route_permute + moe_w4_grouped_ffn +
+    moe_unpermute_combine on the same inputs: every output bitwise equal, and
+    the layer output within the oracle tolerance."""
+    cfg = get_config("decode_fine", num_experts=E, hidden=H, ffn=F, top_k=k, shared_ffn=Fs)
+    mats, experts = quantized_experts(cfg)
+    wr, b = G.router(cfg)
+    shared = G.shared_expert(cfg)
+    x = G.activations(cfg, tokens=T, batch=T)
+    ref = O.moe_layer(x, wr, b, experts, cfg.top_k, shared=shared)
+    layer = make_gpu_layer(cfg, mats, wr, b, shared)
+    b1, b2 = layer.alloc(T), layer.alloc(T)
+    xd = to_dev(x)
+    layer.forward(xd, b1, gather=gather)
+    layer.forward_staged(xd, b2, gather=gather)
+    torch.cuda.synchronize()
+    names = ["topk_idx", "topk_w", "offsets", "perm_src", "inv_pos", "y_perm", "y_shared", "out"]
+    if gather:
+        names.append("x_perm")
+    for name in names:
+        assert _np(getattr(b1, name)).tobytes() == _np(getattr(b2, name)).tobytes(), name
+    diff = route_compare(_np(b1.topk_idx), ref["idx"], ref["logits"], cfg.top_k)
+    if gather and not diff.any():
+        assert _np(b1.x_perm).tobytes() == np.asarray(ref["x_perm"], np.float16).tobytes()
+    ok = ~diff
+    tol_check(_np(b1.out)[ok], ref["out"][ok], "out")
+
+
+def test_forward_into_separate_output_with_norm():
+    """moe_layer_forward writing `out` (not the buffer's) with the RMS norm, as
+    between stacked layers, against the staged calls doing the same."""
+    cfg = get_config("decode_fine", num_experts=40, hidden=512, ffn=256, shared_ffn=256)
+    mats, experts = quantized_experts(cfg)
+    wr, b = G.router(cfg)
+    shared = G.shared_expert(cfg)
+    x = G.activations(cfg, tokens=16, batch=5)
+    ref = O.moe_layer(x, wr, b, experts, cfg.top_k, shared=shared)
+    layer = make_gpu_layer(cfg, mats, wr, b, shared)
+    buf = layer.alloc(16)
+    o1 = torch.empty((16, cfg.hidden), dtype=torch.float16, device=buf.out.device)
+    o2 = torch.empty_like(o1)
+    xd = to_dev(x)
+    layer.forward(xd, buf, rmsnorm=True, eps=cfg.rms_eps, out=o1)
+    layer.forward_staged(xd, buf, rmsnorm=True, eps=cfg.rms_eps, out=o2)
+    torch.cuda.synchronize()
+    assert _np(o1).tobytes() == _np(o2).tobytes()
+    normed = O.rmsnorm(ref["out"], cfg.rms_eps)
+    diff = route_compare(_np(buf.topk_idx), ref["idx"], ref["logits"], cfg.top_k)
+    ok = ~diff
+    tol_check(_np(o1)[ok], normed[ok], "out")

@@ -29,9 +29,8 @@ lib = ctypes.CDLL(LIB_PATH)
 MOE_RMSNORM = 1
 
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_route_permute",
-           "moe_w4_grouped_ffn",
-           "moe_unpermute_combine", "moe_w4_dequant", "moe_w4_quantize", "moe_status_str",
-           "moe_last_hip_error")
+           "moe_w4_grouped_ffn", "moe_unpermute_combine", "moe_layer_forward",
+           "moe_w4_dequant", "moe_w4_quantize", "moe_status_str", "moe_last_hip_error")
 
 
 class MoeLayer(ctypes.Structure):
@@ -71,6 +70,8 @@ _sigs = {
     "moe_w4_grouped_ffn": (ctypes.c_int, [_LP, _P, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
     "moe_unpermute_combine": (ctypes.c_int, [_LP, _P, _P, _P, _P, _I32, ctypes.c_uint32,
                                              ctypes.c_float, _P, _P]),
+    "moe_layer_forward": (ctypes.c_int, [_LP, _P, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
+                                         ctypes.c_uint32, ctypes.c_float, _P, _P, _SZ, _P]),
     "moe_w4_dequant": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P]),
     "moe_w4_quantize": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
     "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
@@ -161,6 +162,15 @@ def moe_unpermute_combine(layer, y_perm, y_shared, inv_pos, topk_w, T, flags, ep
            lib.moe_unpermute_combine(ctypes.byref(layer), _ptr(y_perm), _ptr(y_shared),
                                      _ptr(inv_pos), _ptr(topk_w), T, flags, eps, _ptr(out),
                                      _stream(stream)))
+
+
+def moe_layer_forward(layer, x, T, topk_idx, topk_w, offsets, perm_src, inv_pos, x_perm, y_perm,
+                      y_shared, flags, eps, out, ws, ws_bytes, stream=None):
+    _check("moe_layer_forward",
+           lib.moe_layer_forward(ctypes.byref(layer), _ptr(x), T, _ptr(topk_idx), _ptr(topk_w),
+                                 _ptr(offsets), _ptr(perm_src), _ptr(inv_pos), _ptr(x_perm),
+                                 _ptr(y_perm), _ptr(y_shared), flags, eps, _ptr(out), _ptr(ws),
+                                 ws_bytes, _stream(stream)))
 
 
 def moe_w4_dequant(q, s, rows, cols, out, stream=None):

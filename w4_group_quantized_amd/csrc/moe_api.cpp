@@ -76,6 +76,77 @@ static inline moe_status hip_status(hipError_t e) {
 // not be reported as ours: clear them before launching.
 static inline void clear_stale_hip_error() { (void)hipGetLastError(); }
 
+// Pointer checks of the stages (the layer and T > 0 already checked).
+static moe_status check_route_args(const moe_layer *L, const uint16_t *x,
+                                   const int32_t *topk_idx, const float *topk_w) {
+  if (!ok_ptr(L->router_w) || !ok_ptr(x) || !ok_ptr(topk_idx) || !ok_ptr(topk_w))
+    return MOE_EINVAL;
+  if (L->router_b && !aligned16(L->router_b)) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+static moe_status check_permute_args(const uint16_t *x, const int32_t *topk_idx,
+                                     const int32_t *offsets, const int32_t *perm_src,
+                                     const int32_t *inv_pos, const uint16_t *x_perm) {
+  if (!ok_ptr(topk_idx) || !ok_ptr(offsets) || !ok_ptr(perm_src) || !ok_ptr(inv_pos))
+    return MOE_EINVAL;
+  if (x_perm && (!ok_ptr(x) || !aligned16(x_perm))) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+static moe_status check_ffn_args(const moe_layer *L, int32_t T, const uint16_t *x,
+                                 const uint16_t *x_perm, const int32_t *perm_src,
+                                 const int32_t *offsets, const uint16_t *y_perm,
+                                 const uint16_t *y_shared) {
+  if (!ok_ptr(offsets) || !ok_ptr(y_perm) || !ok_ptr(L->gate_q) || !ok_ptr(L->gate_s) ||
+      !ok_ptr(L->up_q) || !ok_ptr(L->up_s) || !ok_ptr(L->down_q) || !ok_ptr(L->down_s))
+    return MOE_EINVAL;
+  if (x_perm ? !aligned16(x_perm) : (!ok_ptr(x) || !ok_ptr(perm_src))) return MOE_EINVAL;
+  // gathering rows straight from x addresses it with 32-bit byte offsets
+  if (!x_perm && (int64_t)T * L->hidden * 2 >= ((int64_t)1 << 31)) return MOE_EUNSUPPORTED;
+  if (L->shared_ffn > 0 && (!ok_ptr(x) || !ok_ptr(y_shared) || !ok_ptr(L->shared_gate) ||
+                            !ok_ptr(L->shared_up) || !ok_ptr(L->shared_down)))
+    return MOE_EINVAL;
+  return MOE_OK;
+}
+
+static moe_status check_combine_args(const uint16_t *y_perm, const uint16_t *y_shared,
+                                     const int32_t *inv_pos, const float *topk_w,
+                                     uint32_t flags, float eps, const uint16_t *out) {
+  if (!ok_ptr(y_perm) || !ok_ptr(inv_pos) || !ok_ptr(topk_w) || !ok_ptr(out)) return MOE_EINVAL;
+  if (y_shared && !aligned16(y_shared)) return MOE_EINVAL;
+  if (flags & ~MOE_RMSNORM) return MOE_EINVAL;
+  if ((flags & MOE_RMSNORM) && !(eps >= 0.0f)) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+static inline bool fused_route(const moe_layer &L, int32_t T) {
+  return T <= kFusedMaxT && (int64_t)T * L.num_experts <= kFusedMaxLogits;
+}
+
+// Route + permute on `st`: one launch for small batches, else the router
+// and the permutation launches.
+static hipError_t run_route_permute(const moe_layer &L, const uint16_t *x, int32_t T,
+                                    int32_t *topk_idx, float *topk_w, int32_t *offsets,
+                                    int32_t *perm_src, int32_t *inv_pos, uint16_t *x_perm,
+                                    char *base, const WsLayout &w, hipStream_t st) {
+  if (fused_route(L, T)) {
+    hipError_t e = launch_route_permute_fused(
+        L, x, T, topk_idx, topk_w, offsets, perm_src, inv_pos,
+        reinterpret_cast<float *>(base + w.logits), reinterpret_cast<unsigned int *>(base + w.sync),
+        st);
+    if (e == hipSuccess && x_perm) e = launch_gather(L, x, perm_src, T, x_perm, st);
+    return e;
+  }
+  hipError_t e = launch_route(L, x, T, topk_idx, topk_w,
+                              reinterpret_cast<float *>(base + w.logits), st);
+  if (e == hipSuccess)
+    e = launch_permute(L, x, topk_idx, T, offsets, perm_src, inv_pos, x_perm,
+                       reinterpret_cast<int32_t *>(base + w.counts),
+                       reinterpret_cast<int32_t *>(base + w.bases), st);
+  return e;
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -93,9 +164,7 @@ moe_status moe_route(const moe_layer *L, const uint16_t *x, int32_t T, int32_t *
   if ((s = check_layer(L)) != MOE_OK) return s;
   if ((s = check_tokens(L, T)) != MOE_OK) return s;
   if (T == 0) return MOE_OK;
-  if (!ok_ptr(L->router_w) || !ok_ptr(x) || !ok_ptr(topk_idx) || !ok_ptr(topk_w))
-    return MOE_EINVAL;
-  if (L->router_b && !aligned16(L->router_b)) return MOE_EINVAL;
+  if ((s = check_route_args(L, x, topk_idx, topk_w)) != MOE_OK) return s;
   if ((s = check_ws(L, T, ws, ws_bytes)) != MOE_OK) return s;
   const WsLayout w = ws_layout(*L, T);
   float *logits = reinterpret_cast<float *>(static_cast<char *>(ws) + w.logits);
@@ -110,9 +179,8 @@ moe_status moe_permute(const moe_layer *L, const uint16_t *x, const int32_t *top
   if ((s = check_layer(L)) != MOE_OK) return s;
   if ((s = check_tokens(L, T)) != MOE_OK) return s;
   if (T == 0) return MOE_OK;
-  if (!ok_ptr(topk_idx) || !ok_ptr(offsets) || !ok_ptr(perm_src) || !ok_ptr(inv_pos))
-    return MOE_EINVAL;
-  if (x_perm && (!ok_ptr(x) || !aligned16(x_perm))) return MOE_EINVAL;
+  if ((s = check_permute_args(x, topk_idx, offsets, perm_src, inv_pos, x_perm)) != MOE_OK)
+    return s;
   if ((s = check_ws(L, T, ws, ws_bytes)) != MOE_OK) return s;
   const WsLayout w = ws_layout(*L, T);
   char *base = static_cast<char *>(ws);
@@ -130,31 +198,14 @@ moe_status moe_route_permute(const moe_layer *L, const uint16_t *x, int32_t T, i
   if ((s = check_layer(L)) != MOE_OK) return s;
   if ((s = check_tokens(L, T)) != MOE_OK) return s;
   if (T == 0) return MOE_OK;
-  if (!ok_ptr(L->router_w) || !ok_ptr(x) || !ok_ptr(topk_idx) || !ok_ptr(topk_w) ||
-      !ok_ptr(offsets) || !ok_ptr(perm_src) || !ok_ptr(inv_pos))
-    return MOE_EINVAL;
-  if (L->router_b && !aligned16(L->router_b)) return MOE_EINVAL;
-  if (x_perm && !aligned16(x_perm)) return MOE_EINVAL;
+  if ((s = check_route_args(L, x, topk_idx, topk_w)) != MOE_OK) return s;
+  if ((s = check_permute_args(x, topk_idx, offsets, perm_src, inv_pos, x_perm)) != MOE_OK)
+    return s;
   if ((s = check_ws(L, T, ws, ws_bytes)) != MOE_OK) return s;
   const WsLayout w = ws_layout(*L, T);
-  char *base = static_cast<char *>(ws);
-  hipStream_t st = (hipStream_t)stream;
   clear_stale_hip_error();
-  if (T <= kFusedMaxT && (int64_t)T * L->num_experts <= kFusedMaxLogits) {
-    hipError_t e = launch_route_permute_fused(
-        *L, x, T, topk_idx, topk_w, offsets, perm_src, inv_pos,
-        reinterpret_cast<float *>(base + w.logits), reinterpret_cast<unsigned int *>(base + w.sync),
-        st);
-    if (e == hipSuccess && x_perm) e = launch_gather(*L, x, perm_src, T, x_perm, st);
-    return hip_status(e);
-  }
-  hipError_t e = launch_route(*L, x, T, topk_idx, topk_w,
-                              reinterpret_cast<float *>(base + w.logits), st);
-  if (e == hipSuccess)
-    e = launch_permute(*L, x, topk_idx, T, offsets, perm_src, inv_pos, x_perm,
-                       reinterpret_cast<int32_t *>(base + w.counts),
-                       reinterpret_cast<int32_t *>(base + w.bases), st);
-  return hip_status(e);
+  return hip_status(run_route_permute(*L, x, T, topk_idx, topk_w, offsets, perm_src, inv_pos,
+                                      x_perm, static_cast<char *>(ws), w, (hipStream_t)stream));
 }
 
 moe_status moe_w4_grouped_ffn(const moe_layer *L, const uint16_t *x, const uint16_t *x_perm,
@@ -165,15 +216,8 @@ moe_status moe_w4_grouped_ffn(const moe_layer *L, const uint16_t *x, const uint1
   if ((s = check_layer(L)) != MOE_OK) return s;
   if ((s = check_tokens(L, T)) != MOE_OK) return s;
   if (T == 0) return MOE_OK;
-  if (!ok_ptr(offsets) || !ok_ptr(y_perm) || !ok_ptr(L->gate_q) || !ok_ptr(L->gate_s) ||
-      !ok_ptr(L->up_q) || !ok_ptr(L->up_s) || !ok_ptr(L->down_q) || !ok_ptr(L->down_s))
-    return MOE_EINVAL;
-  if (x_perm ? !aligned16(x_perm) : (!ok_ptr(x) || !ok_ptr(perm_src))) return MOE_EINVAL;
-  // gathering rows straight from x addresses it with 32-bit byte offsets
-  if (!x_perm && (int64_t)T * L->hidden * 2 >= ((int64_t)1 << 31)) return MOE_EUNSUPPORTED;
-  if (L->shared_ffn > 0 && (!ok_ptr(x) || !ok_ptr(y_shared) || !ok_ptr(L->shared_gate) ||
-                            !ok_ptr(L->shared_up) || !ok_ptr(L->shared_down)))
-    return MOE_EINVAL;
+  if ((s = check_ffn_args(L, T, x, x_perm, perm_src, offsets, y_perm, y_shared)) != MOE_OK)
+    return s;
   if ((s = check_ws(L, T, ws, ws_bytes)) != MOE_OK) return s;
   const WsLayout w = ws_layout(*L, T);
   char *base = static_cast<char *>(ws);
@@ -193,13 +237,43 @@ moe_status moe_unpermute_combine(const moe_layer *L, const uint16_t *y_perm,
   if ((s = check_layer(L)) != MOE_OK) return s;
   if ((s = check_tokens(L, T)) != MOE_OK) return s;
   if (T == 0) return MOE_OK;
-  if (!ok_ptr(y_perm) || !ok_ptr(inv_pos) || !ok_ptr(topk_w) || !ok_ptr(out)) return MOE_EINVAL;
-  if (y_shared && !aligned16(y_shared)) return MOE_EINVAL;
-  if (flags & ~MOE_RMSNORM) return MOE_EINVAL;
-  if ((flags & MOE_RMSNORM) && !(eps >= 0.0f)) return MOE_EINVAL;
+  if ((s = check_combine_args(y_perm, y_shared, inv_pos, topk_w, flags, eps, out)) != MOE_OK)
+    return s;
   clear_stale_hip_error();
   return hip_status(launch_combine(*L, y_perm, y_shared, inv_pos, topk_w, T, flags, eps, out,
                                    (hipStream_t)stream));
+}
+
+moe_status moe_layer_forward(const moe_layer *L, const uint16_t *x, int32_t T, int32_t *topk_idx,
+                             float *topk_w, int32_t *offsets, int32_t *perm_src, int32_t *inv_pos,
+                             uint16_t *x_perm, uint16_t *y_perm, uint16_t *y_shared,
+                             uint32_t flags, float eps, uint16_t *out, void *ws, size_t ws_bytes,
+                             void *stream) {
+  moe_status s;
+  if ((s = check_layer(L)) != MOE_OK) return s;
+  if ((s = check_tokens(L, T)) != MOE_OK) return s;
+  if (T == 0) return MOE_OK;
+  if ((s = check_route_args(L, x, topk_idx, topk_w)) != MOE_OK) return s;
+  if ((s = check_permute_args(x, topk_idx, offsets, perm_src, inv_pos, x_perm)) != MOE_OK)
+    return s;
+  if ((s = check_ffn_args(L, T, x, x_perm, perm_src, offsets, y_perm, y_shared)) != MOE_OK)
+    return s;
+  uint16_t *ys = L->shared_ffn > 0 ? y_shared : nullptr;
+  if ((s = check_combine_args(y_perm, ys, inv_pos, topk_w, flags, eps, out)) != MOE_OK) return s;
+  if ((s = check_ws(L, T, ws, ws_bytes)) != MOE_OK) return s;
+  const WsLayout w = ws_layout(*L, T);
+  char *base = static_cast<char *>(ws);
+  const hipStream_t st = (hipStream_t)stream;
+  clear_stale_hip_error();
+  hipError_t e = run_route_permute(*L, x, T, topk_idx, topk_w, offsets, perm_src, inv_pos, x_perm,
+                                   base, w, st);
+  if (e == hipSuccess)
+    e = launch_ffn(*L, x, x_perm, perm_src, offsets, T, y_perm, ys,
+                   reinterpret_cast<uint16_t *>(base + w.h),
+                   reinterpret_cast<uint16_t *>(base + w.h_shared), st);
+  if (e == hipSuccess)
+    e = launch_combine(*L, y_perm, ys, inv_pos, topk_w, T, flags, eps, out, st);
+  return hip_status(e);
 }
 
 moe_status moe_w4_dequant(const uint8_t *q, const uint16_t *s, int64_t rows, int64_t cols,

@@ -98,17 +98,34 @@ class W4MoELayer:
                                 buf.inv_pos, buf.topk_w, T, N.MOE_RMSNORM if rmsnorm else 0,
                                 eps, buf.out if out is None else out, stream)
 
-    def forward(self, x, buf, T=None, rmsnorm=False, eps=1e-6, out=None, stream=None):
+    def forward(self, x, buf, T=None, rmsnorm=False, eps=1e-6, out=None, gather=False,
+                stream=None):
         """x fp16 [T, H] on the device -> buf.out (or `out`) fp16 [T, H].
 
-        Three launches-worth of calls: route + permute (one launch for small
-        batches), the grouped FFN reading token rows through perm_src, and the
+        One C call (moe_layer_forward): route + permute (one launch for small
+        batches), the grouped FFN reading token rows through perm_src (or from
+        buf.x_perm, written by the permutation, with gather=True), and the
         combine."""
         T = x.shape[0] if T is None else T
         if T > buf.max_tokens:
             raise ValueError("more tokens than the buffers were allocated for")
-        self.route_permute(x, buf, T, stream=stream)
-        self.ffn(x, buf, T, stream=stream)
+        o = buf.out if out is None else out
+        N.moe_layer_forward(self.desc, x, T, buf.topk_idx, buf.topk_w, buf.offsets, buf.perm_src,
+                            buf.inv_pos, buf.x_perm if gather else None, buf.y_perm,
+                            buf.y_shared if self.Fs else None,
+                            N.MOE_RMSNORM if rmsnorm else 0, eps, o, buf.ws, buf.ws.numel(),
+                            stream)
+        return buf.out[:T] if out is None else out
+
+    def forward_staged(self, x, buf, T=None, rmsnorm=False, eps=1e-6, out=None, gather=False,
+                       stream=None):
+        """The same layer as three C calls: moe_route_permute,
+        moe_w4_grouped_ffn, moe_unpermute_combine."""
+        T = x.shape[0] if T is None else T
+        if T > buf.max_tokens:
+            raise ValueError("more tokens than the buffers were allocated for")
+        self.route_permute(x, buf, T, gather=gather, stream=stream)
+        self.ffn(x, buf, T, use_x_perm=gather, stream=stream)
         self.combine(buf, T, rmsnorm, eps, out, stream)
         return buf.out[:T] if out is None else out
 
