@@ -52,7 +52,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="decode_fine",
-                    choices=["decode_fine", "decode_coarse", "prefill", "decode_stack", "tiny"])
+                    choices=["decode_fine", "decode_coarse", "prefill", "decode_stack",
+                             "decode_fine512", "tiny"])
     ap.add_argument("--weight-sets", type=int, default=0, help="0 = workload default")
     ap.add_argument("--batches", type=int, default=4, help="distinct token batches rotated")
     ap.add_argument("--no-cpu-baseline", action="store_true")

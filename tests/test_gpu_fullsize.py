@@ -68,7 +68,7 @@ def oracle_tokens(x64, wr, b, k, experts, shared):
 
 
 @pytest.mark.parametrize("name,n_sample", [("decode_fine", None), ("decode_coarse", None),
-                                           ("prefill", 48)])
+                                           ("prefill", 48), ("decode_fine512", None)])
 def test_full_size_layer(name, n_sample):
     cfg = get_config(name)
     layer, mats, wr, b, shared = device_layer(cfg)

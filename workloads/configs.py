@@ -1,4 +1,4 @@
-"""The five MoE-layer workloads, with the input recipe of each.
+"""The MoE-layer workloads, with the input recipe of each.
 
 Shapes and distributions follow the workload descriptions of this project;
 the expert shape of the fine-grained layers (288 routed experts + 1 shared,
@@ -15,6 +15,15 @@ Readings (the descriptions leave these open):
   * "uniform-random routing logits" (coarse layer): router weights
     N(0, 1/H) and no bias, so every expert is equally likely.
   * expert weights N(0, 0.02) where not stated; shared expert fp16 N(0, 0.02).
+  * the 512-expert decode layer (the second model of [P5] §09: 48 layers, 512
+    routed experts, 10 routed + 1 shared per token, expert intermediate size
+    640) gets hidden 2560: the page gives no width, and 125B parameters over
+    48 layers x 512 experts x 3 matrices x 640 leave at most ~2650 for the
+    experts alone, so the nearest common model width below it; the shared
+    expert has the routed experts' shape (ffn 640); 8 decode tokens as in the
+    288-expert layer; the same Zipf(1.1) bias recipe, with alpha = 0.5 so
+    that again about 20% of the experts take about 80% of the selections
+    (logit std ~1.01 from N(0,0.02) router weights at H = 2560).
 """
 from __future__ import annotations
 
@@ -78,6 +87,9 @@ CONFIGS = {
     "decode_stack": MoEConfig("decode_stack", 5, num_experts=288, hidden=4096,
                               ffn=1536, top_k=8, tokens=16, shared_ffn=1536,
                               layers=42, zipf_alpha=0.7),
+    "decode_fine512": MoEConfig("decode_fine512", 6, num_experts=512, hidden=2560,
+                                ffn=640, top_k=10, tokens=8, shared_ffn=640,
+                                zipf_alpha=0.5),
 }
 
 
