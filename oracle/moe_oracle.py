@@ -31,10 +31,15 @@ the 16 rows' chunks side by side:
                                           + c * 256 + (n % 16) * 16 + b
 
 so the 16 rows x 128 columns of one quantization group are 1 KB contiguous.
-The fp16 scales [out, in/128] are stored the same way, 16 rows side by side:
-offset(row n, group g) = (n // 16) * 16 * (in/128) + g * 16 + n % 16.
+The fp16 scales [out, in/group] are stored the same way, 16 rows side by
+side: offset(row n, group g) = (n // 16) * 16 * (in/group) + g * 16 + n % 16.
 Both are kept as arrays of the logical shape [out, in/2] bytes and
-[out, in/128] fp16 whose memory follows these offsets.
+[out, in/group] fp16 whose memory follows these offsets.
+
+Group size: 128 everywhere unless a caller asks for 64 or 256, the two
+neighbours [P2] §2.1 reports measuring (64: more scale metadata for no
+speed; 256: quantization error starts to show) and the one [P2] §4.1
+suggests trying when output quality drops (64).
 """
 from __future__ import annotations
 
@@ -141,7 +146,7 @@ def unpack_w4(packed: np.ndarray) -> np.ndarray:
 
 
 def pack_scales(s: np.ndarray) -> np.ndarray:
-    """fp16 scales [out, in/128] -> stored order (16 rows side by side)."""
+    """fp16 scales [out, in/group] -> stored order (16 rows side by side)."""
     return _rows_to_tiles(np.asarray(s, dtype=np.float16), 1)
 
 
@@ -251,10 +256,12 @@ def swiglu_ffn(X: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray) ->
     return h @ np.asarray(Wd, dtype=np.float64).T
 
 
-def expert_ffn_w4(X, gate_q, gate_s, up_q, up_s, down_q, down_s) -> np.ndarray:
-    """One routed expert: dequantize its three int4 matrices, then SwiGLU."""
-    return swiglu_ffn(X, dequant(gate_q, gate_s), dequant(up_q, up_s),
-                      dequant(down_q, down_s))
+def expert_ffn_w4(X, gate_q, gate_s, up_q, up_s, down_q, down_s,
+                  group: int = GROUP) -> np.ndarray:
+    """One routed expert: dequantize its three int4 matrices (scales per
+    `group` columns), then SwiGLU."""
+    return swiglu_ffn(X, dequant(gate_q, gate_s, group), dequant(up_q, up_s, group),
+                      dequant(down_q, down_s, group))
 
 
 # ---------------------------------------------------------------------------

@@ -68,36 +68,39 @@ def test_quantizer_golden_example():
     np.testing.assert_array_equal(q, exp)
 
 
-def test_quantizer_exact_rational_bruteforce():
+@pytest.mark.parametrize("group", [64, 128, 256])
+def test_quantizer_exact_rational_bruteforce(group):
     """Recompute s and q for random fp16 weights with exact rational
     arithmetic and a brute-force fp16 rounding, independent of float64."""
     g = np.random.default_rng(2)
-    w = (g.standard_normal((3, 256)) * 0.02).astype(np.float16)
-    q, s = O.group_quantize(w)
+    w = (g.standard_normal((3, 512)) * 0.02).astype(np.float16)
+    q, s = O.group_quantize(w, group)
+    assert s.shape == (3, 512 // group)
     for n in range(w.shape[0]):
-        for grp in range(2):
-            ws = [Fraction(float(v)) for v in w[n, grp * 128:(grp + 1) * 128]]
+        for grp in range(512 // group):
+            ws = [Fraction(float(v)) for v in w[n, grp * group:(grp + 1) * group]]
             m = max(abs(v) for v in ws)
             s_ref = nearest_f16(m / 7)
             assert Fraction(float(s[n, grp])) == s_ref
             for c, v in enumerate(ws):
                 r = nearest_f16(v / s_ref)
                 q_ref = max(-8, min(7, round(r)))          # round(): half to even
-                assert int(q[n, grp * 128 + c]) == q_ref
+                assert int(q[n, grp * group + c]) == q_ref
 
 
-def test_quantizer_invariants():
+@pytest.mark.parametrize("group", [64, 128, 256])
+def test_quantizer_invariants(group):
     cfg = get_config("tiny")
     w = G.expert_master(cfg, 0, 3, G.GATE).astype(np.float16)       # [512, 256]
-    w[5, 128:256] = 0                                               # an all-zero group
-    q, s = O.group_quantize(w)
+    w[5, 256 - group:256] = 0                                       # an all-zero group
+    q, s = O.group_quantize(w, group)
     assert q.min() >= -7 and q.max() <= 7                           # -8 never produced
-    qa = np.abs(q.astype(np.int32)).reshape(q.shape[0], -1, 128).max(-1)
+    qa = np.abs(q.astype(np.int32)).reshape(q.shape[0], -1, group).max(-1)
     nz = s.astype(np.float64) > 0
     assert (qa[nz] == 7).all()
-    assert (qa[~nz] == 0).all() and not nz[5, 1]
-    err = np.abs(w.astype(np.float64) - O.dequant(O.pack_w4(q), O.pack_scales(s)))
-    bound = (0.5 + 2.0 ** -9) * np.repeat(s.astype(np.float64), 128, axis=1)
+    assert (qa[~nz] == 0).all() and not nz[5, -1]
+    err = np.abs(w.astype(np.float64) - O.dequant(O.pack_w4(q), O.pack_scales(s), group))
+    bound = (0.5 + 2.0 ** -9) * np.repeat(s.astype(np.float64), group, axis=1)
     assert (err <= bound).all()
 
 
@@ -140,14 +143,15 @@ def test_scale_layout():
     np.testing.assert_array_equal(O.unpack_scales(O.pack_scales(s)), s)
 
 
-def test_dequant_exact():
+@pytest.mark.parametrize("group", [64, 128, 256])
+def test_dequant_exact(group):
     g = np.random.default_rng(3)
     q = g.integers(-8, 8, size=(16, 256)).astype(np.int8)
-    s = (g.uniform(1e-3, 1e-2, size=(16, 2))).astype(np.float16)
-    W = O.dequant(O.pack_w4(q), O.pack_scales(s))
+    s = (g.uniform(1e-3, 1e-2, size=(16, 256 // group))).astype(np.float16)
+    W = O.dequant(O.pack_w4(q), O.pack_scales(s), group)
     for n in range(16):
         for c in range(0, 256, 7):
-            assert Fraction(W[n, c]) == int(q[n, c]) * Fraction(float(s[n, c // 128]))
+            assert Fraction(W[n, c]) == int(q[n, c]) * Fraction(float(s[n, c // group]))
     # q*s is exact in fp32 as well (4 + 11 significant bits)
     np.testing.assert_array_equal(W.astype(np.float32).astype(np.float64), W)
 
