@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--workload", default="decode_fine",
                     choices=["decode_fine", "decode_coarse", "prefill", "decode_stack",
                              "decode_fine512", "tiny"])
+    ap.add_argument("--group-size", type=int, default=128, choices=[64, 128, 256],
+                    help="int4 quantization group size of the experts")
     ap.add_argument("--weight-sets", type=int, default=0, help="0 = workload default")
     ap.add_argument("--batches", type=int, default=4, help="distinct token batches rotated")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -64,7 +66,7 @@ def parse():
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU: turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, "
                          "WRITE_SIZE) of a run with --copy-calibration-mib into "
-                         "profiles/traffic_<workload>.json")
+                         "profiles/traffic_<workload>[_g<group size>].json")
     return ap.parse_args()
 
 
@@ -126,19 +128,24 @@ def traffic_from_csv(fetch_csv, write_csv, copy_mib):
     return res
 
 
-def summarize_traffic(workload, fetch_csv, write_csv, copy_mib):
-    """Write profiles/traffic_<workload>.json for the current FFN sources."""
-    res = {"workload": workload, "source_sha256": ffn_source_hash()}
+def traffic_path(workload, group_size):
+    tag = "" if group_size == 128 else f"_g{group_size}"
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}{tag}.json")
+
+
+def summarize_traffic(workload, group_size, fetch_csv, write_csv, copy_mib):
+    """Write the traffic summary of a workload for the current FFN sources."""
+    res = {"workload": workload, "group_size": group_size, "source_sha256": ffn_source_hash()}
     res.update(traffic_from_csv(fetch_csv, write_csv, copy_mib))
-    out = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    out = traffic_path(workload, group_size)
     with open(out, "w") as fh:
         json.dump(res, fh, indent=1)
     print(json.dumps(res))
 
 
-def measured_traffic(workload):
+def measured_traffic(workload, group_size=128):
     """HBM bytes per FFN call measured for the current kernel sources, else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    path = traffic_path(workload, group_size)
     try:
         with open(path) as fh:
             t = json.load(fh)
@@ -168,14 +175,15 @@ def build_layer(cfg, wset, layer_idx, dev):
     for m, name in ((G.GATE, "gate"), (G.UP, "up"), (G.DOWN, "down")):
         out_dim, in_dim = G.matrix_shape(cfg, m)
         q = torch.empty((E, out_dim, in_dim // 2), dtype=torch.uint8, device=dev)
-        s = torch.empty((E, out_dim, in_dim // 128), dtype=torch.float16, device=dev)
+        s = torch.empty((E, out_dim, in_dim // cfg.group_size), dtype=torch.float16, device=dev)
         # a few experts per draw keeps the fp32 temporaries small
         per = max(1, min(E, (1 << 28) // (out_dim * in_dim)))
         for e0 in range(0, E, per):
             e1 = min(E, e0 + per)
             seed = G.torch_seed(cfg, G.T_EXPERT, layer=layer_idx, expert=e0, matrix=m, batch=wset)
             w = gpu_normal16(((e1 - e0) * out_dim, in_dim), cfg.weight_std, seed, dev)
-            NAT.moe_w4_quantize(w, (e1 - e0) * out_dim, in_dim, q[e0:e1], s[e0:e1])
+            NAT.moe_w4_quantize(w, (e1 - e0) * out_dim, in_dim, cfg.group_size, q[e0:e1],
+                                s[e0:e1])
             del w
         mats[name] = (q, s)
     wr, b = G.router(cfg, layer_idx + 1000 * wset)
@@ -202,6 +210,7 @@ def cpu_baseline(cfg, budget_s):
     cost does not depend on their values) and only for the experts the oracle's
     own routing selects; drawing them is not timed.  Repeats the forward until
     `budget_s` is spent (at least once)."""
+    import functools
     import oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -229,7 +238,8 @@ def cpu_baseline(cfg, budget_s):
     runs, t_total = 0, 0.0
     while runs == 0 or t_total < budget_s:
         t0 = time.perf_counter()
-        O.moe_layer(x, wr, b, lazy, cfg.top_k, shared=shared)
+        O.moe_layer(x, wr, b, lazy, cfg.top_k, shared=shared,
+                    expert_ffn=functools.partial(O.expert_ffn_w4, group=cfg.group_size))
         t_total += time.perf_counter() - t0
         runs += 1
         if t_total > budget_s * 0.5 and runs >= 1 and t_total / runs > budget_s * 0.5:
@@ -257,8 +267,8 @@ def cpu_baseline(cfg, budget_s):
 def main():
     args = parse()
     if args.summarize_traffic:
-        summarize_traffic(args.workload, args.summarize_traffic[0], args.summarize_traffic[1],
-                          args.copy_calibration_mib)
+        summarize_traffic(args.workload, args.group_size, args.summarize_traffic[0],
+                          args.summarize_traffic[1], args.copy_calibration_mib)
         return
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -267,7 +277,7 @@ def main():
     import torch
     import w4_group_quantized_amd  # noqa: F401  (fails loudly without the HIP library)
 
-    cfg = get_config(args.workload)
+    cfg = get_config(args.workload, group_size=args.group_size)
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     layers_per_step = cfg.layers
@@ -362,7 +372,7 @@ def main():
     # (gate, up, down), the shared expert 6*H*Fs per token
     ffn_flops = T * (cfg.top_k * 6.0 * cfg.hidden * cfg.ffn + 6.0 * cfg.hidden * cfg.shared_ffn)
     achieved_tflops = float(ffn_flops / (ffn_ms_mean * 1e-3) / 1e12)
-    traffic = measured_traffic(cfg.name)
+    traffic = measured_traffic(cfg.name, cfg.group_size)
     if cfg.name == "prefill":
         roofline = {"bound": "mfma", "achieved": achieved_tflops, "peak": MFMA_F16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": achieved_tflops / MFMA_F16_PEAK_TFLOPS,
@@ -387,7 +397,8 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        layer_cfg = cfg if cfg.layers == 1 else get_config(cfg.name, layers=1)
+        layer_cfg = cfg if cfg.layers == 1 else get_config(cfg.name, layers=1,
+                                                           group_size=cfg.group_size)
         cpu = cpu_baseline(layer_cfg, args.cpu_budget_s)
         if cfg.layers > 1:       # one oracle layer of the 42: scale to a whole step
             cpu["value"] /= cfg.layers
@@ -410,7 +421,8 @@ def main():
             "workload": cfg.name, "experts": cfg.num_experts, "shared_ffn": cfg.shared_ffn,
             "hidden": cfg.hidden, "ffn": cfg.ffn, "top_k": cfg.top_k, "tokens": T,
             "layers_per_step": layers_per_step, "weight_sets": n_sets, "batches": args.batches,
-            "weights": "int4 g128 (fp16 scales), router fp16, shared expert fp16",
+            "group_size": cfg.group_size,
+            "weights": f"int4 g{cfg.group_size} (fp16 scales), router fp16, shared expert fp16",
             "distinct_experts_per_step_mean": float(np.mean(u_per_combo)),
         },
         "roofline": roofline,

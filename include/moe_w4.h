@@ -42,18 +42,22 @@
  *    that every call leaves at zero.
  *
  * Packed int4 weight format (this library's choice; the page stores int8
- * codes).  A matrix [out, in] (out a multiple of 16, in a multiple of 128) is
- * stored as out*in/2 bytes of codes plus out*in/128 fp16 scales.  A code q in
+ * codes).  A matrix [out, in] with group size gs (out a multiple of 16, in a
+ * multiple of 128 and of gs) is stored as out*in/2 bytes of codes plus
+ * out*in/gs fp16 scales.  A code q in
  * [-8, 7] is the nibble u = q + 8.  Eight consecutive columns 8w..8w+7 of a
  * row form one little-endian 32-bit word whose nibble p (bits 4p..4p+3) holds
  * column 8w + {0,2,4,6,1,3,5,7}[p]; four words (32 columns) form a 16-byte
  * chunk.  Rows are stored in tiles of 16, the 16 rows' chunks side by side,
- * so the 16 rows x 128 columns of one quantization group are 1 KB contiguous
- * (the weight layout is reordered for contiguous access, as
- * dpshk.com/news/6309482 §3.2 recommends):
+ * so the 16 rows x 128 columns of one block are 1 KB contiguous (the weight
+ * layout is reordered for contiguous access, as dpshk.com/news/6309482 §3.2
+ * recommends):
  *     byte(row n, chunk c, b) = (n/16)*16*(in/2) + c*256 + (n%16)*16 + b
- *     scale(row n, group g)   = (n/16)*16*(in/128) + g*16 + n%16
- * The dequantized weight is W[n][c] = q[n][c] * scale[n][c / 128].
+ *     scale(row n, group g)   = (n/16)*16*(in/gs) + g*16 + n%16
+ * The dequantized weight is W[n][c] = q[n][c] * scale[n][c / gs].  The code
+ * layout does not depend on gs.  gs is 128 (lpnh.cn/news/2730718 §2.1), or
+ * 64 or 256, the sizes that page compares it with (§2.1) and suggests trying
+ * when quality drops (64, §4.1).
  */
 #ifndef MOE_W4_H
 #define MOE_W4_H
@@ -79,12 +83,12 @@ typedef enum {
  *  hidden       H, multiple of 128, <= 65536
  *  ffn          F (per routed expert), multiple of 128
  *  top_k        k, 1..min(E, 32)
- *  group_size   must be 128
+ *  group_size   gs: 64, 128 or 256; hidden and ffn must be multiples of it
  *  router_w     fp16 [E, H]
  *  router_b     fp32 [E], or NULL for no bias (added to the logits before the
  *               softmax, so it also changes the combine weights)
  *  gate_q, up_q packed int4, E matrices [F, H] back to back (E*F*H/2 bytes);
- *               gate_s, up_s their fp16 scales (E*F*H/128)
+ *               gate_s, up_s their fp16 scales (E*F*H/gs)
  *  down_q       packed int4, E matrices [H, F] (E*H*F/2 bytes); down_s scales
  *  shared_ffn   Fs of the always-on shared expert, multiple of 128, or 0
  *  shared_gate, shared_up  fp16 [Fs, H];   shared_down   fp16 [H, Fs]
@@ -209,19 +213,21 @@ moe_status moe_layer_forward(const moe_layer *layer, const uint16_t *x, int32_t 
                              float eps, uint16_t *out, void *ws, size_t ws_bytes,
                              void *stream);
 
-/* Test hook: out[n][c] = q[n][c] * s[n][c/128] in fp32 (exact, row-major
- * [rows, cols]) for one matrix in the packed format above; rows multiple of
- * 16, cols multiple of 128 (MOE_EUNSUPPORTED otherwise). */
+/* Test hook: out[n][c] = q[n][c] * s[n][c/gs] in fp32 (exact, row-major
+ * [rows, cols]) for one matrix in the packed format above with group size
+ * gs = group_size (64, 128 or 256); rows multiple of 16, cols multiple of 128
+ * and of gs (MOE_EUNSUPPORTED otherwise). */
 moe_status moe_w4_dequant(const uint8_t *q, const uint16_t *s, int64_t rows,
-                          int64_t cols, float *out, void *stream);
+                          int64_t cols, int32_t group_size, float *out, void *stream);
 
-/* Group quantization of an fp16 matrix w [rows, cols] (cols multiple of 128),
- * lpnh.cn/news/2730718 §2.1 with every step rounded to fp16 as on an fp16
- * model: s = RN16(max|w_group| / 7), q = clamp(RNE(RN16(w / s)), -8, 7); an
- * all-zero group gets s = 0, q = 0.  w is row-major; writes q and s in the
- * packed format above.  rows multiple of 16, cols multiple of 128. */
+/* Group quantization of an fp16 matrix w [rows, cols] in groups of
+ * group_size columns (64, 128 or 256), lpnh.cn/news/2730718 §2.1 with every
+ * step rounded to fp16 as on an fp16 model: s = RN16(max|w_group| / 7),
+ * q = clamp(RNE(RN16(w / s)), -8, 7); an all-zero group gets s = 0, q = 0.
+ * w is row-major; writes q and s in the packed format above.  rows multiple
+ * of 16, cols multiple of 128 and of group_size. */
 moe_status moe_w4_quantize(const uint16_t *w, int64_t rows, int64_t cols,
-                           uint8_t *q, uint16_t *s, void *stream);
+                           int32_t group_size, uint8_t *q, uint16_t *s, void *stream);
 
 /* Static description of a status code (host). */
 const char *moe_status_str(moe_status status);

@@ -45,7 +45,7 @@ def tol_check(gpu_vals, ref, what="", rel=1e-2, abs_=1e-3):
 def quantized_experts(cfg, layer=0, experts=None):
     """Oracle-quantized expert weights from fp16 masters, stacked per matrix.
 
-    Returns dict of numpy arrays gate_q [E,F,H/2], gate_s [E,F,H/128], ...
+    Returns dict of numpy arrays gate_q [E,F,H/2], gate_s [E,F,H/gs], ...
     and the per-expert tuple list the oracle takes."""
     E = cfg.num_experts
     ids = range(E) if experts is None else experts
@@ -54,7 +54,7 @@ def quantized_experts(cfg, layer=0, experts=None):
     for e in ids:
         tup = []
         for m, name in ((G.GATE, "gate"), (G.UP, "up"), (G.DOWN, "down")):
-            q, s = O.group_quantize(G.expert_master(cfg, layer, e, m))
+            q, s = O.group_quantize(G.expert_master(cfg, layer, e, m), cfg.group_size)
             p, ss = O.pack_w4(q), O.pack_scales(s)
             mats[name + "_q"].append(p)
             mats[name + "_s"].append(ss)

@@ -49,10 +49,15 @@ def test_workspace_size_and_invalid_layers():
     assert N.moe_workspace_size(layer(hidden=200), 16) == 0
     assert N.moe_workspace_size(L, -1) == 0
     assert N.moe_workspace_size(L, 32) >= N.moe_workspace_size(L, 16)
+    for gs in (64, 256):      # the other group sizes are valid layers
+        assert N.moe_workspace_size(layer(group_size=gs), 16) == N.moe_workspace_size(L, 16)
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(group_size=64), EUNSUP),
+    (dict(group_size=32), EUNSUP),
+    (dict(group_size=512), EUNSUP),
+    (dict(group_size=256, hidden=384), EUNSUP),   # hidden not a whole number of groups
+    (dict(group_size=256, ffn=640), EUNSUP),      # ffn not a whole number of groups
     (dict(hidden=200), EUNSUP),
     (dict(ffn=100), EUNSUP),
     (dict(top_k=9), EUNSUP),
@@ -107,11 +112,15 @@ def test_other_calls_argument_errors():
                                        None) == EINVAL                      # unknown flag
     assert N.lib.moe_unpermute_combine(ctypes.byref(L), FAKE, None, FAKE, FAKE, 4, 1, -1.0,
                                        FAKE, None) == EINVAL                # negative eps
-    assert N.lib.moe_w4_dequant(FAKE, FAKE, 4, 100, FAKE, None) == EUNSUP
-    assert N.lib.moe_w4_quantize(FAKE, 16, 256, None, FAKE, None) == EINVAL
-    assert N.lib.moe_w4_quantize(FAKE, -16, 256, FAKE, FAKE, None) == EINVAL
-    assert N.lib.moe_w4_quantize(FAKE, 8, 256, FAKE, FAKE, None) == EUNSUP        # rows % 16
-    assert N.lib.moe_w4_quantize(None, 0, 256, None, None, None) == OK     # empty: no-op
+    assert N.lib.moe_w4_dequant(FAKE, FAKE, 16, 100, 128, FAKE, None) == EUNSUP
+    assert N.lib.moe_w4_dequant(FAKE, FAKE, 16, 256, 32, FAKE, None) == EUNSUP    # group 32
+    assert N.lib.moe_w4_dequant(FAKE, FAKE, 16, 384, 256, FAKE, None) == EUNSUP   # 384 % 256
+    assert N.lib.moe_w4_quantize(FAKE, 16, 256, 128, None, FAKE, None) == EINVAL
+    assert N.lib.moe_w4_quantize(FAKE, -16, 256, 128, FAKE, FAKE, None) == EINVAL
+    assert N.lib.moe_w4_quantize(FAKE, 8, 256, 128, FAKE, FAKE, None) == EUNSUP   # rows % 16
+    assert N.lib.moe_w4_quantize(FAKE, 16, 256, 100, FAKE, FAKE, None) == EUNSUP  # group 100
+    assert N.lib.moe_w4_quantize(FAKE, 16, 384, 256, FAKE, FAKE, None) == EUNSUP  # 384 % 256
+    assert N.lib.moe_w4_quantize(None, 0, 256, 64, None, None, None) == OK  # empty: no-op
 
 
 def test_layer_forward_argument_errors():

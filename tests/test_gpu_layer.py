@@ -1,5 +1,7 @@
 """End-to-end parity of one MoE layer forward (route -> permute -> grouped FFN
 -> combine, all through the C ABI) against the float64 oracle."""
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -23,12 +25,17 @@ def _np(t):
     return t.detach().cpu().numpy()
 
 
+def oracle_layer(x, wr, b, experts, cfg, shared):
+    return O.moe_layer(x, wr, b, experts, cfg.top_k, shared=shared,
+                       expert_ffn=functools.partial(O.expert_ffn_w4, group=cfg.group_size))
+
+
 def run_layer_case(cfg, T, batch=0, separate_calls=False):
     mats, experts = quantized_experts(cfg)
     wr, b = G.router(cfg)
     shared = G.shared_expert(cfg)
     x = G.activations(cfg, tokens=T, batch=batch)
-    ref = O.moe_layer(x, wr, b, experts, cfg.top_k, shared=shared)
+    ref = oracle_layer(x, wr, b, experts, cfg, shared)
     layer = make_gpu_layer(cfg, mats, wr, b, shared)
     buf = layer.alloc(T)
     xd = to_dev(x)
@@ -107,6 +114,25 @@ def test_prefill_kernel_path(E, H, F, k, T):
     with ragged segment tails (segments not multiples of 128 rows)."""
     cfg = get_config("prefill", num_experts=E, hidden=H, ffn=F, top_k=k, dead_experts=1)
     run_layer_case(cfg, T, batch=3)
+
+
+@pytest.mark.parametrize("gs,E,H,F,k,T", [(64, 16, 256, 384, 4, 150), (256, 8, 512, 256, 2, 700),
+                                          (64, 32, 768, 384, 8, 300)])
+def test_prefill_kernel_path_group_sizes(gs, E, H, F, k, T):
+    """The MFMA prefill path with 64- and 256-column groups (its scale of a
+    64-column K step is group step, step / 2 or step / 4)."""
+    cfg = get_config("prefill", num_experts=E, hidden=H, ffn=F, top_k=k, dead_experts=1,
+                     group_size=gs)
+    run_layer_case(cfg, T, batch=4)
+
+
+@pytest.mark.parametrize("gs", [64, 256])
+def test_decode_layer_group_sizes(gs):
+    """A fine-grained decode layer (one-launch router, shared expert) with
+    64- and 256-column groups."""
+    cfg = get_config("decode_fine", num_experts=48, hidden=512, ffn=256, shared_ffn=256,
+                     group_size=gs)
+    run_layer_case(cfg, 8, batch=gs)
 
 
 def test_one_workspace_for_calls_of_different_sizes():
@@ -195,3 +221,11 @@ def test_forward_into_separate_output_with_norm():
     diff = route_compare(_np(buf.topk_idx), ref["idx"], ref["logits"], cfg.top_k)
     ok = ~diff
     tol_check(_np(o1)[ok], normed[ok], "out")
+
+
+@pytest.mark.parametrize("E,k", [(1, 1), (32, 1), (16, 4), (8, 8)])
+def test_small_top_k_and_single_expert(E, k):
+    """Top-1 (one expert per token, one-expert layers) and top-k = E."""
+    cfg = get_config("decode_fine", num_experts=E, hidden=512, ffn=256, top_k=k,
+                     shared_ffn=128)
+    run_layer_case(cfg, 11, batch=E + k)

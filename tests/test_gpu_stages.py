@@ -25,21 +25,22 @@ def _np(t):
 
 
 # ---------------------------------------------------------------- quantizer / dequant
-@pytest.mark.parametrize("shape", [(512, 256), (64, 4096), (48, 1024)])
-def test_quantize_bitexact(shape):
+@pytest.mark.parametrize("shape,gs", [((512, 256), 128), ((64, 4096), 128), ((48, 1024), 128),
+                                      ((64, 4096), 64), ((48, 384), 64), ((32, 1024), 256),
+                                      ((512, 256), 256)])
+def test_quantize_bitexact(shape, gs):
     from w4_group_quantized_amd import quantize_fp16
-    cfg = get_config("tiny")
-    g = np.random.default_rng(shape[0])
+    g = np.random.default_rng(shape[0] + gs)
     w = (g.standard_normal(shape, dtype=np.float32) * 0.02).astype(np.float16)
-    w[3, :128] = 0                                    # all-zero group
-    w[5, 128:256] = np.float16(1e-7)                  # subnormal-range group
+    w[3, :gs] = 0                                     # all-zero group
+    w[5, shape[1] - gs:] = np.float16(1e-7)           # subnormal-range group
     w[6, :] = -w[6, :]
-    q_ref, s_ref = O.group_quantize(w)
-    q, s = quantize_fp16(to_dev(w))
+    q_ref, s_ref = O.group_quantize(w, gs)
+    q, s = quantize_fp16(to_dev(w), gs)
     torch.cuda.synchronize()
+    assert tuple(s.shape) == (shape[0], shape[1] // gs)
     np.testing.assert_array_equal(_np(s).view(np.uint16), O.pack_scales(s_ref).view(np.uint16))
     np.testing.assert_array_equal(_np(q), O.pack_w4(q_ref))
-    del cfg
 
 
 def test_quantize_golden_fixture():
@@ -59,16 +60,17 @@ def test_quantize_golden_fixture():
     np.testing.assert_array_equal(codes, exp)
 
 
-def test_dequant_bitexact_all_codes():
+@pytest.mark.parametrize("gs", [64, 128, 256])
+def test_dequant_bitexact_all_codes(gs):
     from w4_group_quantized_amd import dequantize
     g = np.random.default_rng(11)
     packed = g.integers(0, 256, size=(96, 384), dtype=np.uint8)    # every code, including -8
     packed[0, :256] = np.arange(256, dtype=np.uint8)
-    s = (g.uniform(1e-4, 5e-2, size=(96, 6))).astype(np.float16)
+    s = (g.uniform(1e-4, 5e-2, size=(96, 768 // gs))).astype(np.float16)
     s[1, 2] = 0
     out = dequantize(to_dev(packed), to_dev(s))
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(_np(out).astype(np.float64), O.dequant(packed, s))
+    np.testing.assert_array_equal(_np(out).astype(np.float64), O.dequant(packed, s, gs))
 
 
 # ---------------------------------------------------------------- router
@@ -106,7 +108,7 @@ def _router_only_layer(cfg, wr, b):
     z8 = to_dev(np.zeros((1, 1, 16), np.uint8))
     z16 = to_dev(np.zeros((1, 1, 8), np.float16))
     layer = W4MoELayer(cfg.top_k, to_dev(wr), to_dev(b) if b is not None else None,
-                       z8, z16, z8, z16, z8, z16)
+                       z8, z16, z8, z16, z8, z16, group_size=cfg.group_size)
     layer.desc.ffn = cfg.ffn
     return layer
 
@@ -233,6 +235,19 @@ FFN_CASES = [
     # under two rows per expert on average, but every token also picks expert
     # 0: one 7-row tile of 8 KB rows (56 KB: streamed) among 1-row tiles
     ("tiny", {"num_experts": 8, "hidden": 4096, "ffn": 128, "top_k": 2}, 7, 128, True),
+    # group sizes 64 and 256: one scale per 64 columns (folded into the
+    # unpacked weights) and one per 256 (two K blocks per scale), on the
+    # narrow and the wide tile shapes
+    ("tiny", {"num_experts": 12, "hidden": 512, "ffn": 384, "top_k": 3, "group_size": 64}, 9,
+     256, False),
+    ("tiny", {"num_experts": 4, "hidden": 2048, "ffn": 512, "top_k": 2, "group_size": 64}, 40,
+     256, False),
+    ("tiny", {"num_experts": 12, "hidden": 512, "ffn": 256, "top_k": 3, "group_size": 256}, 9,
+     256, False),
+    ("tiny", {"num_experts": 4, "hidden": 2048, "ffn": 512, "top_k": 2, "group_size": 256}, 40,
+     256, False),
+    ("tiny", {"num_experts": 8, "hidden": 4096, "ffn": 256, "top_k": 2, "group_size": 64}, 7,
+     128, True),
 ]
 
 
@@ -266,7 +281,7 @@ def test_ffn_teacher_forced(name, over, T, Fs, skew, use_x_perm):
     for e in range(cfg.num_experts):
         a, bnd = int(off[e]), int(off[e + 1])
         if bnd > a:
-            ref = O.expert_ffn_w4(x_perm[a:bnd], *experts[e])
+            ref = O.expert_ffn_w4(x_perm[a:bnd], *experts[e], group=cfg.group_size)
             tol_check(y_perm[a:bnd], ref, f"expert {e}")
     if Fs:
         tol_check(_np(buf.y_shared), O.swiglu_ffn(x, *shared), "shared")

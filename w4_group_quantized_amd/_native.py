@@ -72,8 +72,8 @@ _sigs = {
                                              ctypes.c_float, _P, _P]),
     "moe_layer_forward": (ctypes.c_int, [_LP, _P, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
                                          ctypes.c_uint32, ctypes.c_float, _P, _P, _SZ, _P]),
-    "moe_w4_dequant": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P]),
-    "moe_w4_quantize": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
+    "moe_w4_dequant": (ctypes.c_int, [_P, _P, _I64, _I64, _I32, _P, _P]),
+    "moe_w4_quantize": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P]),
     "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_last_hip_error": (ctypes.c_char_p, []),
 }
@@ -173,14 +173,14 @@ def moe_layer_forward(layer, x, T, topk_idx, topk_w, offsets, perm_src, inv_pos,
                                  ws_bytes, _stream(stream)))
 
 
-def moe_w4_dequant(q, s, rows, cols, out, stream=None):
-    _check("moe_w4_dequant", lib.moe_w4_dequant(_ptr(q), _ptr(s), rows, cols, _ptr(out),
-                                                _stream(stream)))
+def moe_w4_dequant(q, s, rows, cols, group_size, out, stream=None):
+    _check("moe_w4_dequant", lib.moe_w4_dequant(_ptr(q), _ptr(s), rows, cols, group_size,
+                                                _ptr(out), _stream(stream)))
 
 
-def moe_w4_quantize(w, rows, cols, q, s, stream=None):
-    _check("moe_w4_quantize", lib.moe_w4_quantize(_ptr(w), rows, cols, _ptr(q), _ptr(s),
-                                                  _stream(stream)))
+def moe_w4_quantize(w, rows, cols, group_size, q, s, stream=None):
+    _check("moe_w4_quantize", lib.moe_w4_quantize(_ptr(w), rows, cols, group_size, _ptr(q),
+                                                  _ptr(s), _stream(stream)))
 
 
 def moe_status_str(status: int) -> str:

@@ -14,7 +14,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
-constexpr int kGroup = 128;   // weights per quantization group along in_features
+constexpr int kGroup = 128;   // columns per K block: one 1 KB chunk of a 16-row int4 tile
 
 // D[16x16] += A[16x32] * B[32x16], fp16 inputs, fp32 accumulation.
 // Lane l supplies A row (l % 16) and B column (l % 16), 8 consecutive k each,

@@ -96,8 +96,8 @@ __device__ bool locate_tile(const int32_t *__restrict__ off, int E, int slot, in
 }
 
 // PHASE 1: PAIR = gate and up tiles per wave, SwiGLU epilogue.
-// PHASE 2: one matrix, plain epilogue.
-template <int PHASE, int NT, int S>
+// PHASE 2: one matrix, plain epilogue.  GM: quantization group size (GroupMode).
+template <int PHASE, int NT, int S, int GM>
 __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
   constexpr bool kPair = PHASE == 1;
   constexpr int kMats = kPair ? 2 : 1;
@@ -123,15 +123,18 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
     const uint8_t *qrow[kMats * NT];
     const f16 *srow[kMats * NT];
     int nrow[NT];
+    // scale groups per row, and this lane's scale within a 64-column pair
+    const int Gs = GM == kG64 ? 2 * G : (GM == kG256 ? G / 2 : G);
+    const int sl = r + (GM == kG64 ? (kb >> 1) * 16 : 0);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       nrow[t] = nt * 64 * NT + (wid * NT + t) * 16 + r;
       const size_t row0 = (size_t)e * Nrows + (nrow[t] - r);      // first row of the tile
       qrow[t] = p.q0 + row0 * (K / 2) + lane * 16;
-      srow[t] = p.s0 + row0 * G + r;
+      srow[t] = p.s0 + row0 * Gs + sl;
       if (kPair) {
         qrow[NT + t] = p.q1 + row0 * (K / 2) + lane * 16;
-        srow[NT + t] = p.s1 + row0 * G + r;
+        srow[NT + t] = p.s1 + row0 * Gs + sl;
       }
     }
     f32x4 acc[kMats * NT];
@@ -171,7 +174,7 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
 #pragma unroll
       for (int j = 0; j < kStagePieces; ++j) stg[j] = bload16(rs, voff[j], 0);
       const ALds<kActLdsVec> al(s_act, min(r, rows - 1), stride, kb);
-      w4_tiles<kMats * NT, S>(al, qrow, srow, 0, G, acc, [&] {
+      w4_tiles<kMats * NT, S, GM>(al, qrow, srow, 0, G, acc, [&] {
 #pragma unroll
         for (int j = 0; j < kStagePieces; ++j) {
           const int i = j * 256 + tid;
@@ -193,7 +196,7 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
       const ARows arow = p.perm_src
                              ? ARows(p.a_routed, p.T, K, tok, live, kb)
                              : ARows(p.a_routed + (size_t)seg0 * K, rows, K, tok, live, kb);
-      w4_tiles<kMats * NT, S>(arow, qrow, srow, 0, G, acc);
+      w4_tiles<kMats * NT, S, GM>(arow, qrow, srow, 0, G, acc);
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t)
@@ -254,6 +257,17 @@ constexpr int kWideMinAvgRows = 2;
 // matrix with 32-bit byte offsets.
 constexpr int kPrefillMinAvgRows = 32;
 
+// One decode launch, instantiated for the layer's group size.
+template <int PHASE, int NT, int S>
+static void launch_decode(int group_size, int blocks, const FfnArgs &a, hipStream_t st) {
+  if (group_size == 64)
+    hipLaunchKernelGGL((ffn_decode_kernel<PHASE, NT, S, kG64>), dim3(blocks), dim3(256), 0, st, a);
+  else if (group_size == 256)
+    hipLaunchKernelGGL((ffn_decode_kernel<PHASE, NT, S, kG256>), dim3(blocks), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((ffn_decode_kernel<PHASE, NT, S, kG128>), dim3(blocks), dim3(256), 0, st, a);
+}
+
 bool ffn_prefill_mode(const moe_layer &L, int32_t T) {
   const int64_t N = (int64_t)T * L.top_k;
   const int64_t H = L.hidden, F = L.ffn;
@@ -300,11 +314,9 @@ hipError_t launch_ffn(const moe_layer &L, const uint16_t *x, const uint16_t *x_p
   a.shared_items = Fs ? mtiles_shared * (Fs / 16) : 0;
   if (a.routed_items + a.shared_items > 0) {
     if (wide)
-      hipLaunchKernelGGL((ffn_decode_kernel<1, 2, 1>), dim3(a.routed_items + a.shared_items),
-                         dim3(256), 0, st, a);
+      launch_decode<1, 2, 1>(L.group_size, a.routed_items + a.shared_items, a, st);
     else
-      hipLaunchKernelGGL((ffn_decode_kernel<1, 1, 2>), dim3(a.routed_items + a.shared_items),
-                         dim3(256), 0, st, a);
+      launch_decode<1, 1, 2>(L.group_size, a.routed_items + a.shared_items, a, st);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
 
@@ -326,11 +338,9 @@ hipError_t launch_ffn(const moe_layer &L, const uint16_t *x, const uint16_t *x_p
   a.shared_items = Fs ? mtiles_shared * (H / 16) : 0;
   if (a.routed_items + a.shared_items > 0) {
     if (wide2)
-      hipLaunchKernelGGL((ffn_decode_kernel<2, 4, 1>), dim3(a.routed_items + a.shared_items),
-                         dim3(256), 0, st, a);
+      launch_decode<2, 4, 1>(L.group_size, a.routed_items + a.shared_items, a, st);
     else
-      hipLaunchKernelGGL((ffn_decode_kernel<2, 2, 2>), dim3(a.routed_items + a.shared_items),
-                         dim3(256), 0, st, a);
+      launch_decode<2, 2, 2>(L.group_size, a.routed_items + a.shared_items, a, st);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   return hipSuccess;

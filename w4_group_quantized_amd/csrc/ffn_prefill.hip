@@ -53,6 +53,7 @@ struct PrefillArgs {
   const f16 *s0, *s1;
   f16 *out;                   // phase 1: h [N, F]; phase 2: y_perm [N, H]
   int ntiles;                 // weight-row tiles per segment tile
+  int sshift;                 // scale group of K step s: s >> sshift (group 64 / 128 / 256: 0 / 1 / 2)
 };
 
 __device__ __forceinline__ f32x16 mfma_32x32x16(f16x8 a, f16x8 b, f32x16 c) {
@@ -119,6 +120,7 @@ struct PrefillOperands {
   uint32_t b_off[2];          // code chunk per N-tile in its code buffer
   uint32_t s_off[2];          // group-0 scale per N-tile in its scale buffer
   int nsteps;
+  int sshift;                 // scale group of step s: s >> sshift
 };
 
 // The K loop.  Step s: meet at the barrier (stage s % 2 is complete), issue
@@ -148,8 +150,8 @@ __device__ __forceinline__ void prefill_gemm(f16 *sA, rsrc_t a_rs, rsrc_t b_rs0,
   auto load_b = [&](int step, int u) {
     rb[u][0] = bload16(b_rs0, o.b_off[0], step * 512);
     rb[u][1] = bload16(b_rs1, o.b_off[1], step * 512);
-    rs[u][0] = bload_f16(s_rs0, o.s_off[0], (step >> 1) * 32);
-    rs[u][1] = bload_f16(s_rs1, o.s_off[1], (step >> 1) * 32);
+    rs[u][0] = bload_f16(s_rs0, o.s_off[0], (step >> o.sshift) * 32);
+    rs[u][1] = bload_f16(s_rs1, o.s_off[1], (step >> o.sshift) * 32);
   };
   auto store_a = [&](int step) {
     if (!a_loader) return;
@@ -273,7 +275,7 @@ __global__ __launch_bounds__(256, 2) void ffn_prefill_kernel(PrefillArgs p) {
   const int h = lane >> 5, l32 = lane & 31;
   const int K = kPair ? p.H : p.F;
   const int Nrows = kPair ? p.F : p.H;            // rows of one weight matrix
-  const int G = K / kGroup;
+  const int G = (K / kPK) >> p.sshift;            // scale groups per row
 
   TileInfo ti;
   if (!locate_tile(p.offsets, p.E, p.ntiles, &ti)) return;
@@ -283,6 +285,7 @@ __global__ __launch_bounds__(256, 2) void ffn_prefill_kernel(PrefillArgs p) {
 
   PrefillOperands o;
   o.nsteps = K / kPK;
+  o.sshift = p.sshift;
   // ---- activation pieces: piece j of wave wv's lane i is stored at row
   // r = 32*wv + 8*j + i/8, position i%8 of a stage (the wave's 64 lanes fill
   // 1 KB contiguously), which holds logical piece (i%8) ^ sw(r).  Rows past
@@ -358,6 +361,7 @@ hipError_t launch_ffn_prefill_phase(const moe_layer &L, int phase, const uint16_
     p.q0 = L.down_q; p.s0 = reinterpret_cast<const f16 *>(L.down_s);
     p.ntiles = L.hidden / kPN;
   }
+  p.sshift = L.group_size == 64 ? 0 : (L.group_size == 256 ? 2 : 1);
   const int max_tiles = (E < N ? E : N) + (N + kPM - 1) / kPM;
   int blocks = max_tiles * p.ntiles;
   blocks = (blocks + 7) / 8 * 8;

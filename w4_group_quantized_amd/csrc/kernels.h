@@ -10,7 +10,8 @@
 namespace moe {
 
 constexpr int kPermChunk = 256;   // flat (token, slot) entries per permutation block
-constexpr int kGroupSize = 128;   // the only group size the kernels implement
+// quantization group sizes the kernels implement (along in_features)
+constexpr bool supported_group_size(int gs) { return gs == 64 || gs == 128 || gs == 256; }
 constexpr int kFusedMaxT = 64;    // route + permute in one launch up to this many tokens
 constexpr int kRouterWideMinT = 256;   // 32-token x 128-expert router tiles from this many tokens
 constexpr int kFusedMaxKsb = 16;  // K parts of the fused router's logits
@@ -29,9 +30,9 @@ struct WsLayout {
 };
 WsLayout ws_layout(const moe_layer &L, int32_t T);
 
-hipError_t launch_quantize(const uint16_t *w, int64_t rows, int64_t cols, uint8_t *q,
+hipError_t launch_quantize(const uint16_t *w, int64_t rows, int64_t cols, int gs, uint8_t *q,
                            uint16_t *s, hipStream_t st);
-hipError_t launch_dequant(const uint8_t *q, const uint16_t *s, int64_t rows, int64_t cols,
+hipError_t launch_dequant(const uint8_t *q, const uint16_t *s, int64_t rows, int64_t cols, int gs,
                           float *out, hipStream_t st);
 hipError_t launch_route(const moe_layer &L, const uint16_t *x, int32_t T, int32_t *idx,
                         float *w, float *logits, hipStream_t st);

@@ -39,13 +39,15 @@ WsLayout ws_layout(const moe_layer &L, int32_t T) {
 // Shape limits of the kernels.
 static moe_status check_layer(const moe_layer *L) {
   if (!L) return MOE_EINVAL;
-  if (L->group_size != kGroupSize) return MOE_EUNSUPPORTED;
+  if (!supported_group_size(L->group_size)) return MOE_EUNSUPPORTED;
   if (L->num_experts < 1 || L->num_experts > 1024) return MOE_EUNSUPPORTED;
   if (L->hidden < 128 || L->hidden > 65536 || L->hidden % 128) return MOE_EUNSUPPORTED;
   if (L->ffn < 128 || L->ffn > 262144 || L->ffn % 128) return MOE_EUNSUPPORTED;
   if (L->top_k < 1 || L->top_k > 32 || L->top_k > L->num_experts) return MOE_EUNSUPPORTED;
   if (L->shared_ffn < 0 || L->shared_ffn > 262144 || L->shared_ffn % 128)
     return MOE_EUNSUPPORTED;
+  // whole groups per row of every int4 matrix (in_features H and F)
+  if (L->hidden % L->group_size || L->ffn % L->group_size) return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
 
@@ -277,25 +279,27 @@ moe_status moe_layer_forward(const moe_layer *L, const uint16_t *x, int32_t T, i
 }
 
 moe_status moe_w4_dequant(const uint8_t *q, const uint16_t *s, int64_t rows, int64_t cols,
-                          float *out, void *stream) {
+                          int32_t group_size, float *out, void *stream) {
   if (rows < 0 || cols < 0) return MOE_EINVAL;
-  if (cols % 128 || rows % 16) return MOE_EUNSUPPORTED;
+  if (!supported_group_size(group_size)) return MOE_EUNSUPPORTED;
+  if (cols % 128 || cols % group_size || rows % 16) return MOE_EUNSUPPORTED;
   if (rows == 0 || cols == 0) return MOE_OK;
   if ((rows * (cols / 8) + 255) / 256 > 0x7fffffffLL) return MOE_EUNSUPPORTED;
   if (!ok_ptr(q) || !ok_ptr(s) || !ok_ptr(out)) return MOE_EINVAL;
   clear_stale_hip_error();
-  return hip_status(launch_dequant(q, s, rows, cols, out, (hipStream_t)stream));
+  return hip_status(launch_dequant(q, s, rows, cols, group_size, out, (hipStream_t)stream));
 }
 
-moe_status moe_w4_quantize(const uint16_t *w, int64_t rows, int64_t cols, uint8_t *q, uint16_t *s,
-                           void *stream) {
+moe_status moe_w4_quantize(const uint16_t *w, int64_t rows, int64_t cols, int32_t group_size,
+                           uint8_t *q, uint16_t *s, void *stream) {
   if (rows < 0 || cols < 0) return MOE_EINVAL;
-  if (cols % 128 || rows % 16) return MOE_EUNSUPPORTED;
+  if (!supported_group_size(group_size)) return MOE_EUNSUPPORTED;
+  if (cols % 128 || cols % group_size || rows % 16) return MOE_EUNSUPPORTED;
   if (rows == 0 || cols == 0) return MOE_OK;
   if ((rows * (cols / 8) + 255) / 256 > 0x7fffffffLL) return MOE_EUNSUPPORTED;
   if (!ok_ptr(w) || !ok_ptr(q) || !ok_ptr(s)) return MOE_EINVAL;
   clear_stale_hip_error();
-  return hip_status(launch_quantize(w, rows, cols, q, s, (hipStream_t)stream));
+  return hip_status(launch_quantize(w, rows, cols, group_size, q, s, (hipStream_t)stream));
 }
 
 const char *moe_last_hip_error(void) {
@@ -306,8 +310,8 @@ const char *moe_status_str(moe_status status) {
   switch (status) {
     case MOE_OK: return "ok";
     case MOE_EINVAL: return "invalid argument (null or misaligned pointer, negative size, bad flag)";
-    case MOE_EUNSUPPORTED: return "unsupported shape (group size, hidden/ffn multiple of 128, "
-                                  "top_k, expert count)";
+    case MOE_EUNSUPPORTED: return "unsupported shape (group size 64/128/256, hidden/ffn multiple "
+                                  "of 128 and of the group size, top_k, expert count)";
     case MOE_EWORKSPACE: return "workspace smaller than moe_workspace_size()";
     case MOE_EHIP: return "HIP runtime error at launch";
   }

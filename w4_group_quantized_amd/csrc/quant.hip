@@ -20,20 +20,21 @@ __device__ __forceinline__ size_t word_offset(int64_t row, int64_t word, int64_t
   return (size_t)(row >> 4) * 16 * (cols / 2) + (size_t)(word >> 2) * 256 +
          (size_t)(row & 15) * 16 + (size_t)(word & 3) * 4;
 }
-__device__ __forceinline__ size_t scale_offset(int64_t row, int64_t g, int64_t cols) {
-  return (size_t)(row >> 4) * 16 * (cols / 128) + (size_t)g * 16 + (size_t)(row & 15);
+__device__ __forceinline__ size_t scale_offset(int64_t row, int64_t g, int64_t cols, int gs) {
+  return (size_t)(row >> 4) * 16 * (cols / gs) + (size_t)g * 16 + (size_t)(row & 15);
 }
 
-// One thread per 8 consecutive columns (one 32-bit packed word); 16 threads
-// cover one 128-column group, a wave covers 4 groups of one row.
+// One thread per 8 consecutive columns (one 32-bit packed word); gs/8
+// consecutive lanes (8, 16 or 32) cover one group of gs columns.  A row holds
+// a whole number of groups, so no group straddles two waves.
 __global__ __launch_bounds__(256) void quantize_kernel(const f16 *__restrict__ w,
-                                                       int64_t rows, int64_t cols,
+                                                       int64_t rows, int64_t cols, int gs,
                                                        uint8_t *__restrict__ q,
                                                        f16 *__restrict__ s) {
   const int64_t words_per_row = cols / 8;
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = rows * words_per_row;
-  // Lanes past the end still take part in the 16-lane max so that the
+  // Lanes past the end still take part in the group max so that the
   // shuffles see a full group; they load nothing and store nothing.
   const bool live = t < total;
   const int64_t row = live ? t / words_per_row : 0, word = live ? t % words_per_row : 0;
@@ -48,8 +49,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const f16 *__restrict__ w
       m = fmaxf(m, fabsf(v[i]));
     }
   }
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+  const int glanes = gs / 8;
+  for (int o = 1; o < glanes; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
   if (!live) return;
   const f16 s16 = (f16)__fdiv_rn(m, 7.0f);
   const float sf = (float)s16;
@@ -67,14 +68,14 @@ __global__ __launch_bounds__(256) void quantize_kernel(const f16 *__restrict__ w
   const uint32_t packed = u[0] | (u[2] << 4) | (u[4] << 8) | (u[6] << 12) | (u[1] << 16) |
                           (u[3] << 20) | (u[5] << 24) | (u[7] << 28);
   *reinterpret_cast<uint32_t *>(q + word_offset(row, word, cols)) = packed;
-  if ((word & 15) == 0) s[scale_offset(row, word / 16, cols)] = s16;
+  if (word % glanes == 0) s[scale_offset(row, word / glanes, cols, gs)] = s16;
 }
 
-// out[n][c] = q[n][c] * s[n][c/128] in fp32 (exact), decoding with the same
+// out[n][c] = q[n][c] * s[n][c/gs] in fp32 (exact), decoding with the same
 // unpack8() the FFN kernels use.  One thread per stored 32-bit word.
 __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t *__restrict__ q,
                                                       const f16 *__restrict__ s,
-                                                      int64_t rows, int64_t cols,
+                                                      int64_t rows, int64_t cols, int gs,
                                                       float *__restrict__ out) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= rows * (cols / 8)) return;
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t *__restrict
   const int64_t chunk = rem / 256, r = (rem % 256) / 16, word_in_chunk = (rem % 16) / 4;
   const int64_t row = tile * 16 + r;
   const int64_t col = chunk * 32 + word_in_chunk * 8;
-  const float sc = (float)s[scale_offset(row, col / 128, cols)];
+  const float sc = (float)s[scale_offset(row, col / gs, cols, gs)];
   const f16x8 c = unpack8(q[t], unpack_consts());
   f32x4 a = {(float)c[0] * sc, (float)c[1] * sc, (float)c[2] * sc, (float)c[3] * sc};
   f32x4 b = {(float)c[4] * sc, (float)c[5] * sc, (float)c[6] * sc, (float)c[7] * sc};
@@ -93,22 +94,23 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t *__restrict
   o[1] = b;
 }
 
-hipError_t launch_quantize(const uint16_t *w, int64_t rows, int64_t cols, uint8_t *q,
+hipError_t launch_quantize(const uint16_t *w, int64_t rows, int64_t cols, int gs, uint8_t *q,
                            uint16_t *s, hipStream_t st) {
   const int64_t total = rows * (cols / 8);
   const int64_t blocks = (total + 255) / 256;
   hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
-                     reinterpret_cast<const f16 *>(w), rows, cols, q, reinterpret_cast<f16 *>(s));
+                     reinterpret_cast<const f16 *>(w), rows, cols, gs, q,
+                     reinterpret_cast<f16 *>(s));
   return hipGetLastError();
 }
 
-hipError_t launch_dequant(const uint8_t *q, const uint16_t *s, int64_t rows, int64_t cols,
+hipError_t launch_dequant(const uint8_t *q, const uint16_t *s, int64_t rows, int64_t cols, int gs,
                           float *out, hipStream_t st) {
   const int64_t total = rows * (cols / 8);
   const int64_t blocks = (total + 255) / 256;
   hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
                      reinterpret_cast<const uint32_t *>(q), reinterpret_cast<const f16 *>(s),
-                     rows, cols, out);
+                     rows, cols, gs, out);
   return hipGetLastError();
 }
 

@@ -55,6 +55,21 @@ struct ALds {
   __device__ __forceinline__ u32x4 load(int g, int m) const { return lds[idx + 16 * g + m]; }
 };
 
+// Quantization group size of the int4 weights.  The K loop always walks
+// 128-column blocks (one 1 KB chunk per 16-row tile); the scale of a block
+// is applied after its MFMAs when the block lies inside one group (128 and
+// 256), and folded into the unpacked weights, RN16(q * s), when each lane's
+// 32 columns have their own group (64: lanes kb = 0, 1 and kb = 2, 3 of a
+// block read two different scales).
+enum GroupMode { kG128 = 0, kG64 = 1, kG256 = 2 };
+
+// Scale group of 128-column block gg (the lane's kb offset for kG64 is part
+// of the caller's scale pointer).
+template <int GM>
+__device__ __forceinline__ int scale_group(int gg) {
+  return GM == kG64 ? 2 * gg : (GM == kG256 ? gg >> 1 : gg);
+}
+
 // One pipeline stage of the int4 path: S groups of activations, weights and
 // scales for NT weight tiles.
 template <int NT, int S>
@@ -64,7 +79,7 @@ struct W4Stage {
   f16 s[S][NT];
 };
 
-template <int NT, int S, class A>
+template <int NT, int S, int GM, class A>
 __device__ __forceinline__ void w4_load(W4Stage<NT, S> &st, const A &a,
                                         const uint8_t *const (&qrow)[NT],
                                         const f16 *const (&srow)[NT], int g, int G) {
@@ -74,7 +89,7 @@ __device__ __forceinline__ void w4_load(W4Stage<NT, S> &st, const A &a,
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       st.q[i][t] = ld16(qrow[t] + (size_t)gg * 1024);
-      st.s[i][t] = srow[t][(size_t)gg * 16];
+      st.s[i][t] = srow[t][(size_t)scale_group<GM>(gg) * 16];
     }
     if (!A::kDeferred) {
 #pragma unroll
@@ -83,7 +98,7 @@ __device__ __forceinline__ void w4_load(W4Stage<NT, S> &st, const A &a,
   }
 }
 
-template <int NT, int S, class A>
+template <int NT, int S, int GM, class A>
 __device__ __forceinline__ void w4_compute(const W4Stage<NT, S> &st, const A &a, int g, int ngroups,
                                            const UnpackConsts &magic, f32x4 (&acc)[NT]) {
 #pragma unroll
@@ -94,21 +109,29 @@ __device__ __forceinline__ void w4_compute(const W4Stage<NT, S> &st, const A &a,
       for (int m = 0; m < 4; ++m) x[m] = A::kDeferred ? a.load(g + i, m) : st.x[i][m];
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
+        if (GM == kG64) {       // RN16(q * s), accumulated straight into acc
+          const f16 s = st.s[i][t];
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-          tmp = mfma_16x16x32(as_f16x8(x[m]), unpack8(st.q[i][t][m], magic), tmp);
-        const float s = (float)st.s[i][t];
-        acc[t] += s * tmp;
+          for (int m = 0; m < 4; ++m)
+            acc[t] = mfma_16x16x32(as_f16x8(x[m]), unpack8(st.q[i][t][m], magic) * s, acc[t]);
+        } else {
+          f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            tmp = mfma_16x16x32(as_f16x8(x[m]), unpack8(st.q[i][t][m], magic), tmp);
+          const float s = (float)st.s[i][t];
+          acc[t] += s * tmp;
+        }
       }
     }
   }
 }
 
 // int4 weights: acc[t] += sum_g scale[t][g] * sum_{k in g} A[tok][k] * q[t][k]
-// for g in [g0, g1).  arow: this lane's activation rows (ARows or ALds);
-// qrow[t]: base of weight tile t (16 rows) + lane*16 bytes, so group g is at
-// qrow[t] + g*1024; srow[t]: the tile's scales + r, group g at srow[t][g*16].
+// for 128-column blocks g in [g0, g1).  arow: this lane's activation rows
+// (ARows or ALds); qrow[t]: base of weight tile t (16 rows) + lane*16 bytes,
+// so block g is at qrow[t] + g*1024; srow[t]: the tile's scales + r (+ 16 for
+// lanes kb = 2, 3 with 64-column groups), scale group sg at srow[t][sg*16].
 // after_first() runs once the first stage's loads are issued (the block can
 // stage its activations there while they are in flight).  The loop body has
 // no control flow, so the two stages stay in fixed registers and only the
@@ -116,32 +139,32 @@ __device__ __forceinline__ void w4_compute(const W4Stage<NT, S> &st, const A &a,
 struct NoOp {
   __device__ __forceinline__ void operator()() const {}
 };
-template <int NT, int S, class A, class F = NoOp>
+template <int NT, int S, int GM, class A, class F = NoOp>
 __device__ __forceinline__ void w4_tiles(const A &arow, const uint8_t *const (&qrow)[NT],
                                          const f16 *const (&srow)[NT], int g0, int g1,
                                          f32x4 (&acc)[NT], F after_first = F()) {
   if (g0 >= g1) return;
   const UnpackConsts magic = unpack_consts();
   W4Stage<NT, S> a, b;
-  w4_load<NT, S>(a, arow, qrow, srow, g0, g1);
+  w4_load<NT, S, GM>(a, arow, qrow, srow, g0, g1);
   after_first();
   int g = g0;
   for (; g + 2 * S <= g1; g += 2 * S) {
-    w4_load<NT, S>(b, arow, qrow, srow, g + S, g1);
+    w4_load<NT, S, GM>(b, arow, qrow, srow, g + S, g1);
     sched_fence();
-    w4_compute<NT, S>(a, arow, g, S, magic, acc);
+    w4_compute<NT, S, GM>(a, arow, g, S, magic, acc);
     sched_fence();
-    w4_load<NT, S>(a, arow, qrow, srow, g + 2 * S, g1);
+    w4_load<NT, S, GM>(a, arow, qrow, srow, g + 2 * S, g1);
     sched_fence();
-    w4_compute<NT, S>(b, arow, g + S, S, magic, acc);
+    w4_compute<NT, S, GM>(b, arow, g + S, S, magic, acc);
     sched_fence();
   }
   const int rest = g1 - g;          // 0 <= rest < 2S groups; stage a holds group g..
   if (rest > 0) {
-    w4_compute<NT, S>(a, arow, g, rest, magic, acc);
+    w4_compute<NT, S, GM>(a, arow, g, rest, magic, acc);
     if (rest > S) {
-      w4_load<NT, S>(b, arow, qrow, srow, g + S, g1);
-      w4_compute<NT, S>(b, arow, g + S, rest - S, magic, acc);
+      w4_load<NT, S, GM>(b, arow, qrow, srow, g + S, g1);
+      w4_compute<NT, S, GM>(b, arow, g + S, rest - S, magic, acc);
     }
   }
 }

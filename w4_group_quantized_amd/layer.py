@@ -30,25 +30,32 @@ class MoEBuffers:
 
 
 class W4MoELayer:
-    """One MoE layer whose routed experts are int4 g128 and whose optional
-    shared expert is fp16.  All tensors live on one GPU.
+    """One MoE layer whose routed experts are int4 with fp16 group scales
+    (group size gs = 128, or 64 / 256; read off the scale shapes unless
+    given) and whose optional shared expert is fp16.  All tensors live on one
+    GPU.
 
     router_w fp16 [E,H], router_b fp32 [E] or None,
-    gate_q/up_q uint8 [E,F,H/2], gate_s/up_s fp16 [E,F,H/128],
-    down_q uint8 [E,H,F/2], down_s fp16 [E,H,F/128],
+    gate_q/up_q uint8 [E,F,H/2], gate_s/up_s fp16 [E,F,H/gs],
+    down_q uint8 [E,H,F/2], down_s fp16 [E,H,F/gs],
     shared = None or (Wg fp16 [Fs,H], Wu fp16 [Fs,H], Wd fp16 [H,Fs]).
     """
 
     def __init__(self, top_k, router_w, router_b, gate_q, gate_s, up_q, up_s, down_q, down_s,
-                 shared=None):
+                 shared=None, group_size=None):
         E, H = router_w.shape
         F = gate_q.shape[1]
         self.E, self.H, self.F, self.k = E, H, F, top_k
         self.Fs = shared[0].shape[0] if shared is not None else 0
+        if group_size is None:
+            group_size = H // gate_s.shape[2]
+            if gate_s.shape[2] * group_size != H or down_s.shape[2] * group_size != F:
+                raise ValueError("scale shapes do not give one group size for both matrices")
+        self.group_size = group_size
         self.tensors = (router_w, router_b, gate_q, gate_s, up_q, up_s, down_q, down_s, shared)
         sg, su, sd = shared if shared is not None else (None, None, None)
         self.desc = N.make_layer(E, H, F, top_k, router_w, router_b, gate_q, gate_s, up_q, up_s,
-                                 down_q, down_s, self.Fs, sg, su, sd)
+                                 down_q, down_s, self.Fs, sg, su, sd, group_size=self.group_size)
 
     @property
     def device(self):
@@ -130,20 +137,21 @@ class W4MoELayer:
         return buf.out[:T] if out is None else out
 
 
-def quantize_fp16(w: torch.Tensor, stream=None):
+def quantize_fp16(w: torch.Tensor, group_size: int = 128, stream=None):
     """Group-quantize an fp16 device matrix [rows, cols] with the HIP kernel.
 
-    Returns (packed uint8 [rows, cols/2], scales fp16 [rows, cols/128])."""
+    Returns (packed uint8 [rows, cols/2], scales fp16 [rows, cols/group_size])."""
     rows, cols = w.shape
     q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=w.device)
-    s = torch.empty((rows, cols // 128), dtype=torch.float16, device=w.device)
-    N.moe_w4_quantize(w, rows, cols, q, s, stream)
+    s = torch.empty((rows, cols // group_size), dtype=torch.float16, device=w.device)
+    N.moe_w4_quantize(w, rows, cols, group_size, q, s, stream)
     return q, s
 
 
 def dequantize(q: torch.Tensor, s: torch.Tensor, stream=None):
-    """Exact fp32 dequantization of one packed matrix (the test hook)."""
+    """Exact fp32 dequantization of one packed matrix (the test hook); the
+    group size is read off the shapes."""
     rows, half = q.shape
     out = torch.empty((rows, half * 2), dtype=torch.float32, device=q.device)
-    N.moe_w4_dequant(q, s, rows, half * 2, out, stream)
+    N.moe_w4_dequant(q, s, rows, half * 2, (half * 2) // s.shape[1], out, stream)
     return out

@@ -50,20 +50,17 @@ class MoEConfig:
     shared_std: float = 0.02
     x_std: float = 1.0
     rms_eps: float = 1e-6        # used between stacked layers only
+    group_size: int = 128        # int4 quantization group along in_features (64 / 128 / 256)
 
     @property
     def has_bias(self) -> bool:
         return self.zipf_alpha != 0.0 or self.dead_experts > 0
 
-    @property
-    def group_size(self) -> int:
-        return 128
-
     def expert_packed_bytes(self) -> int:
         return 3 * self.hidden * self.ffn // 2
 
     def expert_scale_bytes(self) -> int:
-        return 3 * self.hidden * self.ffn // 128 * 2
+        return 3 * self.hidden * self.ffn // self.group_size * 2
 
     def expert_bytes(self) -> int:
         return self.expert_packed_bytes() + self.expert_scale_bytes()

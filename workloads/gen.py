@@ -102,6 +102,6 @@ def expert_codes(cfg: MoEConfig, layer: int, expert: int, matrix: int):
     out_dim, in_dim = matrix_shape(cfg, matrix)
     g = rng(cfg, T_CODES, layer=layer, expert=expert, matrix=matrix)
     packed = g.integers(0, 256, size=(out_dim, in_dim // 2), dtype=np.uint8)
-    s = (cfg.weight_std * g.uniform(0.15, 0.30, size=(out_dim, in_dim // 128))
+    s = (cfg.weight_std * g.uniform(0.15, 0.30, size=(out_dim, in_dim // cfg.group_size))
          ).astype(np.float16)
     return packed, s

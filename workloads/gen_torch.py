@@ -17,7 +17,7 @@ from . import gen as G
 def layer_codes(cfg: MoEConfig, layer: int, device, weight_set: int = 0):
     """dict gate_q/gate_s/up_q/up_s/down_q/down_s for all experts of a layer:
     codes uint8 [E, out, in/2] (every byte value equally likely) and scales fp16
-    [E, out, in/128] = weight_std * U(0.15, 0.30)."""
+    [E, out, in/group_size] = weight_std * U(0.15, 0.30)."""
     out = {}
     for m, name in ((G.GATE, "gate"), (G.UP, "up"), (G.DOWN, "down")):
         out_dim, in_dim = G.matrix_shape(cfg, m)
@@ -28,7 +28,8 @@ def layer_codes(cfg: MoEConfig, layer: int, device, weight_set: int = 0):
         for e in range(E):     # one expert at a time keeps int64 temporaries small
             q[e] = torch.randint(0, 256, (out_dim, in_dim // 2), generator=g, device=device,
                                  dtype=torch.uint8)
-        s = (cfg.weight_std * (0.15 + 0.15 * torch.rand((E, out_dim, in_dim // 128), generator=g,
+        s = (cfg.weight_std * (0.15 + 0.15 * torch.rand((E, out_dim, in_dim // cfg.group_size),
+                                                          generator=g,
                                                           device=device))).to(torch.float16)
         out[name + "_q"], out[name + "_s"] = q, s
     return out
