@@ -181,11 +181,16 @@ moe_status moe_w4_grouped_ffn(const moe_layer *layer, const uint16_t *x,
                               void *ws, size_t ws_bytes, void *stream);
 
 #define MOE_RMSNORM 1u
+#define MOE_RENORM 2u
 
 /* Combine: out[t] = y_shared[t] + sum_j topk_w[t][j] * y_perm[inv_pos[t*k+j]]
  * in fp32 (y_shared may be NULL: then that term is 0).  With flags &
- * MOE_RMSNORM the row is then divided by sqrt(mean(row^2) + eps) (no gain, no
- * residual), as between stacked layers.  Stored as fp16.
+ * MOE_RENORM each topk_w[t][j] is first divided by the sum of the token's k
+ * weights (the chosen experts' probabilities rescaled to sum to 1; an option
+ * beyond the pages, whose routing keeps the plain softmax probabilities).
+ * With flags & MOE_RMSNORM the row is then divided by
+ * sqrt(mean(row^2) + eps) (no gain, no residual), as between stacked layers.
+ * Stored as fp16.
  *   out  fp16 [T, H] out.  inv_pos entries must lie in [0, T*k) (clamped on
  *        the device otherwise). */
 moe_status moe_unpermute_combine(const moe_layer *layer, const uint16_t *y_perm,

@@ -268,17 +268,21 @@ def expert_ffn_w4(X, gate_q, gate_s, up_q, up_s, down_q, down_s,
 # a8: weighted combine + shared expert, and the RMS normalisation that links
 #   stacked layers
 # ---------------------------------------------------------------------------
-def combine(y_perm, ys, inv_pos, topk_w, T: int, k: int) -> np.ndarray:
+def combine(y_perm, ys, inv_pos, topk_w, T: int, k: int, renorm: bool = False) -> np.ndarray:
     """out[t] = ys[t] + sum_j w[t, j] * y_perm[inv_pos[t*k + j]]  (float64).
 
     The shared expert enters with weight 1 and no gate ([P5] §01 "8 routed +
-    1 shared"; reading: the shared expert is always on, unweighted).
+    1 shared"; reading: the shared expert is always on, unweighted).  With
+    renorm, w[t, j] is replaced by w[t, j] / sum_j' w[t, j'] (an option beyond
+    the pages, whose routing keeps the plain softmax probabilities).
     """
     y_perm = np.asarray(y_perm, dtype=np.float64)
     H = y_perm.shape[1] if y_perm.ndim == 2 and y_perm.shape[0] else (
         np.asarray(ys).shape[1] if ys is not None else 0)
     out = np.zeros((T, H)) if ys is None else np.asarray(ys, dtype=np.float64).copy()
     w = np.asarray(topk_w, dtype=np.float64).reshape(T, k)
+    if renorm:
+        w = w / w.sum(axis=1, keepdims=True)
     inv = np.asarray(inv_pos, dtype=np.int64).reshape(T, k)
     for j in range(k):
         out += w[:, j:j + 1] * y_perm[inv[:, j]]

@@ -108,7 +108,7 @@ def test_other_calls_argument_errors():
     assert rp(ctypes.byref(L), FAKE, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 64,
               None) == EWS
     assert rp(ctypes.byref(L), None, 0, None, None, None, None, None, None, None, 0, None) == OK
-    assert N.lib.moe_unpermute_combine(ctypes.byref(L), FAKE, None, FAKE, FAKE, 4, 2, 1e-6, FAKE,
+    assert N.lib.moe_unpermute_combine(ctypes.byref(L), FAKE, None, FAKE, FAKE, 4, 4, 1e-6, FAKE,
                                        None) == EINVAL                      # unknown flag
     assert N.lib.moe_unpermute_combine(ctypes.byref(L), FAKE, None, FAKE, FAKE, 4, 1, -1.0,
                                        FAKE, None) == EINVAL                # negative eps
@@ -144,7 +144,7 @@ def test_layer_forward_argument_errors():
     assert call(a6=None) == EINVAL                      # no perm_src
     assert call(a8=MISALIGNED) == EINVAL                # x_perm misaligned
     assert call(a9=None) == EINVAL                      # no y_perm
-    assert call(a11=2) == EINVAL                        # unknown flag
+    assert call(a11=4) == EINVAL                        # unknown flag
     assert call(a11=1, a12=-1.0) == EINVAL              # negative eps
     assert call(a13=None) == EINVAL                     # no out
     assert call(a15=64) == EWS

@@ -229,3 +229,25 @@ def test_small_top_k_and_single_expert(E, k):
     cfg = get_config("decode_fine", num_experts=E, hidden=512, ffn=256, top_k=k,
                      shared_ffn=128)
     run_layer_case(cfg, 11, batch=E + k)
+
+
+@pytest.mark.parametrize("T", [8, 150])
+def test_layer_with_renormalised_weights(T):
+    """moe_layer_forward with MOE_RENORM against the oracle layer whose
+    combine divides each token's k weights by their sum."""
+    cfg = get_config("decode_fine", num_experts=32, hidden=512, ffn=256, top_k=4,
+                     shared_ffn=128)
+    mats, experts = quantized_experts(cfg)
+    wr, b = G.router(cfg)
+    shared = G.shared_expert(cfg)
+    x = G.activations(cfg, tokens=T, batch=3)
+    ref = O.moe_layer(x, wr, b, experts, cfg.top_k, shared=shared)
+    out_ref = O.combine(ref["y_perm"], ref["ys"], ref["inv_pos"], ref["w"], T, cfg.top_k,
+                        renorm=True)
+    layer = make_gpu_layer(cfg, mats, wr, b, shared)
+    buf = layer.alloc(T)
+    out = _np(layer.forward(to_dev(x), buf, renorm=True))
+    torch.cuda.synchronize()
+    diff = route_compare(_np(buf.topk_idx), ref["idx"], ref["logits"], cfg.top_k)
+    ok = ~diff
+    tol_check(out[ok], out_ref[ok], "renormalised out")

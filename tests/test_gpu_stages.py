@@ -288,18 +288,19 @@ def test_ffn_teacher_forced(name, over, T, Fs, skew, use_x_perm):
 
 
 # ---------------------------------------------------------------- combine
+@pytest.mark.parametrize("renorm", [False, True])
 @pytest.mark.parametrize("rms", [False, True])
 @pytest.mark.parametrize("T,k,H,with_shared", [(16, 2, 256, False), (9, 8, 4096, True),
                                                (3, 32, 384, True), (5, 8, 6144, True),
                                                (4, 3, 12416, False), (2, 4, 20480, True)])
-def test_combine(T, k, H, with_shared, rms):
+def test_combine(T, k, H, with_shared, rms, renorm):
     g = np.random.default_rng(T + k)
     N = T * k
     y_perm = (g.standard_normal((N, H)) * 0.3).astype(np.float16)
     ys = (g.standard_normal((T, H)) * 0.3).astype(np.float16) if with_shared else None
     inv = g.permutation(N).astype(np.int32)
     w = g.uniform(0, 0.3, size=(T, k)).astype(np.float32)
-    ref = O.combine(y_perm, ys, inv, w, T, k)
+    ref = O.combine(y_perm, ys, inv, w, T, k, renorm=renorm)
     if rms:
         ref = O.rmsnorm(ref, 1e-6)
     E = max(k, 8)
@@ -314,6 +315,6 @@ def test_combine(T, k, H, with_shared, rms):
         buf.y_shared.copy_(to_dev(ys))
     buf.inv_pos.copy_(to_dev(inv))
     buf.topk_w.copy_(to_dev(w))
-    layer.combine(buf, T, rmsnorm=rms)
+    layer.combine(buf, T, rmsnorm=rms, renorm=renorm)
     torch.cuda.synchronize()
     tol_check(_np(buf.out), ref, "combine")

@@ -329,6 +329,32 @@ def test_layer_special_cases():
     np.testing.assert_allclose(res["out"], ref, rtol=0, atol=1e-12 * np.abs(ref).max())
 
 
+def test_combine_renormalised_weights():
+    """With renorm the k weights act as a convex combination: identical
+    expert rows come back unchanged, and scaling every weight of a token by a
+    constant changes nothing; against loops that divide by the sum."""
+    g = np.random.default_rng(19)
+    T, k, H = 5, 3, 4
+    ys = g.standard_normal((T, H))
+    inv = g.permutation(T * k).astype(np.int32)
+    w = g.uniform(0.01, 0.3, size=(T, k))
+    v = g.standard_normal(H)
+    same = np.tile(v, (T * k, 1))
+    out = O.combine(same, ys, inv, w, T, k, renorm=True)
+    np.testing.assert_allclose(out, ys + v[None, :], rtol=0, atol=1e-14)
+    y_perm = g.standard_normal((T * k, H))
+    a = O.combine(y_perm, ys, inv, w, T, k, renorm=True)
+    b = O.combine(y_perm, ys, inv, w * 7.5, T, k, renorm=True)
+    np.testing.assert_allclose(a, b, rtol=1e-14, atol=0)
+    for t in range(T):
+        tot = sum(w[t, j] for j in range(k))
+        for h in range(H):
+            ref = ys[t, h] + sum(w[t, j] / tot * y_perm[inv[t * k + j], h] for j in range(k))
+            assert abs(a[t, h] - ref) < 1e-14
+    # without renorm the same weights are used as they are
+    assert not np.allclose(O.combine(y_perm, ys, inv, w, T, k), a)
+
+
 def test_combine_bruteforce():
     g = np.random.default_rng(9)
     T, k, H = 4, 2, 5

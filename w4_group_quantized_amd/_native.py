@@ -27,6 +27,7 @@ import torch  # noqa: E402,F401
 lib = ctypes.CDLL(LIB_PATH)
 
 MOE_RMSNORM = 1
+MOE_RENORM = 2
 
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_route_permute",
            "moe_w4_grouped_ffn", "moe_unpermute_combine", "moe_layer_forward",

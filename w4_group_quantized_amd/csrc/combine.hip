@@ -3,8 +3,9 @@
 // out[t] = y_shared[t] + sum_j w[t][j] * y_perm[inv_pos[t*k + j]] in fp32, in
 // that fixed order; the shared expert is always on with weight 1
 // (haowenji.com/articles/x-2109226022155796480 §01: 8 routed + 1 shared
-// experts per token).  With MOE_RMSNORM the row is divided by
-// sqrt(mean(row^2) + eps), as between stacked decode layers.
+// experts per token).  With MOE_RENORM each w[t][j] is first divided by
+// w[t][0] + ... + w[t][k-1] (summed in that order).  With MOE_RMSNORM the row
+// is divided by sqrt(mean(row^2) + eps), as between stacked decode layers.
 #include "common.h"
 #include "kernels.h"
 
@@ -12,12 +13,24 @@ namespace moe {
 
 constexpr int kMaxK = 32;
 
+// w[j] / (w[0] + ... + w[k-1]) for the k weights in LDS, the sum in that
+// order (every thread forms the same sum; the block then meets again so that
+// no weight is overwritten while another thread still reads it).
+__device__ __forceinline__ void renorm_weights(float *s_w, int k) {
+  float sum = 0.0f;
+  for (int j = 0; j < k; ++j) sum += s_w[j];
+  const float wj = threadIdx.x < (unsigned)k ? s_w[threadIdx.x] / sum : 0.0f;
+  __syncthreads();
+  if (threadIdx.x < (unsigned)k) s_w[threadIdx.x] = wj;
+  __syncthreads();
+}
+
 // One block per token; each thread owns 8-column chunks of the row.
 __global__ __launch_bounds__(256) void combine_kernel(const f16 *__restrict__ y_perm,
                                                       const f16 *__restrict__ ys,
                                                       const int32_t *__restrict__ inv_pos,
                                                       const float *__restrict__ w, int k, int H,
-                                                      int N, int rmsnorm, float eps,
+                                                      int N, int rmsnorm, int renorm, float eps,
                                                       f16 *__restrict__ out) {
   __shared__ int s_row[kMaxK];
   __shared__ float s_w[kMaxK];
@@ -29,6 +42,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const f16 *__restrict__ y_
     s_w[threadIdx.x] = w[(size_t)t * k + threadIdx.x];
   }
   __syncthreads();
+  if (renorm) renorm_weights(s_w, k);
 
   auto row_chunk = [&](int c, float (&v)[8]) {
     if (ys) {
@@ -78,11 +92,17 @@ __global__ __launch_bounds__(64) void combine_cols_kernel(const f16 *__restrict_
                                                           const f16 *__restrict__ ys,
                                                           const int32_t *__restrict__ inv_pos,
                                                           const float *__restrict__ w, int k,
-                                                          int H, int N, f16 *__restrict__ out) {
+                                                          int H, int N, int renorm,
+                                                          f16 *__restrict__ out) {
   const int chunks = (H + 511) / 512;
   const int t = blockIdx.x / chunks;
   const int c = (blockIdx.x % chunks) * 512 + threadIdx.x * 8;
   if (c >= H) return;
+  float wsum = 1.0f;
+  if (renorm) {
+    wsum = 0.0f;
+    for (int j = 0; j < k; ++j) wsum += w[(size_t)t * k + j];
+  }
   float v[8];
   if (ys) {
     const f16x8 a = as_f16x8(ld16(ys + (size_t)t * H + c));
@@ -95,7 +115,7 @@ __global__ __launch_bounds__(64) void combine_cols_kernel(const f16 *__restrict_
   for (int j = 0; j < k; ++j) {
     int r = inv_pos[(size_t)t * k + j];
     r = r < 0 ? 0 : (r >= N ? N - 1 : r);
-    const float wj = w[(size_t)t * k + j];
+    const float wj = renorm ? w[(size_t)t * k + j] / wsum : w[(size_t)t * k + j];
     const f16x8 y = as_f16x8(ld16(y_perm + (size_t)r * H + c));
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = fmaf(wj, (float)y[i], v[i]);
@@ -112,7 +132,7 @@ __global__ __launch_bounds__(1024) void combine_norm_kernel(const f16 *__restric
                                                             const f16 *__restrict__ ys,
                                                             const int32_t *__restrict__ inv_pos,
                                                             const float *__restrict__ w, int k,
-                                                            int H, int N, float eps,
+                                                            int H, int N, int renorm, float eps,
                                                             f16 *__restrict__ out) {
   __shared__ int s_row[kMaxK];
   __shared__ float s_w[kMaxK];
@@ -136,6 +156,7 @@ __global__ __launch_bounds__(1024) void combine_norm_kernel(const f16 *__restric
     for (int i = 0; i < 8; ++i) v[i] = 0.0f;
   }
   __syncthreads();
+  if (renorm) renorm_weights(s_w, k);
   if (live) {
     for (int j = 0; j < k; ++j) {
       const f16x8 y = as_f16x8(ld16(y_perm + (size_t)s_row[j] * H + c));
@@ -166,24 +187,25 @@ hipError_t launch_combine(const moe_layer &L, const uint16_t *y_perm, const uint
                           const int32_t *inv_pos, const float *w, int32_t T, uint32_t flags,
                           float eps, uint16_t *out, hipStream_t st) {
   const int k = L.top_k, H = L.hidden;
+  const int renorm = (flags & MOE_RENORM) ? 1 : 0;
   if (!(flags & MOE_RMSNORM)) {
     hipLaunchKernelGGL(combine_cols_kernel, dim3(T * ((H + 511) / 512)), dim3(64), 0, st,
                        reinterpret_cast<const f16 *>(y_perm),
                        reinterpret_cast<const f16 *>(y_shared), inv_pos, w, k, H, T * k,
-                       reinterpret_cast<f16 *>(out));
+                       renorm, reinterpret_cast<f16 *>(out));
     return hipGetLastError();
   }
   if (H <= 8192) {
     const int threads = ((H / 8 + kWave - 1) / kWave) * kWave;
     hipLaunchKernelGGL(combine_norm_kernel, dim3(T), dim3(threads), 0, st,
                        reinterpret_cast<const f16 *>(y_perm),
-                       reinterpret_cast<const f16 *>(y_shared), inv_pos, w, k, H, T * k, eps,
-                       reinterpret_cast<f16 *>(out));
+                       reinterpret_cast<const f16 *>(y_shared), inv_pos, w, k, H, T * k, renorm,
+                       eps, reinterpret_cast<f16 *>(out));
     return hipGetLastError();
   }
   hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(256), 0, st,
                      reinterpret_cast<const f16 *>(y_perm), reinterpret_cast<const f16 *>(y_shared),
-                     inv_pos, w, k, H, T * k, (flags & MOE_RMSNORM) ? 1 : 0, eps,
+                     inv_pos, w, k, H, T * k, (flags & MOE_RMSNORM) ? 1 : 0, renorm, eps,
                      reinterpret_cast<f16 *>(out));
   return hipGetLastError();
 }

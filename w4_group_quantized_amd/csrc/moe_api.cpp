@@ -117,7 +117,7 @@ static moe_status check_combine_args(const uint16_t *y_perm, const uint16_t *y_s
                                      uint32_t flags, float eps, const uint16_t *out) {
   if (!ok_ptr(y_perm) || !ok_ptr(inv_pos) || !ok_ptr(topk_w) || !ok_ptr(out)) return MOE_EINVAL;
   if (y_shared && !aligned16(y_shared)) return MOE_EINVAL;
-  if (flags & ~MOE_RMSNORM) return MOE_EINVAL;
+  if (flags & ~(MOE_RMSNORM | MOE_RENORM)) return MOE_EINVAL;
   if ((flags & MOE_RMSNORM) && !(eps >= 0.0f)) return MOE_EINVAL;
   return MOE_OK;
 }

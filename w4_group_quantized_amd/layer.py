@@ -100,32 +100,34 @@ class W4MoELayer:
                              buf.offsets, T, buf.y_perm, buf.y_shared if self.Fs else None,
                              buf.ws, buf.ws.numel(), stream)
 
-    def combine(self, buf, T, rmsnorm=False, eps=1e-6, out=None, stream=None):
+    def combine(self, buf, T, rmsnorm=False, eps=1e-6, out=None, renorm=False, stream=None):
+        flags = (N.MOE_RMSNORM if rmsnorm else 0) | (N.MOE_RENORM if renorm else 0)
         N.moe_unpermute_combine(self.desc, buf.y_perm, buf.y_shared if self.Fs else None,
-                                buf.inv_pos, buf.topk_w, T, N.MOE_RMSNORM if rmsnorm else 0,
-                                eps, buf.out if out is None else out, stream)
+                                buf.inv_pos, buf.topk_w, T, flags, eps,
+                                buf.out if out is None else out, stream)
 
     def forward(self, x, buf, T=None, rmsnorm=False, eps=1e-6, out=None, gather=False,
-                stream=None):
+                renorm=False, stream=None):
         """x fp16 [T, H] on the device -> buf.out (or `out`) fp16 [T, H].
 
         One C call (moe_layer_forward): route + permute (one launch for small
         batches), the grouped FFN reading token rows through perm_src (or from
         buf.x_perm, written by the permutation, with gather=True), and the
-        combine."""
+        combine (with renorm=True the k combine weights of a token are rescaled
+        to sum to 1)."""
         T = x.shape[0] if T is None else T
         if T > buf.max_tokens:
             raise ValueError("more tokens than the buffers were allocated for")
         o = buf.out if out is None else out
+        flags = (N.MOE_RMSNORM if rmsnorm else 0) | (N.MOE_RENORM if renorm else 0)
         N.moe_layer_forward(self.desc, x, T, buf.topk_idx, buf.topk_w, buf.offsets, buf.perm_src,
                             buf.inv_pos, buf.x_perm if gather else None, buf.y_perm,
-                            buf.y_shared if self.Fs else None,
-                            N.MOE_RMSNORM if rmsnorm else 0, eps, o, buf.ws, buf.ws.numel(),
-                            stream)
+                            buf.y_shared if self.Fs else None, flags, eps, o, buf.ws,
+                            buf.ws.numel(), stream)
         return buf.out[:T] if out is None else out
 
     def forward_staged(self, x, buf, T=None, rmsnorm=False, eps=1e-6, out=None, gather=False,
-                       stream=None):
+                       renorm=False, stream=None):
         """The same layer as three C calls: moe_route_permute,
         moe_w4_grouped_ffn, moe_unpermute_combine."""
         T = x.shape[0] if T is None else T
@@ -133,7 +135,7 @@ class W4MoELayer:
             raise ValueError("more tokens than the buffers were allocated for")
         self.route_permute(x, buf, T, gather=gather, stream=stream)
         self.ffn(x, buf, T, use_x_perm=gather, stream=stream)
-        self.combine(buf, T, rmsnorm, eps, out, stream)
+        self.combine(buf, T, rmsnorm, eps, out, renorm, stream)
         return buf.out[:T] if out is None else out
 
 
