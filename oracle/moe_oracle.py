@@ -67,7 +67,7 @@ def rn16(a) -> np.ndarray:
 # a0: symmetric group quantization  ([P2] §2.1 group-quantization pseudo-code;
 #     applied offline to every module whose name contains "expert", [P2] §3.2)
 # ---------------------------------------------------------------------------
-def group_quantize(w16: np.ndarray, group: int = GROUP):
+def group_quantize(w16: np.ndarray, group: int = GROUP, bits: int = 4):
     """Quantize an fp16 weight [out, in] to int4 codes and fp16 group scales.
 
     [P2] §2.1: the weight is viewed as [out, in/group, group]; each group's
@@ -76,6 +76,10 @@ def group_quantize(w16: np.ndarray, group: int = GROUP):
     in fp16 ([P2] §3.2), so every operation rounds to fp16:
 
         s = RN16(max|w| / 7),   q = clamp(RNE(RN16(w / s)), -8, 7).
+
+    bits = 8 gives the 8-bit weights [P1] §3.1 keeps for the shared FFN (with
+    128-weight groups): the same steps with 2**(bits-1)-1 = 127 and the
+    clamp range [-128, 127] (reading: the pages print only the 4-bit case).
 
     Each quotient is formed in float64 and then rounded once to fp16; since
     53 >= 2*11 + 2 this equals the correctly rounded fp16 quotient.  A group
@@ -91,12 +95,15 @@ def group_quantize(w16: np.ndarray, group: int = GROUP):
     out_dim, in_dim = w16.shape
     if in_dim % group:
         raise ValueError("in_features must be a multiple of the group size")
+    if bits not in (4, 8):
+        raise ValueError("bits must be 4 or 8")
+    qmax, qmin = 2 ** (bits - 1) - 1, -2 ** (bits - 1)
     w = w16.astype(np.float64).reshape(out_dim, in_dim // group, group)
     m = np.abs(w).max(axis=-1, keepdims=True)
-    s = rn16(m / QMAX)
+    s = rn16(m / qmax)
     with np.errstate(divide="ignore", invalid="ignore"):
         r = rn16(np.where(s > 0, w / np.where(s > 0, s, 1.0), 0.0))
-    q = np.clip(np.rint(r), QMIN, QHI)          # np.rint rounds half to even
+    q = np.clip(np.rint(r), qmin, qmax)          # np.rint rounds half to even
     q = np.where(s > 0, q, 0.0)
     return (q.astype(np.int8).reshape(out_dim, in_dim),
             s.reshape(out_dim, in_dim // group).astype(np.float16))
@@ -143,6 +150,30 @@ def unpack_w4(packed: np.ndarray) -> np.ndarray:
         u[:, :, _LO_COL[b]] = (p[:, :, b] & 0x0F).astype(np.int8)
         u[:, :, _HI_COL[b]] = (p[:, :, b] >> 4).astype(np.int8)
     return (u - 8).reshape(p.shape[0], -1)
+
+
+def pack_w8(q: np.ndarray) -> np.ndarray:
+    """int8 codes [out, in] -> stored bytes [out, in]: the offset-binary byte
+    q + 128, rows in tiles of 16 with each 16-column chunk of the 16 rows side
+    by side, byte(n, c) = (n // 16) * 16 * in + (c // 16) * 256 + (n % 16) * 16
+    + c % 16 (a format of this library for the 8-bit shared expert)."""
+    q = np.asarray(q)
+    if q.shape[0] % 16 or q.shape[1] % GROUP:
+        raise ValueError("out_features must be a multiple of 16, in_features of 128")
+    u = (q.astype(np.int16) + 128).astype(np.uint8)
+    return _rows_to_tiles(u, 16)
+
+
+def unpack_w8(packed: np.ndarray) -> np.ndarray:
+    """Stored bytes [out, in] -> int8 codes [out, in]."""
+    u = _tiles_to_rows(np.asarray(packed, dtype=np.uint8), 16)
+    return (u.astype(np.int16) - 128).astype(np.int8)
+
+
+def dequant_w8(packed: np.ndarray, s_stored: np.ndarray, group: int = GROUP) -> np.ndarray:
+    """W[n, c] = q[n, c] * s[n, c // group] in float64 for a stored 8-bit matrix."""
+    q = unpack_w8(packed).astype(np.float64)
+    return q * np.repeat(unpack_scales(s_stored).astype(np.float64), group, axis=1)
 
 
 def pack_scales(s: np.ndarray) -> np.ndarray:

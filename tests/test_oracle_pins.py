@@ -156,6 +156,67 @@ def test_dequant_exact(group):
     np.testing.assert_array_equal(W.astype(np.float32).astype(np.float64), W)
 
 
+# ---------------------------------------------------------------- 8-bit shared expert
+def test_w8_quantizer_exact_rational_bruteforce():
+    """8-bit codes: s = RN16(max|w| / 127), q = clamp(RNE(RN16(w / s)), -128,
+    127), recomputed with exact rationals and brute-force fp16 rounding."""
+    g = np.random.default_rng(21)
+    w = (g.standard_normal((2, 256)) * 0.02).astype(np.float16)
+    q, s = O.group_quantize(w, 128, bits=8)
+    for n in range(2):
+        for grp in range(2):
+            ws = [Fraction(float(v)) for v in w[n, grp * 128:(grp + 1) * 128]]
+            s_ref = nearest_f16(max(abs(v) for v in ws) / 127)
+            assert Fraction(float(s[n, grp])) == s_ref
+            for c, v in enumerate(ws):
+                q_ref = max(-128, min(127, round(nearest_f16(v / s_ref))))
+                assert int(q[n, grp * 128 + c]) == q_ref
+
+
+def test_w8_quantizer_invariants():
+    cfg = get_config("tiny")
+    w = G.expert_master(cfg, 0, 5, G.UP).astype(np.float16)          # [512, 256]
+    w[7, :128] = 0
+    q, s = O.group_quantize(w, 128, bits=8)
+    assert q.min() >= -127 and q.max() <= 127                        # -128 never produced
+    qa = np.abs(q.astype(np.int32)).reshape(q.shape[0], -1, 128).max(-1)
+    nz = s.astype(np.float64) > 0
+    assert (qa[nz] == 127).all() and (qa[~nz] == 0).all() and not nz[7, 0]
+    err = np.abs(w.astype(np.float64) - O.dequant_w8(O.pack_w8(q), O.pack_scales(s)))
+    # |w/s - RN16(w/s)| <= 2^-5 below 128, plus the final rounding to an integer
+    bound = (0.5 + 2.0 ** -5) * np.repeat(s.astype(np.float64), 128, axis=1)
+    assert (err <= bound).all()
+
+
+def test_w8_pack_layout_every_byte():
+    """Every byte value at random storage offsets of a [32, 256] matrix,
+    against byte(n, c) = (n//16)*16*256 + (c//16)*256 + (n%16)*16 + c%16 and
+    value = byte - 128."""
+    rows, cols = 32, 256
+    rng = np.random.default_rng(22)
+    for v in range(256):
+        n, c = int(rng.integers(rows)), int(rng.integers(cols))
+        flat = np.full(rows * cols, 128, dtype=np.uint8)
+        flat[(n // 16) * 16 * cols + (c // 16) * 256 + (n % 16) * 16 + c % 16] = v
+        q = O.unpack_w8(flat.reshape(rows, cols))
+        expect = np.zeros((rows, cols), dtype=np.int8)
+        expect[n, c] = v - 128
+        np.testing.assert_array_equal(q, expect)
+        np.testing.assert_array_equal(O.pack_w8(q).reshape(-1), flat)
+
+
+def test_w8_dequant_exact():
+    g = np.random.default_rng(23)
+    q = g.integers(-128, 128, size=(16, 256)).astype(np.int8)
+    s = g.uniform(1e-4, 1e-3, size=(16, 2)).astype(np.float16)
+    W = O.dequant_w8(O.pack_w8(q), O.pack_scales(s))
+    for n in range(16):
+        for c in range(0, 256, 5):
+            assert Fraction(W[n, c]) == int(q[n, c]) * Fraction(float(s[n, c // 128]))
+    # q*s needs at most 8 + 11 bits: exact in fp32
+    np.testing.assert_array_equal(W.astype(np.float32).astype(np.float64), W)
+
+
 # ---------------------------------------------------------------- router
 def test_softmax_closed_form():
     E = 6
