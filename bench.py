@@ -56,6 +56,8 @@ def parse():
                              "decode_fine512", "tiny"])
     ap.add_argument("--group-size", type=int, default=128, choices=[64, 128, 256],
                     help="int4 quantization group size of the experts")
+    ap.add_argument("--shared-bits", type=int, default=16, choices=[16, 8],
+                    help="shared expert weights: fp16, or 8-bit g128")
     ap.add_argument("--weight-sets", type=int, default=0, help="0 = workload default")
     ap.add_argument("--batches", type=int, default=4, help="distinct token batches rotated")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -128,24 +130,25 @@ def traffic_from_csv(fetch_csv, write_csv, copy_mib):
     return res
 
 
-def traffic_path(workload, group_size):
-    tag = "" if group_size == 128 else f"_g{group_size}"
+def traffic_path(workload, group_size, shared_bits=16):
+    tag = ("" if group_size == 128 else f"_g{group_size}") + ("" if shared_bits == 16 else "_s8")
     return os.path.join(ROOT, "profiles", f"traffic_{workload}{tag}.json")
 
 
-def summarize_traffic(workload, group_size, fetch_csv, write_csv, copy_mib):
+def summarize_traffic(workload, group_size, shared_bits, fetch_csv, write_csv, copy_mib):
     """Write the traffic summary of a workload for the current FFN sources."""
-    res = {"workload": workload, "group_size": group_size, "source_sha256": ffn_source_hash()}
+    res = {"workload": workload, "group_size": group_size, "shared_bits": shared_bits,
+           "source_sha256": ffn_source_hash()}
     res.update(traffic_from_csv(fetch_csv, write_csv, copy_mib))
-    out = traffic_path(workload, group_size)
+    out = traffic_path(workload, group_size, shared_bits)
     with open(out, "w") as fh:
         json.dump(res, fh, indent=1)
     print(json.dumps(res))
 
 
-def measured_traffic(workload, group_size=128):
+def measured_traffic(workload, group_size=128, shared_bits=16):
     """HBM bytes per FFN call measured for the current kernel sources, else None."""
-    path = traffic_path(workload, group_size)
+    path = traffic_path(workload, group_size, shared_bits)
     try:
         with open(path) as fh:
             t = json.load(fh)
@@ -194,10 +197,19 @@ def build_layer(cfg, wset, layer_idx, dev):
             gpu_normal16(shp, cfg.shared_std,
                          G.torch_seed(cfg, G.T_SHARED, layer=layer_idx, matrix=m, batch=wset), dev)
             for m, shp in ((G.GATE, (Fs, H)), (G.UP, (Fs, H)), (G.DOWN, (H, Fs))))
+    shared_w8 = None
+    if shared is not None and cfg.shared_bits == 8:   # quantized by the HIP 8-bit quantizer
+        shared_w8 = []
+        for w in shared:
+            q = torch.empty(w.shape, dtype=torch.uint8, device=dev)
+            s = torch.empty((w.shape[0], w.shape[1] // 128), dtype=torch.float16, device=dev)
+            NAT.moe_w8_quantize(w, w.shape[0], w.shape[1], q, s)
+            shared_w8.append((q, s))
+        shared_w8, shared = tuple(shared_w8), None
     t = lambda a: torch.from_numpy(a).to(dev)  # noqa: E731
     return W4MoELayer(cfg.top_k, t(wr), t(b) if b is not None else None,
                       mats["gate"][0], mats["gate"][1], mats["up"][0], mats["up"][1],
-                      mats["down"][0], mats["down"][1], shared=shared)
+                      mats["down"][0], mats["down"][1], shared=shared, shared_w8=shared_w8)
 
 
 # ---------------------------------------------------------------- CPU baseline
@@ -220,6 +232,9 @@ def cpu_baseline(cfg, budget_s):
     wr, b = G.router(cfg, 0)
     x = G.activations(cfg, batch=0)
     shared = G.shared_expert(cfg, 0)
+    if shared is not None and cfg.shared_bits == 8:   # the 8-bit weights, dequantized
+        shared = tuple(O.dequant_w8(O.pack_w8(q), O.pack_scales(s)) for q, s in
+                       (O.group_quantize(w, 128, bits=8) for w in shared))
     idx, _, _ = O.route(x, wr, b, cfg.top_k)
     cache = {}
 
@@ -267,8 +282,9 @@ def cpu_baseline(cfg, budget_s):
 def main():
     args = parse()
     if args.summarize_traffic:
-        summarize_traffic(args.workload, args.group_size, args.summarize_traffic[0],
-                          args.summarize_traffic[1], args.copy_calibration_mib)
+        summarize_traffic(args.workload, args.group_size, args.shared_bits,
+                          args.summarize_traffic[0], args.summarize_traffic[1],
+                          args.copy_calibration_mib)
         return
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -277,7 +293,7 @@ def main():
     import torch
     import w4_group_quantized_amd  # noqa: F401  (fails loudly without the HIP library)
 
-    cfg = get_config(args.workload, group_size=args.group_size)
+    cfg = get_config(args.workload, group_size=args.group_size, shared_bits=args.shared_bits)
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     layers_per_step = cfg.layers
@@ -372,7 +388,7 @@ def main():
     # (gate, up, down), the shared expert 6*H*Fs per token
     ffn_flops = T * (cfg.top_k * 6.0 * cfg.hidden * cfg.ffn + 6.0 * cfg.hidden * cfg.shared_ffn)
     achieved_tflops = float(ffn_flops / (ffn_ms_mean * 1e-3) / 1e12)
-    traffic = measured_traffic(cfg.name, cfg.group_size)
+    traffic = measured_traffic(cfg.name, cfg.group_size, cfg.shared_bits)
     if cfg.name == "prefill":
         roofline = {"bound": "mfma", "achieved": achieved_tflops, "peak": MFMA_F16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": achieved_tflops / MFMA_F16_PEAK_TFLOPS,
@@ -398,7 +414,8 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         layer_cfg = cfg if cfg.layers == 1 else get_config(cfg.name, layers=1,
-                                                           group_size=cfg.group_size)
+                                                           group_size=cfg.group_size,
+                                                           shared_bits=cfg.shared_bits)
         cpu = cpu_baseline(layer_cfg, args.cpu_budget_s)
         if cfg.layers > 1:       # one oracle layer of the 42: scale to a whole step
             cpu["value"] /= cfg.layers
@@ -421,8 +438,9 @@ def main():
             "workload": cfg.name, "experts": cfg.num_experts, "shared_ffn": cfg.shared_ffn,
             "hidden": cfg.hidden, "ffn": cfg.ffn, "top_k": cfg.top_k, "tokens": T,
             "layers_per_step": layers_per_step, "weight_sets": n_sets, "batches": args.batches,
-            "group_size": cfg.group_size,
-            "weights": f"int4 g{cfg.group_size} (fp16 scales), router fp16, shared expert fp16",
+            "group_size": cfg.group_size, "shared_bits": cfg.shared_bits,
+            "weights": (f"int4 g{cfg.group_size} (fp16 scales), router fp16, shared expert "
+                        + ("fp16" if cfg.shared_bits == 16 else "8-bit g128")),
             "distinct_experts_per_step_mean": float(np.mean(u_per_combo)),
         },
         "roofline": roofline,

@@ -91,7 +91,22 @@ typedef enum {
  *               gate_s, up_s their fp16 scales (E*F*H/gs)
  *  down_q       packed int4, E matrices [H, F] (E*H*F/2 bytes); down_s scales
  *  shared_ffn   Fs of the always-on shared expert, multiple of 128, or 0
- *  shared_gate, shared_up  fp16 [Fs, H];   shared_down   fp16 [H, Fs]
+ *  shared_bits  16 (or 0): the shared expert's weights are fp16,
+ *                 shared_gate, shared_up  fp16 [Fs, H];  shared_down  fp16 [H, Fs]
+ *               8: they are 8-bit with 128-weight groups, as
+ *                 xdnf.cn/news/329730 §3.1 keeps the shared FFN (the 8-bit
+ *                 format below), shared_gate_q / shared_up_q [Fs, H] and
+ *                 shared_down_q [H, Fs] codes with their fp16 scales
+ *                 shared_gate_s / shared_up_s [Fs, H/128], shared_down_s
+ *                 [H, Fs/128]; the fp16 pointers are then unused
+ *
+ * 8-bit format (shared expert): a matrix [out, in] (out a multiple of 16, in
+ * of 128) is out*in bytes of codes plus out*in/128 fp16 scales; the code q in
+ * [-128, 127] is the byte q + 128; rows in tiles of 16 with each 16-column
+ * chunk of the 16 rows side by side:
+ *     byte(row n, col c)    = (n/16)*16*in + (c/16)*256 + (n%16)*16 + c%16
+ *     scale(row n, group g) = (n/16)*16*(in/128) + g*16 + n%16
+ * W[n][c] = q[n][c] * scale[n][c / 128].
  */
 typedef struct moe_layer {
     int32_t num_experts;
@@ -111,6 +126,13 @@ typedef struct moe_layer {
     const uint16_t *shared_gate;
     const uint16_t *shared_up;
     const uint16_t *shared_down;
+    int32_t shared_bits;
+    const uint8_t *shared_gate_q;
+    const uint16_t *shared_gate_s;
+    const uint8_t *shared_up_q;
+    const uint16_t *shared_up_s;
+    const uint8_t *shared_down_q;
+    const uint16_t *shared_down_s;
 } moe_layer;
 
 /* Bytes of workspace that every call below needs for up to `max_tokens`
@@ -233,6 +255,15 @@ moe_status moe_w4_dequant(const uint8_t *q, const uint16_t *s, int64_t rows,
  * of 16, cols multiple of 128 and of group_size. */
 moe_status moe_w4_quantize(const uint16_t *w, int64_t rows, int64_t cols,
                            int32_t group_size, uint8_t *q, uint16_t *s, void *stream);
+
+/* 8-bit group quantization of an fp16 matrix w [rows, cols] for the shared
+ * expert (128-weight groups; xdnf.cn/news/329730 §3.1): the 4-bit steps of
+ * moe_w4_quantize with 127 in place of 7 and codes clamped to [-128, 127]:
+ * s = RN16(max|w_group| / 127), q = clamp(RNE(RN16(w / s)), -128, 127); an
+ * all-zero group gets s = 0, q = 0.  Writes q and s in the 8-bit format
+ * above.  rows multiple of 16, cols multiple of 128. */
+moe_status moe_w8_quantize(const uint16_t *w, int64_t rows, int64_t cols,
+                           uint8_t *q, uint16_t *s, void *stream);
 
 /* Static description of a status code (host). */
 const char *moe_status_str(moe_status status);

@@ -78,13 +78,28 @@ def coded_experts(cfg, layer=0):
     return {k: np.stack(v) for k, v in mats.items()}, per_expert
 
 
-def make_gpu_layer(cfg, mats, wr, b, shared):
+def shared_w8(shared):
+    """The fp16 shared expert quantized to 8 bits by the oracle: the stored
+    ((q, s), (q, s), (q, s)) numpy arrays for the device, and the float64
+    dequantized (Wg, Wu, Wd) the oracle's SwiGLU takes."""
+    stored, deq = [], []
+    for w in shared:
+        q, s = O.group_quantize(w, 128, bits=8)
+        p, ss = O.pack_w8(q), O.pack_scales(s)
+        stored.append((p, ss))
+        deq.append(O.dequant_w8(p, ss))
+    return tuple(stored), tuple(deq)
+
+
+def make_gpu_layer(cfg, mats, wr, b, shared, w8=None):
+    """w8: the stored arrays of an 8-bit shared expert (shared is then None)."""
     from w4_group_quantized_amd import W4MoELayer
     d = {k: to_dev(v) for k, v in mats.items()}
     sh = tuple(to_dev(w) for w in shared) if shared is not None else None
+    s8 = tuple((to_dev(q), to_dev(s)) for q, s in w8) if w8 is not None else None
     layer = W4MoELayer(cfg.top_k, to_dev(wr), to_dev(b) if b is not None else None,
                        d["gate_q"], d["gate_s"], d["up_q"], d["up_s"], d["down_q"], d["down_s"],
-                       shared=sh)
+                       shared=sh, shared_w8=s8)
     return layer
 
 

@@ -158,6 +158,33 @@ def test_layer_forward_argument_errors():
                 a13=None, a14=None, a15=0) == OK            # T = 0: no-op
 
 
+def test_8bit_shared_expert_arguments():
+    big = 1 << 30
+    ffn = N.lib.moe_w4_grouped_ffn
+    L8 = layer(shared_ffn=256)
+    L8.shared_bits = 8            # 8-bit shared expert declared, its arrays missing
+    assert ffn(ctypes.byref(L8), FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, big, None) == EINVAL
+    L8.shared_gate_q = L8.shared_up_q = L8.shared_down_q = FAKE
+    L8.shared_gate_s = L8.shared_up_s = L8.shared_down_s = FAKE
+    assert ffn(ctypes.byref(L8), FAKE, FAKE, FAKE, FAKE, 4, FAKE, None, FAKE, big,
+               None) == EINVAL                                              # no y_shared
+    Lb = layer()
+    Lb.shared_bits = 4
+    assert N.moe_workspace_size(Lb, 4) == 0                                 # unsupported
+    assert N.lib.moe_w8_quantize(FAKE, 16, 200, FAKE, FAKE, None) == EUNSUP
+    assert N.lib.moe_w8_quantize(FAKE, 8, 256, FAKE, FAKE, None) == EUNSUP
+    assert N.lib.moe_w8_quantize(FAKE, 16, 256, None, FAKE, None) == EINVAL
+    assert N.lib.moe_w8_quantize(None, 0, 256, None, None, None) == OK
+
+
+def test_layer_struct_matches_the_header():
+    """The binding's mirror of moe_layer has the header's fields in order."""
+    src = open(HEADER).read()
+    body = src[src.index("typedef struct moe_layer {"):src.index("} moe_layer;")]
+    names = re.findall(r"\b(\w+);", body)
+    assert names == [f[0] for f in N.MoeLayer._fields_], names
+
+
 def test_status_strings():
     for s in (OK, EINVAL, EUNSUP, EWS, -4):
         assert N.moe_status_str(s)

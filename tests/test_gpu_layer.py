@@ -251,3 +251,26 @@ def test_layer_with_renormalised_weights(T):
     diff = route_compare(_np(buf.topk_idx), ref["idx"], ref["logits"], cfg.top_k)
     ok = ~diff
     tol_check(out[ok], out_ref[ok], "renormalised out")
+
+
+@pytest.mark.parametrize("T", [8, 150])
+def test_layer_with_8bit_shared_expert(T):
+    """A whole layer whose shared expert is 8-bit g128 (one-launch router at
+    8 tokens, separate launches at 150), against the oracle layer whose
+    shared expert uses the same dequantized 8-bit weights."""
+    from gpu_util import shared_w8
+    cfg = get_config("decode_fine", num_experts=32, hidden=512, ffn=256, top_k=4,
+                     shared_ffn=256)
+    mats, experts = quantized_experts(cfg)
+    wr, b = G.router(cfg)
+    stored8, deq = shared_w8(G.shared_expert(cfg))
+    x = G.activations(cfg, tokens=T, batch=11)
+    ref = O.moe_layer(x, wr, b, experts, cfg.top_k, shared=deq)
+    layer = make_gpu_layer(cfg, mats, wr, b, None, w8=stored8)
+    buf = layer.alloc(T)
+    out = _np(layer.forward(to_dev(x), buf))
+    torch.cuda.synchronize()
+    tol_check(_np(buf.y_shared), ref["ys"], "8-bit shared expert")
+    diff = route_compare(_np(buf.topk_idx), ref["idx"], ref["logits"], cfg.top_k)
+    ok = ~diff
+    tol_check(out[ok], ref["out"][ok], "layer out")

@@ -10,7 +10,7 @@ from workloads import get_config
 from workloads import gen as G
 
 from gpu_util import (gpu, require_gpu, to_dev, tol_check, quantized_experts, make_gpu_layer,
-                      route_compare, dev)
+                      route_compare, dev, shared_w8)
 
 pytestmark = gpu
 
@@ -58,6 +58,22 @@ def test_quantize_golden_fixture():
     for c, v in fx["expected_codes_nonzero"].items():
         exp[0, int(c)] = v
     np.testing.assert_array_equal(codes, exp)
+
+
+@pytest.mark.parametrize("shape", [(16, 128), (64, 4096), (48, 1024)])
+def test_quantize_w8_bitexact(shape):
+    """8-bit shared-expert codes and scales against the oracle, byte for byte."""
+    from w4_group_quantized_amd import quantize_w8
+    g = np.random.default_rng(shape[1])
+    w = (g.standard_normal(shape, dtype=np.float32) * 0.02).astype(np.float16)
+    w[3 % shape[0], :128] = 0
+    w[5 % shape[0], -128:] = np.float16(3e-6)
+    w[6 % shape[0], :] = -w[6 % shape[0], :]
+    q_ref, s_ref = O.group_quantize(w, 128, bits=8)
+    q, s = quantize_w8(to_dev(w))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(_np(s).view(np.uint16), O.pack_scales(s_ref).view(np.uint16))
+    np.testing.assert_array_equal(_np(q), O.pack_w8(q_ref))
 
 
 @pytest.mark.parametrize("gs", [64, 128, 256])
@@ -254,11 +270,28 @@ FFN_CASES = [
 @pytest.mark.parametrize("use_x_perm", [False, True])
 @pytest.mark.parametrize("name,over,T,Fs,skew", FFN_CASES)
 def test_ffn_teacher_forced(name, over, T, Fs, skew, use_x_perm):
+    run_ffn_case(name, over, T, Fs, skew, use_x_perm)
+
+
+@pytest.mark.parametrize("over,T", [({"num_experts": 12, "hidden": 512, "ffn": 384, "top_k": 3}, 9),
+                                    ({"num_experts": 4, "hidden": 2048, "ffn": 512, "top_k": 2}, 40),
+                                    ({"num_experts": 2, "hidden": 256, "ffn": 256, "top_k": 2}, 70)])
+def test_ffn_shared_w8(over, T):
+    """The shared expert in 8 bits (g128) on the narrow and wide decode tile
+    shapes and in prefill mode (70 tokens over 2 experts), 3 token tiles at
+    most, K of 2 to 16 blocks split over 4 waves."""
+    run_ffn_case("tiny", over, T, 384, False, False, w8=True)
+
+
+def run_ffn_case(name, over, T, Fs, skew, use_x_perm, w8=False):
     cfg = get_config(name, shared_ffn=Fs, **over)
     mats, experts = quantized_experts(cfg)
     wr, b = G.router(cfg)
     x = G.activations(cfg, tokens=T, batch=5)
     shared = G.shared_expert(cfg) if Fs else None
+    stored8 = None
+    if w8:
+        stored8, shared = shared_w8(shared)     # oracle: the dequantized 8-bit weights
     if skew:                     # token t -> experts 0 and 1 + t % (E - 1)
         idx = np.stack([np.zeros(T, np.int32), 1 + np.arange(T, dtype=np.int32) %
                         (cfg.num_experts - 1)], axis=1)
@@ -266,7 +299,7 @@ def test_ffn_teacher_forced(name, over, T, Fs, skew, use_x_perm):
         idx, w, l = O.route(x, wr, b, cfg.top_k)
     off, perm_src, inv_pos = O.permute(idx, cfg.num_experts)
     x_perm = O.gather_rows(x, perm_src, cfg.top_k)
-    layer = make_gpu_layer(cfg, mats, wr, b, shared)
+    layer = make_gpu_layer(cfg, mats, wr, b, None if w8 else shared, w8=stored8)
     buf = layer.alloc(T)
     buf.offsets.copy_(to_dev(off))
     if use_x_perm:

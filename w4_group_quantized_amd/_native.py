@@ -31,7 +31,8 @@ MOE_RENORM = 2
 
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_route_permute",
            "moe_w4_grouped_ffn", "moe_unpermute_combine", "moe_layer_forward",
-           "moe_w4_dequant", "moe_w4_quantize", "moe_status_str", "moe_last_hip_error")
+           "moe_w4_dequant", "moe_w4_quantize", "moe_w8_quantize", "moe_status_str",
+           "moe_last_hip_error")
 
 
 class MoeLayer(ctypes.Structure):
@@ -54,6 +55,13 @@ class MoeLayer(ctypes.Structure):
         ("shared_gate", ctypes.c_void_p),
         ("shared_up", ctypes.c_void_p),
         ("shared_down", ctypes.c_void_p),
+        ("shared_bits", ctypes.c_int32),
+        ("shared_gate_q", ctypes.c_void_p),
+        ("shared_gate_s", ctypes.c_void_p),
+        ("shared_up_q", ctypes.c_void_p),
+        ("shared_up_s", ctypes.c_void_p),
+        ("shared_down_q", ctypes.c_void_p),
+        ("shared_down_s", ctypes.c_void_p),
     ]
 
 
@@ -75,6 +83,7 @@ _sigs = {
                                          ctypes.c_uint32, ctypes.c_float, _P, _P, _SZ, _P]),
     "moe_w4_dequant": (ctypes.c_int, [_P, _P, _I64, _I64, _I32, _P, _P]),
     "moe_w4_quantize": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P]),
+    "moe_w8_quantize": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
     "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_last_hip_error": (ctypes.c_char_p, []),
 }
@@ -118,11 +127,16 @@ def _check(fn: str, status: int):
 
 def make_layer(num_experts, hidden, ffn, top_k, router_w, router_b, gate_q, gate_s, up_q, up_s,
                down_q, down_s, shared_ffn=0, shared_gate=None, shared_up=None, shared_down=None,
-               group_size=128) -> MoeLayer:
+               group_size=128, shared_w8=None) -> MoeLayer:
+    """shared_w8: None, or ((gate_q, gate_s), (up_q, up_s), (down_q, down_s)) of
+    an 8-bit shared expert (then shared_gate/up/down are not used)."""
+    w8 = shared_w8 if shared_w8 is not None else ((None, None),) * 3
     return MoeLayer(num_experts, hidden, ffn, top_k, group_size, shared_ffn,
                     _ptr(router_w), _ptr(router_b), _ptr(gate_q), _ptr(gate_s), _ptr(up_q),
                     _ptr(up_s), _ptr(down_q), _ptr(down_s), _ptr(shared_gate), _ptr(shared_up),
-                    _ptr(shared_down))
+                    _ptr(shared_down), 8 if shared_w8 is not None else 16,
+                    _ptr(w8[0][0]), _ptr(w8[0][1]), _ptr(w8[1][0]), _ptr(w8[1][1]),
+                    _ptr(w8[2][0]), _ptr(w8[2][1]))
 
 
 def moe_workspace_size(layer: MoeLayer, max_tokens: int) -> int:
@@ -177,6 +191,11 @@ def moe_layer_forward(layer, x, T, topk_idx, topk_w, offsets, perm_src, inv_pos,
 def moe_w4_dequant(q, s, rows, cols, group_size, out, stream=None):
     _check("moe_w4_dequant", lib.moe_w4_dequant(_ptr(q), _ptr(s), rows, cols, group_size,
                                                 _ptr(out), _stream(stream)))
+
+
+def moe_w8_quantize(w, rows, cols, q, s, stream=None):
+    _check("moe_w8_quantize", lib.moe_w8_quantize(_ptr(w), rows, cols, _ptr(q), _ptr(s),
+                                                  _stream(stream)))
 
 
 def moe_w4_quantize(w, rows, cols, group_size, q, s, stream=None):

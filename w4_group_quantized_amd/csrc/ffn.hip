@@ -24,7 +24,8 @@
 //     read their MFMA operands from there.
 //   shared item = (16-token tile, 16 weight rows); the 4 waves split K 4 ways,
 //     so that a wave moves as many bytes as a routed wave (fp16 weights are 4x
-//     the bytes of int4).
+//     the bytes of int4).  The shared expert's weights are fp16, or 8-bit g128
+//     codes (xdnf.cn/news/329730 §3.1 keeps the shared FFN at 8 bits).
 // The grid is sized for the worst case on the host; items past the live
 // segment tiles exit right after locating themselves (nothing is read back to
 // the host between calls).
@@ -50,6 +51,9 @@ struct FfnArgs {
   const uint8_t *q0, *q1;           // phase 1: gate_q, up_q;  phase 2: down_q, unused
   const f16 *s0, *s1;               // matching scales
   const f16 *w0, *w1;               // shared expert fp16 weights (phase 2: w0 only)
+  const uint8_t *wq0, *wq1;         // or its 8-bit codes (shared_w8) ...
+  const f16 *ws0, *ws1;             // ... and their g128 scales
+  int shared_w8;
   f16 *out_routed;                  // phase 1: h [N, F];      phase 2: y_perm [N, H]
   f16 *out_shared;                  // phase 1: h_shared;      phase 2: y_shared
   int shared_items;                 // shared-expert items (blocks 0 .. shared_items-1)
@@ -223,14 +227,27 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
   const int rows = min(kTileM, p.T - tok0);
   const ARows arow(p.a_shared + (size_t)tok0 * Ks, rows, Ks, r, r < rows, kb);
   const int nrow = nt * 16 + r;
-  const f16 *wrow[kMats];
-  wrow[0] = p.w0 + (size_t)nrow * Ks;
-  if (kPair) wrow[kMats - 1] = p.w1 + (size_t)nrow * Ks;
   f32x4 acc[kMats];
 #pragma unroll
   for (int t = 0; t < kMats; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
   const int g0 = wid * Gs / 4, g1 = (wid + 1) * Gs / 4;
-  f16_tiles<kMats>(arow, wrow, kb, g0, g1, acc);
+  if (p.shared_w8) {     // block-uniform: 8-bit codes, 16-row tile nt
+    const size_t tile = (size_t)nt * 16;
+    const uint8_t *qrow[kMats];
+    const f16 *srow[kMats];
+    qrow[0] = p.wq0 + tile * Ks + kb * 512 + r * 16;
+    srow[0] = p.ws0 + tile * Gs + r;
+    if (kPair) {
+      qrow[kMats - 1] = p.wq1 + tile * Ks + kb * 512 + r * 16;
+      srow[kMats - 1] = p.ws1 + tile * Gs + r;
+    }
+    w8_tiles<kMats>(arow, qrow, srow, g0, g1, acc);
+  } else {
+    const f16 *wrow[kMats];
+    wrow[0] = p.w0 + (size_t)nrow * Ks;
+    if (kPair) wrow[kMats - 1] = p.w1 + (size_t)nrow * Ks;
+    f16_tiles<kMats>(arow, wrow, kb, g0, g1, acc);
+  }
   ksplit_reduce<kMats>(acc, red);
   if (wid != 0) return;
 #pragma unroll
@@ -307,6 +324,10 @@ hipError_t launch_ffn(const moe_layer &L, const uint16_t *x, const uint16_t *x_p
   a.s1 = reinterpret_cast<const f16 *>(L.up_s);
   a.w0 = reinterpret_cast<const f16 *>(L.shared_gate);
   a.w1 = reinterpret_cast<const f16 *>(L.shared_up);
+  a.shared_w8 = L.shared_bits == 8;
+  a.wq0 = L.shared_gate_q; a.wq1 = L.shared_up_q;
+  a.ws0 = reinterpret_cast<const f16 *>(L.shared_gate_s);
+  a.ws1 = reinterpret_cast<const f16 *>(L.shared_up_s);
   a.out_routed = reinterpret_cast<f16 *>(h);
   a.out_shared = reinterpret_cast<f16 *>(h_shared);
   const bool wide = N >= kWideMinAvgRows * E;
@@ -331,6 +352,8 @@ hipError_t launch_ffn(const moe_layer &L, const uint16_t *x, const uint16_t *x_p
   a.q0 = L.down_q; a.q1 = nullptr;
   a.s0 = reinterpret_cast<const f16 *>(L.down_s); a.s1 = nullptr;
   a.w0 = reinterpret_cast<const f16 *>(L.shared_down); a.w1 = nullptr;
+  a.wq0 = L.shared_down_q; a.wq1 = nullptr;
+  a.ws0 = reinterpret_cast<const f16 *>(L.shared_down_s); a.ws1 = nullptr;
   a.out_routed = reinterpret_cast<f16 *>(y_perm);
   a.out_shared = reinterpret_cast<f16 *>(y_shared);
   const bool wide2 = wide && H % 256 == 0;

@@ -34,6 +34,8 @@ hipError_t launch_quantize(const uint16_t *w, int64_t rows, int64_t cols, int gs
                            uint16_t *s, hipStream_t st);
 hipError_t launch_dequant(const uint8_t *q, const uint16_t *s, int64_t rows, int64_t cols, int gs,
                           float *out, hipStream_t st);
+hipError_t launch_quantize8(const uint16_t *w, int64_t rows, int64_t cols, uint8_t *q,
+                            uint16_t *s, hipStream_t st);
 hipError_t launch_route(const moe_layer &L, const uint16_t *x, int32_t T, int32_t *idx,
                         float *w, float *logits, hipStream_t st);
 hipError_t launch_route_permute_fused(const moe_layer &L, const uint16_t *x, int32_t T,

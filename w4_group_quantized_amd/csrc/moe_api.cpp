@@ -48,6 +48,7 @@ static moe_status check_layer(const moe_layer *L) {
     return MOE_EUNSUPPORTED;
   // whole groups per row of every int4 matrix (in_features H and F)
   if (L->hidden % L->group_size || L->ffn % L->group_size) return MOE_EUNSUPPORTED;
+  if (L->shared_bits != 0 && L->shared_bits != 16 && L->shared_bits != 8) return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
 
@@ -106,9 +107,16 @@ static moe_status check_ffn_args(const moe_layer *L, int32_t T, const uint16_t *
   if (x_perm ? !aligned16(x_perm) : (!ok_ptr(x) || !ok_ptr(perm_src))) return MOE_EINVAL;
   // gathering rows straight from x addresses it with 32-bit byte offsets
   if (!x_perm && (int64_t)T * L->hidden * 2 >= ((int64_t)1 << 31)) return MOE_EUNSUPPORTED;
-  if (L->shared_ffn > 0 && (!ok_ptr(x) || !ok_ptr(y_shared) || !ok_ptr(L->shared_gate) ||
-                            !ok_ptr(L->shared_up) || !ok_ptr(L->shared_down)))
-    return MOE_EINVAL;
+  if (L->shared_ffn > 0) {
+    if (!ok_ptr(x) || !ok_ptr(y_shared)) return MOE_EINVAL;
+    if (L->shared_bits == 8) {
+      if (!ok_ptr(L->shared_gate_q) || !ok_ptr(L->shared_gate_s) || !ok_ptr(L->shared_up_q) ||
+          !ok_ptr(L->shared_up_s) || !ok_ptr(L->shared_down_q) || !ok_ptr(L->shared_down_s))
+        return MOE_EINVAL;
+    } else if (!ok_ptr(L->shared_gate) || !ok_ptr(L->shared_up) || !ok_ptr(L->shared_down)) {
+      return MOE_EINVAL;
+    }
+  }
   return MOE_OK;
 }
 
@@ -300,6 +308,17 @@ moe_status moe_w4_quantize(const uint16_t *w, int64_t rows, int64_t cols, int32_
   if (!ok_ptr(w) || !ok_ptr(q) || !ok_ptr(s)) return MOE_EINVAL;
   clear_stale_hip_error();
   return hip_status(launch_quantize(w, rows, cols, group_size, q, s, (hipStream_t)stream));
+}
+
+moe_status moe_w8_quantize(const uint16_t *w, int64_t rows, int64_t cols, uint8_t *q, uint16_t *s,
+                           void *stream) {
+  if (rows < 0 || cols < 0) return MOE_EINVAL;
+  if (cols % 128 || rows % 16) return MOE_EUNSUPPORTED;
+  if (rows == 0 || cols == 0) return MOE_OK;
+  if ((rows * (cols / 8) + 255) / 256 > 0x7fffffffLL) return MOE_EUNSUPPORTED;
+  if (!ok_ptr(w) || !ok_ptr(q) || !ok_ptr(s)) return MOE_EINVAL;
+  clear_stale_hip_error();
+  return hip_status(launch_quantize8(w, rows, cols, q, s, (hipStream_t)stream));
 }
 
 const char *moe_last_hip_error(void) {

@@ -94,6 +94,61 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t *__restrict
   o[1] = b;
 }
 
+// 8-bit codes for the shared expert (xdnf.cn/news/329730 §3.1: shared FFN at
+// 8 bits, 128-weight groups): the same steps with 127 and [-128, 127]; the
+// byte q + 128 of column c of row n goes to (n/16)*16*cols + (c/16)*256 +
+// (n%16)*16 + c%16, so a thread's 8 columns are one aligned 8-byte store.
+__global__ __launch_bounds__(256) void quantize8_kernel(const f16 *__restrict__ w,
+                                                        int64_t rows, int64_t cols,
+                                                        uint8_t *__restrict__ q,
+                                                        f16 *__restrict__ s) {
+  const int64_t words_per_row = cols / 8;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const bool live = t < rows * words_per_row;
+  const int64_t row = live ? t / words_per_row : 0, word = live ? t % words_per_row : 0;
+  float v[8];
+  float m = 0.0f;
+  if (live) {
+    const f16x8 h = as_f16x8(ld16(w + row * cols + word * 8));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[i] = (float)h[i];
+      m = fmaxf(m, fabsf(v[i]));
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));   // 16 lanes = 128 columns
+  if (!live) return;
+  const f16 s16 = (f16)__fdiv_rn(m, 127.0f);
+  const float sf = (float)s16;
+  uint32_t b[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float qi = 0.0f;
+    if (sf > 0.0f) {
+      const f16 r16 = (f16)__fdiv_rn(v[i], sf);
+      qi = fminf(fmaxf(rintf((float)r16), -128.0f), 127.0f);
+    }
+    b[i] = (uint32_t)((int)qi + 128);
+  }
+  uint2 packed;
+  packed.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+  packed.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+  const int64_t col = word * 8;
+  *reinterpret_cast<uint2 *>(q + (size_t)(row >> 4) * 16 * cols + (size_t)(col >> 4) * 256 +
+                             (size_t)(row & 15) * 16 + (size_t)(col & 15)) = packed;
+  if ((word & 15) == 0) s[scale_offset(row, word / 16, cols, 128)] = s16;
+}
+
+hipError_t launch_quantize8(const uint16_t *w, int64_t rows, int64_t cols, uint8_t *q,
+                            uint16_t *s, hipStream_t st) {
+  const int64_t total = rows * (cols / 8);
+  const int64_t blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(quantize8_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
+                     reinterpret_cast<const f16 *>(w), rows, cols, q, reinterpret_cast<f16 *>(s));
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize(const uint16_t *w, int64_t rows, int64_t cols, int gs, uint8_t *q,
                            uint16_t *s, hipStream_t st) {
   const int64_t total = rows * (cols / 8);

@@ -218,6 +218,85 @@ __device__ __forceinline__ void f16_tiles(const ARows &arow,
   if (g < g1) f16_compute<NT>(a, acc);
 }
 
+// 8-bit weights (the shared expert's W8 g128 format: offset-binary bytes,
+// 16-row tiles of 16-column chunks, 2 KB per tile and 128-column block).
+// Lane (r, kb) holds the 32 bytes of columns [32kb, 32kb + 32) of weight row
+// r in a block: chunks 2kb and 2kb+1, 256 bytes apart; MFMA m uses bytes
+// 8m .. 8m+7, the same columns as the activation piece m.  The codes become
+// exact fp16 values: byte b is placed under the exponent byte 0x64 (giving
+// 1024 + b) and 1152 is subtracted.  One fp16 scale per row and block,
+// applied to the block's product in fp32.
+__device__ __forceinline__ f16x8 unpack_i8x8(uint32_t lo, uint32_t hi) {
+  constexpr uint32_t kHi = 0x64646464u;
+  u32x4 v;
+  // byte selectors: 0..3 pick bytes of the second operand, 4..7 of the first
+  v[0] = __builtin_amdgcn_perm(kHi, lo, 0x05010400u);
+  v[1] = __builtin_amdgcn_perm(kHi, lo, 0x05030402u);
+  v[2] = __builtin_amdgcn_perm(kHi, hi, 0x05010400u);
+  v[3] = __builtin_amdgcn_perm(kHi, hi, 0x05030402u);
+  return as_f16x8(v) - (f16)1152.0f;
+}
+
+template <int NT>
+struct W8Stage {
+  u32x4 x[4];
+  u32x4 q[NT][2];
+  f16 s[NT];
+};
+
+template <int NT>
+__device__ __forceinline__ void w8_load(W8Stage<NT> &st, const ARows &arow,
+                                        const uint8_t *const (&qrow)[NT],
+                                        const f16 *const (&srow)[NT], int g, int G) {
+  const int gg = min(g, G - 1);   // past the end: reload the last block (never used)
+#pragma unroll
+  for (int m = 0; m < 4; ++m) st.x[m] = arow.load(gg, m);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    st.q[t][0] = ld16(qrow[t] + (size_t)gg * 2048);
+    st.q[t][1] = ld16(qrow[t] + (size_t)gg * 2048 + 256);
+    st.s[t] = srow[t][(size_t)gg * 16];
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ void w8_compute(const W8Stage<NT> &st, f32x4 (&acc)[NT]) {
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const u32x4 &c = st.q[t][m >> 1];
+      tmp = mfma_16x16x32(as_f16x8(st.x[m]), unpack_i8x8(c[2 * (m & 1)], c[2 * (m & 1) + 1]), tmp);
+    }
+    acc[t] += (float)st.s[t] * tmp;
+  }
+}
+
+// 8-bit weights: acc[t] += sum_g scale[t][g] * sum_{k in g} A[tok][k] * q[t][k]
+// over blocks [g0, g1); qrow[t]: tile base + 2kb*256 + r*16 (block g at
+// + g*2048); srow[t]: the tile's scales + r (block g at srow[t][g*16]).
+template <int NT>
+__device__ __forceinline__ void w8_tiles(const ARows &arow, const uint8_t *const (&qrow)[NT],
+                                         const f16 *const (&srow)[NT], int g0, int g1,
+                                         f32x4 (&acc)[NT]) {
+  if (g0 >= g1) return;
+  W8Stage<NT> a, b;
+  w8_load<NT>(a, arow, qrow, srow, g0, g1);
+  int g = g0;
+  for (; g + 2 <= g1; g += 2) {
+    w8_load<NT>(b, arow, qrow, srow, g + 1, g1);
+    sched_fence();
+    w8_compute<NT>(a, acc);
+    sched_fence();
+    w8_load<NT>(a, arow, qrow, srow, g + 2, g1);
+    sched_fence();
+    w8_compute<NT>(b, acc);
+    sched_fence();
+  }
+  if (g < g1) w8_compute<NT>(a, acc);
+}
+
 // Sum the accumulators of the NW waves of a block (K split NW ways) into wave
 // 0, in the fixed order wave 0 + 1 + ... + NW-1.
 // red: LDS of (NW - 1) * NT * 4 * 64 floats.

@@ -38,24 +38,32 @@ class W4MoELayer:
     router_w fp16 [E,H], router_b fp32 [E] or None,
     gate_q/up_q uint8 [E,F,H/2], gate_s/up_s fp16 [E,F,H/gs],
     down_q uint8 [E,H,F/2], down_s fp16 [E,H,F/gs],
-    shared = None or (Wg fp16 [Fs,H], Wu fp16 [Fs,H], Wd fp16 [H,Fs]).
+    shared = None or (Wg fp16 [Fs,H], Wu fp16 [Fs,H], Wd fp16 [H,Fs]),
+    or shared_w8 = ((gate_q uint8 [Fs,H], gate_s fp16 [Fs,H/128]), (up ...),
+    (down_q [H,Fs], down_s [H,Fs/128])): an 8-bit shared expert (see
+    quantize_w8).
     """
 
     def __init__(self, top_k, router_w, router_b, gate_q, gate_s, up_q, up_s, down_q, down_s,
-                 shared=None, group_size=None):
+                 shared=None, group_size=None, shared_w8=None):
         E, H = router_w.shape
         F = gate_q.shape[1]
         self.E, self.H, self.F, self.k = E, H, F, top_k
-        self.Fs = shared[0].shape[0] if shared is not None else 0
+        if shared is not None and shared_w8 is not None:
+            raise ValueError("give the shared expert either in fp16 or in 8 bits")
+        self.Fs = (shared[0].shape[0] if shared is not None else
+                   shared_w8[0][0].shape[0] if shared_w8 is not None else 0)
         if group_size is None:
             group_size = H // gate_s.shape[2]
             if gate_s.shape[2] * group_size != H or down_s.shape[2] * group_size != F:
                 raise ValueError("scale shapes do not give one group size for both matrices")
         self.group_size = group_size
-        self.tensors = (router_w, router_b, gate_q, gate_s, up_q, up_s, down_q, down_s, shared)
+        self.tensors = (router_w, router_b, gate_q, gate_s, up_q, up_s, down_q, down_s, shared,
+                        shared_w8)
         sg, su, sd = shared if shared is not None else (None, None, None)
         self.desc = N.make_layer(E, H, F, top_k, router_w, router_b, gate_q, gate_s, up_q, up_s,
-                                 down_q, down_s, self.Fs, sg, su, sd, group_size=self.group_size)
+                                 down_q, down_s, self.Fs, sg, su, sd, group_size=self.group_size,
+                                 shared_w8=shared_w8)
 
     @property
     def device(self):
@@ -147,6 +155,17 @@ def quantize_fp16(w: torch.Tensor, group_size: int = 128, stream=None):
     q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=w.device)
     s = torch.empty((rows, cols // group_size), dtype=torch.float16, device=w.device)
     N.moe_w4_quantize(w, rows, cols, group_size, q, s, stream)
+    return q, s
+
+
+def quantize_w8(w: torch.Tensor, stream=None):
+    """8-bit g128 quantization of an fp16 device matrix [rows, cols] (the
+    shared expert's format).  Returns (codes uint8 [rows, cols], scales fp16
+    [rows, cols/128])."""
+    rows, cols = w.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=w.device)
+    s = torch.empty((rows, cols // 128), dtype=torch.float16, device=w.device)
+    N.moe_w8_quantize(w, rows, cols, q, s, stream)
     return q, s
 
 

@@ -51,6 +51,7 @@ class MoEConfig:
     x_std: float = 1.0
     rms_eps: float = 1e-6        # used between stacked layers only
     group_size: int = 128        # int4 quantization group along in_features (64 / 128 / 256)
+    shared_bits: int = 16        # shared expert weights: fp16, or 8-bit g128
 
     @property
     def has_bias(self) -> bool:
@@ -66,7 +67,8 @@ class MoEConfig:
         return self.expert_packed_bytes() + self.expert_scale_bytes()
 
     def shared_bytes(self) -> int:
-        return 3 * self.hidden * self.shared_ffn * 2
+        n = 3 * self.hidden * self.shared_ffn
+        return n * 2 if self.shared_bits == 16 else n + n // 128 * 2
 
 
 CONFIGS = {
