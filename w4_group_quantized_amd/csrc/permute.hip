@@ -52,8 +52,18 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t *__restri
   const int e = tid % Ep, pp = tid / Ep;
   const int c0 = (int)((int64_t)pp * nchunks / P), c1 = (int)((int64_t)(pp + 1) * nchunks / P);
   int sum = 0;
-  if (e < E)
-    for (int c = c0; c < c1; ++c) sum += counts[(size_t)c * E + e];
+  if (e < E) {
+    // eight independent loads in flight per round
+    int c = c0;
+    for (; c + 8 <= c1; c += 8) {
+      int v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = counts[(size_t)(c + i) * E + e];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sum += v[i];
+    }
+    for (; c < c1; ++c) sum += counts[(size_t)c * E + e];
+  }
   part[tid] = sum;
   __syncthreads();
   int pre = 0, tot = 0;
@@ -73,7 +83,18 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t *__restri
   __syncthreads();
   if (e < E) {
     int run = s_off[e] + pre;
-    for (int c = c0; c < c1; ++c) {
+    int c = c0;
+    for (; c + 8 <= c1; c += 8) {
+      int v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = counts[(size_t)(c + i) * E + e];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        bases[(size_t)(c + i) * E + e] = run;
+        run += v[i];
+      }
+    }
+    for (; c < c1; ++c) {
       const int v = counts[(size_t)c * E + e];
       bases[(size_t)c * E + e] = run;
       run += v;

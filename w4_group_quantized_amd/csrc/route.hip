@@ -134,77 +134,119 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const f16 *__restric
   }
 }
 
-// Prefill-sized batches: one block per 32 tokens x 128 experts; wave w owns
-// experts 32w .. 32w+31 of the block's expert tile and runs the whole K on
-// v_mfma_f32_32x32x16_f16 with both operands loaded straight from global
-// memory (the block's waves share the token rows through the caches), so x
-// is read from memory once instead of once per 16-expert tile.
-//
-// K is walked in 64-wide chunks; lane (row l%32, half l/32) loads the 64
-// contiguous bytes k = 32*(l/32) .. +31 of the chunk for its token row and
-// its expert row, and MFMA s of the chunk contracts piece s of both (k =
-// 8s .. 8s+7 and 32+8s .. 32+8s+7).  Four accumulators (one per piece) are
-// summed in a fixed order at the end.
+// Prefill-sized batches: one block per 32 tokens x 128 experts, so x is
+// read from memory once instead of once per 16-expert tile.  K is walked in
+// chunks of 128 columns.  The block loads each chunk's 32 token rows (8 KB)
+// and 128 router rows (32 KB) as coalesced 16-byte pieces (consecutive
+// threads cover consecutive pieces of a row), kRouterPf chunks ahead in
+// registers, and stores them into one of two LDS stages; wave w multiplies
+// the 32 tokens by experts 32w .. 32w+31 from LDS with
+// v_mfma_f32_32x32x16_f16.  Each LDS row is padded by one piece, so the
+// operand reads of 16 consecutive rows fall on distinct banks.  In each
+// 64-column block, lane (row l%32, half l/32) supplies pieces 4*(l/32) + s
+// to MFMA s (k = 8s .. 8s+7 and 32+8s .. 32+8s+7); the four accumulators
+// (one per s) are summed in a fixed order at the end.
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-struct RouterChunk {
-  u32x4 x[4], w[4];
-};
+constexpr int kRouterKc = 2;   // 64-column K blocks per chunk
+constexpr int kRouterPf = 2;   // chunks in flight in registers ahead of the LDS stage
+constexpr int kRouterRow = 8 * kRouterKc + 1;   // LDS row stride in 16-byte pieces (+1 pad)
 
 __global__ __launch_bounds__(256) void router_logits_wide_kernel(const f16 *__restrict__ x,
                                                                  const f16 *__restrict__ wr,
                                                                  const float *__restrict__ bias,
                                                                  int T, int E, int H,
                                                                  float *__restrict__ logits) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wv = threadIdx.x / kWave;
+  constexpr int KC = kRouterKc, PPR = 8 * KC;   // pieces per row and chunk
+  __shared__ u32x4 sx[2][32 * kRouterRow];
+  __shared__ u32x4 sw[2][128 * kRouterRow];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
   const int etiles = (E + 127) / 128;
   const int tok0 = (blockIdx.x / etiles) * 32;
-  const int e0 = (blockIdx.x % etiles) * 128 + wv * 32;
-  if (e0 >= E) return;
+  const int eb = (blockIdx.x % etiles) * 128;
   const int l32 = lane & 31, kh = lane >> 5;
-  // surplus token rows and expert rows repeat the last one; never stored
-  const f16 *xr = x + (size_t)min(tok0 + l32, T - 1) * H + kh * 32;
-  const f16 *wrr = wr + (size_t)min(e0 + l32, E - 1) * H + kh * 32;
-  const int C = H / 64;
-  auto load = [&](RouterChunk &c, int ci) {
-    const size_t k = (size_t)min(ci, C - 1) * 64;
+  const int C = H / (64 * KC);
+  // this thread's pieces: x piece tid + 256j (j < KC), router piece tid + 256j
+  // (j < 4KC); piece p is row p / PPR, column piece p % PPR
+  const f16 *xp[KC];
+  const f16 *wp[4 * KC];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      c.x[s] = ld16(xr + k + 8 * s);
-      c.w[s] = ld16(wrr + k + 8 * s);
+  for (int j = 0; j < KC; ++j) {
+    const int p = tid + 256 * j;
+    xp[j] = x + (size_t)min(tok0 + p / PPR, T - 1) * H + (p % PPR) * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < 4 * KC; ++j) {
+    const int p = tid + 256 * j;
+    wp[j] = wr + (size_t)min(eb + p / PPR, E - 1) * H + (p % PPR) * 8;
+  }
+  struct Pieces {
+    u32x4 x[KC], w[4 * KC];
+  };
+  auto gload = [&](Pieces &pc, int ci) {
+    const size_t k = (size_t)min(ci, C - 1) * 64 * KC;
+#pragma unroll
+    for (int j = 0; j < KC; ++j) pc.x[j] = ld16(xp[j] + k);
+#pragma unroll
+    for (int j = 0; j < 4 * KC; ++j) pc.w[j] = ld16(wp[j] + k);
+  };
+  auto lstore = [&](const Pieces &pc, int st) {
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+      const int p = tid + 256 * j;
+      sx[st][(p / PPR) * kRouterRow + p % PPR] = pc.x[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 4 * KC; ++j) {
+      const int p = tid + 256 * j;
+      sw[st][(p / PPR) * kRouterRow + p % PPR] = pc.w[j];
     }
   };
   f32x16 acc[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) acc[s] = (f32x16){};
-  auto compute = [&](const RouterChunk &c) {
+  auto compute = [&](int st) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(c.x[s]), as_f16x8(c.w[s]), acc[s],
-                                                     0, 0, 0);
+    for (int h = 0; h < KC; ++h)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const u32x4 a = sx[st][l32 * kRouterRow + 8 * h + 4 * kh + s];
+        const u32x4 b = sw[st][(wv * 32 + l32) * kRouterRow + 8 * h + 4 * kh + s];
+        acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(a), as_f16x8(b), acc[s], 0, 0, 0);
+      }
   };
-  RouterChunk a, b;
-  load(a, 0);
-  int ci = 0;
-  for (; ci + 2 <= C; ci += 2) {
-    load(b, ci + 1);
-    sched_fence();
-    compute(a);
-    sched_fence();
-    load(a, ci + 2);
-    sched_fence();
-    compute(b);
-    sched_fence();
+  constexpr int PF = kRouterPf;
+  Pieces r[PF];
+#pragma unroll
+  for (int u = 0; u < PF; ++u) gload(r[u], u);
+  lstore(r[0], 0);
+  gload(r[0], PF);
+  __syncthreads();
+  for (int c0 = 0;; c0 += PF) {
+    bool done = false;
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      if (!done) {
+        const int ci = c0 + u;
+        compute(ci & 1);
+        if (ci + 1 < C) {
+          lstore(r[(u + 1) % PF], (ci + 1) & 1);
+          gload(r[(u + 1) % PF], ci + 1 + PF);
+        }
+        __syncthreads();
+        done = ci + 1 >= C;
+      }
+    }
+    if (done) break;
   }
-  if (ci < C) compute(a);
-  // D register r of lane l: token row 8*(r/4) + 4*(l/32) + r%4, expert l%32
-  const int e = e0 + l32;
+  const int e = eb + wv * 32 + l32;
   if (e >= E) return;
   const float bb = bias ? bias[e] : 0.0f;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int tok = tok0 + 8 * (r >> 2) + 4 * kh + (r & 3);
-    if (tok < T) logits[(size_t)tok * E + e] = ((acc[0][r] + acc[1][r]) + (acc[2][r] + acc[3][r])) + bb;
+  for (int q = 0; q < 16; ++q) {
+    const int tok = tok0 + 8 * (q >> 2) + 4 * kh + (q & 3);
+    if (tok < T) logits[(size_t)tok * E + e] = ((acc[0][q] + acc[1][q]) + (acc[2][q] + acc[3][q])) + bb;
   }
 }
 
