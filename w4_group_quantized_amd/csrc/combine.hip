@@ -25,6 +25,35 @@ __device__ __forceinline__ void renorm_weights(float *s_w, int k) {
   __syncthreads();
 }
 
+// v[i] += w_j * y_perm[row_j][c + i] for j = 0 .. k-1 in that order, fp32.
+// row_of(j) and w_of(j) give the permuted row (in [0, N)) and the weight of
+// slot j; eight slots at a time, their row indices first and then all eight
+// 16-byte row loads, so that a round costs two memory latencies instead of
+// two per slot.
+template <class RowOf, class WOf>
+__device__ __forceinline__ void accumulate_rows(float (&v)[8], const f16 *__restrict__ y_perm,
+                                                int H, int c, int k, RowOf row_of, WOf w_of) {
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    int r[8];
+    float wj[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      r[i] = j0 + i < k ? row_of(j0 + i) : 0;
+      wj[i] = j0 + i < k ? w_of(j0 + i) : 0.0f;
+    }
+    f16x8 y[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (j0 + i < k) y[i] = as_f16x8(ld16(y_perm + (size_t)r[i] * H + c));
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (j0 + i < k) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = fmaf(wj[i], (float)y[i][e], v[e]);
+      }
+  }
+}
+
 // One block per token; each thread owns 8-column chunks of the row.
 __global__ __launch_bounds__(256) void combine_kernel(const f16 *__restrict__ y_perm,
                                                       const f16 *__restrict__ ys,
@@ -53,12 +82,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const f16 *__restrict__ y_
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] = 0.0f;
     }
-    for (int j = 0; j < k; ++j) {
-      const f16x8 y = as_f16x8(ld16(y_perm + (size_t)s_row[j] * H + c));
-      const float wj = s_w[j];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = fmaf(wj, (float)y[i], v[i]);
-    }
+    accumulate_rows(v, y_perm, H, c, k, [&](int j) { return s_row[j]; },
+                    [&](int j) { return s_w[j]; });
   };
 
   float scale = 1.0f;
@@ -112,14 +137,13 @@ __global__ __launch_bounds__(64) void combine_cols_kernel(const f16 *__restrict_
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = 0.0f;
   }
-  for (int j = 0; j < k; ++j) {
-    int r = inv_pos[(size_t)t * k + j];
-    r = r < 0 ? 0 : (r >= N ? N - 1 : r);
-    const float wj = renorm ? w[(size_t)t * k + j] / wsum : w[(size_t)t * k + j];
-    const f16x8 y = as_f16x8(ld16(y_perm + (size_t)r * H + c));
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = fmaf(wj, (float)y[i], v[i]);
-  }
+  accumulate_rows(
+      v, y_perm, H, c, k,
+      [&](int j) {
+        const int r = inv_pos[(size_t)t * k + j];
+        return r < 0 ? 0 : (r >= N ? N - 1 : r);
+      },
+      [&](int j) { return renorm ? w[(size_t)t * k + j] / wsum : w[(size_t)t * k + j]; });
   f16x8 o;
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = (f16)v[i];
@@ -157,14 +181,9 @@ __global__ __launch_bounds__(1024) void combine_norm_kernel(const f16 *__restric
   }
   __syncthreads();
   if (renorm) renorm_weights(s_w, k);
-  if (live) {
-    for (int j = 0; j < k; ++j) {
-      const f16x8 y = as_f16x8(ld16(y_perm + (size_t)s_row[j] * H + c));
-      const float wj = s_w[j];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = fmaf(wj, (float)y[i], v[i]);
-    }
-  }
+  if (live)
+    accumulate_rows(v, y_perm, H, c, k, [&](int j) { return s_row[j]; },
+                    [&](int j) { return s_w[j]; });
   float ss = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ss = fmaf(v[i], v[i], ss);
