@@ -29,22 +29,30 @@ __device__ __forceinline__ void renorm_weights(float *s_w, int k) {
 // row_of(j) and w_of(j) give the permuted row (in [0, N)) and the weight of
 // slot j; eight slots at a time, their row indices first and then all eight
 // 16-byte row loads, so that a round costs two memory latencies instead of
-// two per slot.
-template <class RowOf, class WOf>
+// two per slot.  The loads are unconditional (slots past k repeat slot k-1
+// and are not added): a load under a branch would make the compiler wait
+// for every earlier load at the branch's end.
+// init(v) sets the starting values once the first round's loads are out.
+struct NoInit {
+  __device__ __forceinline__ void operator()(float (&)[8]) const {}
+};
+template <class RowOf, class WOf, class Init = NoInit>
 __device__ __forceinline__ void accumulate_rows(float (&v)[8], const f16 *__restrict__ y_perm,
-                                                int H, int c, int k, RowOf row_of, WOf w_of) {
+                                                int H, int c, int k, RowOf row_of, WOf w_of,
+                                                Init init = Init()) {
   for (int j0 = 0; j0 < k; j0 += 8) {
     int r[8];
     float wj[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      r[i] = j0 + i < k ? row_of(j0 + i) : 0;
-      wj[i] = j0 + i < k ? w_of(j0 + i) : 0.0f;
+      const int j = min(j0 + i, k - 1);
+      r[i] = row_of(j);
+      wj[i] = w_of(j);
     }
     f16x8 y[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (j0 + i < k) y[i] = as_f16x8(ld16(y_perm + (size_t)r[i] * H + c));
+    for (int i = 0; i < 8; ++i) y[i] = as_f16x8(ld16(y_perm + (size_t)r[i] * H + c));
+    if (j0 == 0) init(v);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       if (j0 + i < k) {
@@ -123,27 +131,28 @@ __global__ __launch_bounds__(64) void combine_cols_kernel(const f16 *__restrict_
   const int t = blockIdx.x / chunks;
   const int c = (blockIdx.x % chunks) * 512 + threadIdx.x * 8;
   if (c >= H) return;
+  // the shared expert's piece through a buffer that is empty without one,
+  // so it loads (as zeros) with the row indices and no branch
+  const rsrc_t yrs = make_rsrc(ys, ys ? (uint32_t)(t + 1) * (uint32_t)H * 2u : 0u);
+  const u32x4 yraw = bload16(yrs, ((uint32_t)t * H + c) * 2u, 0);
   float wsum = 1.0f;
   if (renorm) {
     wsum = 0.0f;
     for (int j = 0; j < k; ++j) wsum += w[(size_t)t * k + j];
   }
   float v[8];
-  if (ys) {
-    const f16x8 a = as_f16x8(ld16(ys + (size_t)t * H + c));
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = (float)a[i];
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-  }
   accumulate_rows(
       v, y_perm, H, c, k,
       [&](int j) {
         const int r = inv_pos[(size_t)t * k + j];
         return r < 0 ? 0 : (r >= N ? N - 1 : r);
       },
-      [&](int j) { return renorm ? w[(size_t)t * k + j] / wsum : w[(size_t)t * k + j]; });
+      [&](int j) { return renorm ? w[(size_t)t * k + j] / wsum : w[(size_t)t * k + j]; },
+      [&](float (&a)[8]) {
+        const f16x8 h = as_f16x8(yraw);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a[i] = (float)h[i];
+      });
   f16x8 o;
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = (f16)v[i];

@@ -18,14 +18,15 @@
 namespace moe {
 
 // One wave: softmax over the E logits of one token and its k best experts in
-// order.  get(i) returns the logit of expert lane + 64 i (i < NPER; experts
-// past E are skipped), get_expert(e) the logit of expert e.  Each lane sorts
+// order.  get_expert(e) returns the logit of expert e; lane l holds experts
+// l + 64 i (i < NPER), read unconditionally (past E: expert E-1, then
+// masked) so that all NPER reads are in flight together.  Each lane sorts
 // its NPER (logit, expert) keys once; every round is one wave-wide maximum
 // over the lanes' current heads, and the winning lane shifts its list.
 // Writes idx_out[0..k), w_out[0..k) and, when lds_idx is given, the indices
 // there too.
-template <int NPER, class Get, class GetE>
-__device__ __forceinline__ void wave_softmax_topk(Get get, GetE get_expert, int E, int k,
+template <int NPER, class GetE>
+__device__ __forceinline__ void wave_softmax_topk(GetE get_expert, int E, int k,
                                                   int32_t *__restrict__ idx_out,
                                                   float *__restrict__ w_out, int *lds_idx) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -33,9 +34,11 @@ __device__ __forceinline__ void wave_softmax_topk(Get get, GetE get_expert, int 
   uint64_t key[NPER];
   float m = -__builtin_inff();
 #pragma unroll
+  for (int i = 0; i < NPER; ++i) v[i] = get_expert(min(lane + i * kWave, E - 1));
+#pragma unroll
   for (int i = 0; i < NPER; ++i) {
     const int e = lane + i * kWave;
-    v[i] = e < E ? get(i) : -__builtin_inff();
+    v[i] = e < E ? v[i] : -__builtin_inff();
     key[i] = e < E ? route_key(v[i], e) : 0ull;
     if (e < E) m = fmax_nan(m, v[i]);
   }
@@ -85,13 +88,13 @@ __device__ __forceinline__ void wave_softmax_topk(Get get, GetE get_expert, int 
 }
 
 // Instantiate for the number of logits each lane holds (1..16, E <= 1024).
-template <class Get, class GetE>
-__device__ __forceinline__ void wave_softmax_topk_any(Get get, GetE get_expert, int E, int k,
+template <class GetE>
+__device__ __forceinline__ void wave_softmax_topk_any(GetE get_expert, int E, int k,
                                                       int32_t *idx_out, float *w_out,
                                                       int *lds_idx) {
   switch ((E + kWave - 1) / kWave) {
 #define MOE_TOPK_CASE(n) \
-    case n: wave_softmax_topk<n>(get, get_expert, E, k, idx_out, w_out, lds_idx); break;
+    case n: wave_softmax_topk<n>(get_expert, E, k, idx_out, w_out, lds_idx); break;
     MOE_TOPK_CASE(1) MOE_TOPK_CASE(2) MOE_TOPK_CASE(3) MOE_TOPK_CASE(4)
     MOE_TOPK_CASE(5) MOE_TOPK_CASE(6) MOE_TOPK_CASE(7) MOE_TOPK_CASE(8)
     MOE_TOPK_CASE(9) MOE_TOPK_CASE(10) MOE_TOPK_CASE(11) MOE_TOPK_CASE(12)
@@ -255,12 +258,10 @@ __global__ __launch_bounds__(256) void softmax_topk_kernel(const float *__restri
                                                            int T, int E, int k,
                                                            int32_t *__restrict__ idx,
                                                            float *__restrict__ w) {
-  const int lane = threadIdx.x & (kWave - 1);
   const int t = blockIdx.x * 4 + threadIdx.x / kWave;
   if (t >= T) return;
   const float *lt = logits + (size_t)t * E;
-  wave_softmax_topk_any([&](int i) { return lt[lane + i * kWave]; },
-                        [&](int e) { return lt[e]; }, E, k, idx + (size_t)t * k,
+  wave_softmax_topk_any([&](int e) { return lt[e]; }, E, k, idx + (size_t)t * k,
                         w + (size_t)t * k, nullptr);
 }
 
@@ -346,22 +347,32 @@ __global__ __launch_bounds__(kFusedWaves * kWave) void route_permute_kernel(Fuse
   // loads are independent so they are all in flight together
   {
     // four logits per thread and K part: 16-byte loads that read the device
-    // coherence point (sc1), like the agent-scope atomic loads they replace
+    // coherence point (sc1), like the agent-scope atomic loads they replace.
+    // The loads are unconditional, so none of them waits for another:
+    // vectors past the last logit read in-bounds values that are never
+    // stored.  The bias (a zero-length buffer when there is none) is loaded
+    // in the same round.
     const rsrc_t prs = make_rsrc(p.partial, (uint32_t)(p.ksb * TEp) * 4u);
+    const rsrc_t brs = make_rsrc(p.bias, p.bias ? (uint32_t)E * 4u : 0u);
     auto sum_parts = [&](auto nparts_tag, auto nvec_tag) {
       constexpr int NP = decltype(nparts_tag)::value;   // K parts held at once
       constexpr int NV = decltype(nvec_tag)::value;     // vectors per thread at once
       for (int base = 0; base < TEp / 4; base += NV * kFusedWaves * kWave) {
         f32x4 part[NV][NP];
+        float bv[NV][4];
 #pragma unroll
         for (int u = 0; u < NV; ++u) {   // every load of the round before any sum
           const int i4 = base + tid + u * kFusedWaves * kWave;
 #pragma unroll
           for (int kp = 0; kp < NP; ++kp)
-            if (kp < p.ksb && i4 < TEp / 4)
-              part[u][kp] = __builtin_bit_cast(
-                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                             prs, (uint32_t)(kp * TEp + 4 * i4) * 4u, 0, kBufCoherent));
+            part[u][kp] = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                           prs, (uint32_t)(kp * TEp + 4 * i4) * 4u, 0, kBufCoherent));
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            bv[u][c] = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(
+                           brs, (uint32_t)(min(4 * i4 + c, TE - 1) % E) * 4u, 0, 0));
         }
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
@@ -372,26 +383,32 @@ __global__ __launch_bounds__(kFusedWaves * kWave) void route_permute_kernel(Fuse
             if (i < TE) {
               float a = part[u][0][c];
 #pragma unroll
-              for (int kp = 1; kp < NP; ++kp)
-                if (kp < p.ksb) a += part[u][kp][c];
-              s_logit[i] = a + (p.bias ? p.bias[i % E] : 0.0f);
+              for (int kp = 1; kp < NP; ++kp) a += part[u][kp][c];
+              s_logit[i] = a + bv[u][c];
             }
           }
         }
       }
     };
-    if (p.ksb <= 4)     // two vectors per thread: up to 8192 logits in one round trip
-      sum_parts(std::integral_constant<int, 4>(), std::integral_constant<int, 2>());
-    else
-      sum_parts(std::integral_constant<int, kFusedMaxKsb>(), std::integral_constant<int, 1>());
+    // ksb is a power of two up to kFusedMaxKsb: one instantiation per value,
+    // so every load issued is a part that exists; up to 4 parts, two vectors
+    // per thread (8192 logits in one round trip)
+    using std::integral_constant;
+    static_assert(kFusedMaxKsb == 16, "one case per power of two up to kFusedMaxKsb");
+    switch (p.ksb) {
+      case 1: sum_parts(integral_constant<int, 1>(), integral_constant<int, 2>()); break;
+      case 2: sum_parts(integral_constant<int, 2>(), integral_constant<int, 2>()); break;
+      case 4: sum_parts(integral_constant<int, 4>(), integral_constant<int, 2>()); break;
+      case 8: sum_parts(integral_constant<int, 8>(), integral_constant<int, 1>()); break;
+      default: sum_parts(integral_constant<int, kFusedMaxKsb>(), integral_constant<int, 1>());
+    }
   }
   __syncthreads();
 
   // softmax + top-k, one wave per token
   for (int t = wid; t < T; t += kFusedWaves) {
     const float *lt = s_logit + t * E;
-    wave_softmax_topk_any([&](int i) { return lt[lane + i * kWave]; },
-                          [&](int e) { return lt[e]; }, E, k, p.idx + (size_t)t * k,
+    wave_softmax_topk_any([&](int e) { return lt[e]; }, E, k, p.idx + (size_t)t * k,
                           p.w + (size_t)t * k, s_idx + t * k);
   }
   for (int e = tid; e < E; e += blockDim.x) s_cnt[e] = 0;
