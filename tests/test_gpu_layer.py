@@ -10,8 +10,8 @@ import oracle as O
 from workloads import get_config
 from workloads import gen as G
 
-from gpu_util import (gpu, require_gpu, to_dev, tol_check, quantized_experts, make_gpu_layer,
-                      route_compare)
+from gpu_util import (gpu, require_gpu, to_dev, tol_check, quantized_experts, coded_experts,
+                      make_gpu_layer, route_compare)
 
 pytestmark = gpu
 
@@ -274,3 +274,45 @@ def test_layer_with_8bit_shared_expert(T):
     diff = route_compare(_np(buf.topk_idx), ref["idx"], ref["logits"], cfg.top_k)
     ok = ~diff
     tol_check(out[ok], ref["out"][ok], "layer out")
+
+
+def test_largest_hidden_size():
+    """hidden = 65536, the largest the ABI accepts: the one-launch router with
+    its maximum of 16 K parts, gate/up rows of 128 KB streamed from memory
+    (too large to stage in LDS), 4096 down-projection row tiles, and the
+    combine over rows wider than one block (without the norm, and with it,
+    the two-pass kernel for rows over 8192 columns).  Expert weights are
+    drawn as codes (the quantizer is pinned elsewhere)."""
+    cfg = get_config("decode_fine", num_experts=3, hidden=65536, ffn=128, top_k=2,
+                     shared_ffn=128)
+    mats, experts = coded_experts(cfg)
+    wr, b = G.router(cfg)
+    shared = G.shared_expert(cfg)
+    x = G.activations(cfg, tokens=5, batch=1)
+    ref = O.moe_layer(x, wr, b, experts, cfg.top_k, shared=shared)
+    layer = make_gpu_layer(cfg, mats, wr, b, shared)
+    buf = layer.alloc(5)
+    for rmsnorm in (False, True):
+        want = O.rmsnorm(ref["out"], cfg.rms_eps) if rmsnorm else ref["out"]
+        out = _np(layer.forward(to_dev(x), buf, rmsnorm=rmsnorm, eps=cfg.rms_eps))
+        torch.cuda.synchronize()
+        diff = route_compare(_np(buf.topk_idx), ref["idx"], ref["logits"], cfg.top_k)
+        ok = ~diff
+        tol_check(out[ok], want[ok], f"H = 65536, norm {rmsnorm}")
+
+
+def test_largest_ffn_size():
+    """ffn = 262144, the largest the ABI accepts: 4096 gate/up row tiles per
+    segment tile and a down projection whose K is 2048 blocks of 128."""
+    cfg = get_config("tiny", num_experts=2, hidden=128, ffn=262144, top_k=1)
+    mats, experts = coded_experts(cfg)
+    wr, b = G.router(cfg)
+    x = G.activations(cfg, tokens=3, batch=2)
+    ref = O.moe_layer(x, wr, b, experts, cfg.top_k)
+    layer = make_gpu_layer(cfg, mats, wr, b, None)
+    buf = layer.alloc(3)
+    out = _np(layer.forward(to_dev(x), buf))
+    torch.cuda.synchronize()
+    diff = route_compare(_np(buf.topk_idx), ref["idx"], ref["logits"], cfg.top_k)
+    ok = ~diff
+    tol_check(out[ok], ref["out"][ok], "F = 262144")
