@@ -8,9 +8,13 @@
  *   moe_permute            per-expert token segments (histogram, scan, scatter)
  *   moe_w4_grouped_ffn     SwiGLU FFN of every routed expert over its segment,
  *                          int4 weights dequantized inside the kernel, plus the
- *                          always-on fp16 shared expert
+ *                          always-on shared expert (fp16, or 8-bit)
  *   moe_unpermute_combine  weighted sum of each token's k expert outputs plus
  *                          the shared expert's output (optional RMS norm)
+ *
+ * moe_route_permute does the first two in one call (one launch for small
+ * batches) and moe_layer_forward all four.  moe_w4_quantize and
+ * moe_w8_quantize write the weight formats below from fp16 matrices.
  *
  * Sources: symmetric int4 group quantization with 128 weights per group along
  * in_features, scale = max|w| / 7, codes clamped to [-8, 7]: lpnh.cn/news/
