@@ -351,3 +351,71 @@ def test_combine(T, k, H, with_shared, rms, renorm):
     layer.combine(buf, T, rmsnorm=rms, renorm=renorm)
     torch.cuda.synchronize()
     tol_check(_np(buf.out), ref, "combine")
+
+
+# ---------------------------------------------------------------- exact-arithmetic probe
+def _probe_codes(rng, rows, cols, kind):
+    """Integer codes for the exact probe: 'gate' rows have 20 leading ones
+    plus sparse ones (every gate pre-activation is an integer >= 20 for
+    activations in {1, 2}); 'up' and 'down' are sparse -1/0/1."""
+    if kind == "gate":
+        q = (rng.random((rows, cols)) < 0.05).astype(np.int8)
+        q[:, :20] = 1
+    else:
+        q = rng.choice(np.array([-1, 0, 1], np.int8), size=(rows, cols), p=[0.02, 0.96, 0.02])
+    return q
+
+
+@pytest.mark.parametrize("E,k,T,shared", [(6, 2, 9, True),      # narrow decode tiles
+                                          (3, 2, 40, False),    # wide decode tiles
+                                          (2, 2, 80, True)])    # prefill MFMA kernel
+def test_ffn_exact_integer_probe(E, k, T, shared):
+    """Activations in {1, 2}, integer codes and unit scales keep every gate and
+    up dot product, h = silu(g) * u (silu(g) = g exactly in fp32 for g >= 20)
+    and the down projection integers below 2048, so fp32 accumulation and the
+    fp16 outputs are exact: the GPU must return integers equal to the oracle
+    up to the oracle's own float64 silu (relative 1e-8), far inside the usual
+    bound."""
+    H, F, Fs = 128, 128, 128 if shared else 0
+    cfg = get_config("tiny", num_experts=E, hidden=H, ffn=F, top_k=k, shared_ffn=Fs)
+    rng = np.random.default_rng(E * 100 + T)
+    one = lambda rows, cols: np.ones((rows, cols // 128), np.float16)  # noqa: E731
+    mats = {n: [] for n in ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s")}
+    experts = []
+    for e in range(E):
+        tup = []
+        for name, (rows, cols) in (("gate", (F, H)), ("up", (F, H)), ("down", (H, F))):
+            p, s = O.pack_w4(_probe_codes(rng, rows, cols, name)), O.pack_scales(one(rows, cols))
+            mats[name + "_q"].append(p)
+            mats[name + "_s"].append(s)
+            tup += [p, s]
+        experts.append(tuple(tup))
+    mats = {n: np.stack(v) for n, v in mats.items()}
+    sh = None
+    if shared:
+        sh = tuple(_probe_codes(rng, r, c, kind).astype(np.float16)
+                   for kind, (r, c) in (("gate", (Fs, H)), ("up", (Fs, H)), ("down", (H, Fs))))
+    x = rng.integers(1, 3, size=(T, H)).astype(np.float16)
+    idx = np.stack([(np.arange(T) + j) % E for j in range(k)], axis=1).astype(np.int32)
+    off, perm_src, inv_pos = O.permute(idx, E)
+    x_perm = O.gather_rows(x, perm_src, k)
+    wr = np.zeros((E, H), np.float16)
+    layer = make_gpu_layer(cfg, mats, wr, None, sh)
+    buf = layer.alloc(T)
+    buf.offsets.copy_(to_dev(off))
+    buf.perm_src.copy_(to_dev(perm_src))
+    layer.ffn(to_dev(x), buf, T)
+    torch.cuda.synchronize()
+    y = _np(buf.y_perm).astype(np.float64)
+    assert (y == np.rint(y)).all() and np.abs(y).max() < 2048
+    for e in range(E):
+        a, bnd = int(off[e]), int(off[e + 1])
+        if bnd > a:
+            ref = O.expert_ffn_w4(x_perm[a:bnd], *experts[e])
+            assert np.abs(ref).max() > 10          # a non-trivial probe
+            np.testing.assert_allclose(y[a:bnd], ref, rtol=1e-8, atol=1e-6)
+    if shared:
+        ys = _np(buf.y_shared).astype(np.float64)
+        ref = O.swiglu_ffn(x, *sh)
+        assert (ys == np.rint(ys)).all()
+        np.testing.assert_allclose(ys, ref, rtol=1e-8, atol=1e-6)
