@@ -21,6 +21,9 @@ call measured by rocprofv3 counters
 turned into bytes with --summarize-traffic), or null when the FFN sources
 have changed since.
 
+`step_ms_p10_p50_p90`: percentiles of single steps timed one by one with an
+event pair each, after the timed region (the events add their own cost).
+
 `cpu_baseline` times the float64 oracle (test infrastructure, run only in
 this leg) on a bounded sample of the same workload on the host cores.
 """
@@ -381,6 +384,20 @@ def main():
     torch.cuda.synchronize()
     ffn_ms_mean = f_start.elapsed_time(f_end) / K
     del ffn_bufs
+
+    # Spread of single steps: a third loop with an event pair around each
+    # step (event processing adds to each figure; the headline is the
+    # timed region above, which has no events inside)
+    n_single = min(K, 200)
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(n_single)]
+    torch.cuda.synchronize()
+    for i in range(n_single):
+        pairs[i][0].record(stream)
+        step(i)
+        pairs[i][1].record(stream)
+    torch.cuda.synchronize()
+    single_ms = np.array([a.elapsed_time(b) for a, b in pairs])
     ffn_bytes = np.array([bytes_per_combo[i % n_combo] for i in range(K)], dtype=np.float64)
     achieved_gbs = float(ffn_bytes.mean() / (ffn_ms_mean * 1e-3) / 1e9)
     tokens_per_s = T * K / (ms_total * 1e-3)
@@ -445,6 +462,7 @@ def main():
         },
         "roofline": roofline,
         "wall_s_timed": wall,
+        "step_ms_p10_p50_p90": [float(np.percentile(single_ms, q)) for q in (10, 50, 90)],
         "cpu_baseline": cpu,
     }
     print(json.dumps(res))
