@@ -42,7 +42,7 @@ def test_traffic_counts_the_ffn_dispatches_only(tmp_path):
     cal = [(copy, 1 << 20, 262144.0)] * 3
     fetch = small + cal + [(g1, 1096, 130.0), (g1, 1096, 134.0), (g2, 500, 60.0),
                            (g2, 500, 62.0),
-                           ("void moe::route_permute_kernel(moe::FusedRouteArgs)", 72, 9.0)]
+                           ("void moe::route_permute_kernel<5>(moe::FusedRouteArgs)", 72, 9.0)]
     write = small + [(copy, 1 << 20, 524288.0)] * 3 + [(g1, 1096, 2.0), (g2, 500, 4.0)]
     fp, wp = tmp_path / "f.csv", tmp_path / "w.csv"
     _csv(fp, "FETCH_SIZE", fetch)

@@ -87,22 +87,21 @@ __device__ __forceinline__ void wave_softmax_topk(GetE get_expert, int E, int k,
   }
 }
 
-// Instantiate for the number of logits each lane holds (1..16, E <= 1024).
-template <class GetE>
-__device__ __forceinline__ void wave_softmax_topk_any(GetE get_expert, int E, int k,
-                                                      int32_t *idx_out, float *w_out,
-                                                      int *lds_idx) {
-  switch ((E + kWave - 1) / kWave) {
-#define MOE_TOPK_CASE(n) \
-    case n: wave_softmax_topk<n>(get_expert, E, k, idx_out, w_out, lds_idx); break;
-    MOE_TOPK_CASE(1) MOE_TOPK_CASE(2) MOE_TOPK_CASE(3) MOE_TOPK_CASE(4)
-    MOE_TOPK_CASE(5) MOE_TOPK_CASE(6) MOE_TOPK_CASE(7) MOE_TOPK_CASE(8)
-    MOE_TOPK_CASE(9) MOE_TOPK_CASE(10) MOE_TOPK_CASE(11) MOE_TOPK_CASE(12)
-    MOE_TOPK_CASE(13) MOE_TOPK_CASE(14) MOE_TOPK_CASE(15) MOE_TOPK_CASE(16)
-#undef MOE_TOPK_CASE
-    default: break;
+// The kernels that run it are instantiated per number of logits per lane
+// (NPER = ceil(E / 64), 1..16 for E <= 1024) and the host launches the one
+// that fits: a kernel holding all sixteen variants behind a switch measured
+// 1.6 us slower per call at 8 tokens (its cold tail runs once per launch).
+#define MOE_NPER_SWITCH(E, CASE)                                            \
+  switch (((E) + kWave - 1) / kWave) {                                      \
+    case 1: CASE(1); break;   case 2: CASE(2); break;                       \
+    case 3: CASE(3); break;   case 4: CASE(4); break;                       \
+    case 5: CASE(5); break;   case 6: CASE(6); break;                       \
+    case 7: CASE(7); break;   case 8: CASE(8); break;                       \
+    case 9: CASE(9); break;   case 10: CASE(10); break;                     \
+    case 11: CASE(11); break; case 12: CASE(12); break;                     \
+    case 13: CASE(13); break; case 14: CASE(14); break;                     \
+    case 15: CASE(15); break; default: CASE(16); break;                     \
   }
-}
 
 // ------------------------------------------------------------ any batch size
 // logits[t][e] = x[t] . Wr[e] + b[e].  One block per (16-token tile,
@@ -254,6 +253,7 @@ __global__ __launch_bounds__(256) void router_logits_wide_kernel(const f16 *__re
 }
 
 // One wave per token, 4 tokens per block.
+template <int NPER>
 __global__ __launch_bounds__(256) void softmax_topk_kernel(const float *__restrict__ logits,
                                                            int T, int E, int k,
                                                            int32_t *__restrict__ idx,
@@ -261,8 +261,8 @@ __global__ __launch_bounds__(256) void softmax_topk_kernel(const float *__restri
   const int t = blockIdx.x * 4 + threadIdx.x / kWave;
   if (t >= T) return;
   const float *lt = logits + (size_t)t * E;
-  wave_softmax_topk_any([&](int e) { return lt[e]; }, E, k, idx + (size_t)t * k,
-                        w + (size_t)t * k, nullptr);
+  wave_softmax_topk<NPER>([&](int e) { return lt[e]; }, E, k, idx + (size_t)t * k,
+                          w + (size_t)t * k, nullptr);
 }
 
 // ------------------------------------------------------------ decode batches
@@ -288,6 +288,7 @@ struct FusedRouteArgs {
   int32_t *inv_pos;              // [T*k]
 };
 
+template <int NPER>
 __global__ __launch_bounds__(kFusedWaves * kWave) void route_permute_kernel(FusedRouteArgs p) {
   __shared__ float red[(kFusedWaves - 1) * 4 * kWave];
   __shared__ int s_idx[kFusedMaxT * 32];
@@ -408,7 +409,7 @@ __global__ __launch_bounds__(kFusedWaves * kWave) void route_permute_kernel(Fuse
   // softmax + top-k, one wave per token
   for (int t = wid; t < T; t += kFusedWaves) {
     const float *lt = s_logit + t * E;
-    wave_softmax_topk_any([&](int e) { return lt[e]; }, E, k, p.idx + (size_t)t * k,
+    wave_softmax_topk<NPER>([&](int e) { return lt[e]; }, E, k, p.idx + (size_t)t * k,
                           p.w + (size_t)t * k, s_idx + t * k);
   }
   for (int e = tid; e < E; e += blockDim.x) s_cnt[e] = 0;
@@ -483,8 +484,11 @@ hipError_t launch_route(const moe_layer &L, const uint16_t *x, int32_t T, int32_
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(softmax_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, st, logits, T, E,
-                     L.top_k, idx, w);
+#define MOE_TOPK_LAUNCH(n)                                                             \
+  hipLaunchKernelGGL(softmax_topk_kernel<n>, dim3((T + 3) / 4), dim3(256), 0, st, logits, T, \
+                     E, L.top_k, idx, w)
+  MOE_NPER_SWITCH(E, MOE_TOPK_LAUNCH)
+#undef MOE_TOPK_LAUNCH
   return hipGetLastError();
 }
 
@@ -501,7 +505,10 @@ hipError_t launch_route_permute_fused(const moe_layer &L, const uint16_t *x, int
   a.partial = partial; a.counter = counter;
   a.idx = idx; a.w = w; a.offsets = offsets; a.perm_src = perm_src; a.inv_pos = inv_pos;
   const int blocks = ((T + 15) / 16) * ((a.E + 15) / 16) * a.ksb;
-  hipLaunchKernelGGL(route_permute_kernel, dim3(blocks), dim3(kFusedWaves * kWave), 0, st, a);
+#define MOE_FUSED_LAUNCH(n) \
+  hipLaunchKernelGGL(route_permute_kernel<n>, dim3(blocks), dim3(kFusedWaves * kWave), 0, st, a)
+  MOE_NPER_SWITCH(a.E, MOE_FUSED_LAUNCH)
+#undef MOE_FUSED_LAUNCH
   return hipGetLastError();
 }
 
