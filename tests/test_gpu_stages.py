@@ -239,6 +239,34 @@ def test_route_permute_fused(name, over, T):
         assert _np(buf.x_perm).tobytes() == O.gather_rows(x, perm_src, cfg.top_k).tobytes()
 
 
+@pytest.mark.parametrize("nper", range(1, 17))
+def test_topk_every_lane_count(nper):
+    """Both top-k kernels (moe_route's and the one-launch moe_route_permute's)
+    exist once per number of logits per lane, ceil(E / 64) = 1 .. 16: an
+    expert count with a ragged last 64 for each, against the oracle."""
+    E = 64 * nper - (13 * nper) % 64
+    cfg = get_config("tiny", num_experts=E, top_k=min(8 + nper, E), hidden=256)
+    wr, b = G.router(cfg)
+    layer = _router_only_layer(cfg, wr, b)
+    for T, fused in ((5, False), (6, True)):
+        x = G.activations(cfg, tokens=T, batch=40 + nper)
+        idx_ref, w_ref, l_ref = O.route(x, wr, b, cfg.top_k)
+        buf = layer.alloc(T)
+        if fused:
+            layer.route_permute(to_dev(x), buf, T, gather=True)
+        else:
+            layer.route(to_dev(x), buf, T)
+        torch.cuda.synchronize()
+        idx = _np(buf.topk_idx)
+        diff = route_compare(idx, idx_ref, l_ref, cfg.top_k)
+        tol_check(_np(buf.topk_w)[~diff], w_ref[~diff], "topk_w", rel=1e-5, abs_=1e-7)
+        if fused:
+            off, perm_src, inv_pos = O.permute(idx, E)
+            np.testing.assert_array_equal(_np(buf.offsets), off)
+            np.testing.assert_array_equal(_np(buf.perm_src), perm_src)
+            np.testing.assert_array_equal(_np(buf.inv_pos), inv_pos)
+
+
 # ---------------------------------------------------------------- FFN
 FFN_CASES = [
     ("tiny", {}, 16, 0, False),
