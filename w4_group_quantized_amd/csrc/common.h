@@ -163,6 +163,8 @@ constexpr int kDppXor1 = 0xB1;          // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;          // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;   // row_half_mirror
 constexpr int kDppMirror = 0x140;       // row_mirror
+constexpr int kDppRowBcast15 = 0x142;   // row_bcast:15 (lane 15 of the previous row)
+constexpr int kDppRowBcast31 = 0x143;   // row_bcast:31 (lane 31, into rows 2 and 3)
 
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
@@ -197,15 +199,21 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return r;
 }
 
+// Every lane holds its 16-lane row's maximum after the first four steps;
+// row_bcast:15 then folds row 0 into row 1 and row 2 into row 3 (row mask
+// 0b1010), row_bcast:31 folds lane 31 (rows 0-1) into rows 2 and 3 (row mask
+// 0b1100), so lane 63 holds the wave's maximum: one read-lane instead of four.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   v = max(v, dpp_u32<kDppXor1>(v));
   v = max(v, dpp_u32<kDppXor2>(v));
   v = max(v, dpp_u32<kDppHalfMirror>(v));
   v = max(v, dpp_u32<kDppMirror>(v));
-  uint32_t r = __builtin_amdgcn_readlane(v, 0);
-#pragma unroll
-  for (int row = 1; row < 4; ++row) r = max(r, (uint32_t)__builtin_amdgcn_readlane(v, row * 16));
-  return r;
+  // rows outside the row mask keep v (the "old" operand): max(v, v) = v
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, kDppRowBcast15, 0xA, 0xF,
+                                                   false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, kDppRowBcast31, 0xC, 0xF,
+                                                   false));
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 // max that propagates NaN
