@@ -88,7 +88,7 @@ __device__ __forceinline__ void w4_load(W4Stage<NT, S> &st, const A &a,
     const int gg = min(g + i, G - 1);   // past the end: reload the last group (never used)
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      st.q[i][t] = ld16(qrow[t] + (size_t)gg * 1024);
+      st.q[i][t] = ld16_stream(qrow[t] + (size_t)gg * 1024);   // 1 KB: 8 whole lines
       st.s[i][t] = srow[t][(size_t)scale_group<GM>(gg) * 16];
     }
     if (!A::kDeferred) {
@@ -253,8 +253,8 @@ __device__ __forceinline__ void w8_load(W8Stage<NT> &st, const ARows &arow,
   for (int m = 0; m < 4; ++m) st.x[m] = arow.load(gg, m);
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    st.q[t][0] = ld16(qrow[t] + (size_t)gg * 2048);
-    st.q[t][1] = ld16(qrow[t] + (size_t)gg * 2048 + 256);
+    st.q[t][0] = ld16_stream(qrow[t] + (size_t)gg * 2048);   // whole lines each
+    st.q[t][1] = ld16_stream(qrow[t] + (size_t)gg * 2048 + 256);
     st.s[t] = srow[t][(size_t)gg * 16];
   }
 }
