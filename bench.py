@@ -1,21 +1,28 @@
 """Benchmark of the W4 g128 sparse-MoE layer on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload decode_fine]
+    python bench.py [--steps K] [--warmup W] [--workload decode_stack]
 
-A step is one full layer forward (moe_layer_forward: route + permute ->
-grouped W4 FFN -> combine) over one batch of synthetic tokens already
-resident in HBM.  Several
-independently drawn weight sets are rotated so that no expert byte is served
-from the 256 MB Infinity Cache across steps.  Prints ONE JSON line.
+A step is one forward of the workload (moe_layer_forward per layer: route +
+permute -> grouped W4 FFN -> combine) over one batch of synthetic tokens
+already resident in HBM; by default the largest configuration, the decode
+step through 42 stacked layers (288 experts + 1 shared, hidden 4096, ffn
+1536, top-8, 16 tokens, RMS norm between layers, 119 GB of weights).  The
+single-layer workloads rotate several independently drawn weight sets so
+that no expert byte is served from the 256 MB Infinity Cache across steps.
+Prints ONE JSON line.
 
 `roofline` is for the dominant stage, the grouped FFN (one
 moe_w4_grouped_ffn call: two launches, gate/up then down): decode: algorithmic
 bytes = distinct experts with tokens in the step x bytes per expert (packed
 int4 + fp16 scales) + the fp16 shared expert; prefill: algorithmic FLOPs =
 6*H*F per (token, chosen expert) pair; divided by the stage's average
-duration: K FFN calls with the steps' weight sets, batches and routing, run
-back to back on the launch stream between one pair of HIP events (so no
-event-processing gaps land on the kernels).  `traffic` is the HBM bytes per
+duration: the FFN calls of the steps' layers (weight sets, layer inputs and
+routing recorded in one untimed pass), K per layer of a step, run back to
+back on the launch stream between one pair of HIP events (so no
+event-processing gaps land on the kernels).  `layer_achieved` / `layer_frac`
+put the whole step on the same roofline: the algorithmic bytes of every
+layer of the step (each counted from its own offsets) over the mean step
+time of the timed region.  `traffic` is the HBM bytes per
 call measured by rocprofv3 counters
 (profiles/traffic_<workload>.json, taken with --copy-calibration-mib and
 turned into bytes with --summarize-traffic), or null when the FFN sources
@@ -54,7 +61,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--workload", default="decode_fine",
+    ap.add_argument("--workload", default="decode_stack",
                     choices=["decode_fine", "decode_coarse", "prefill", "decode_stack",
                              "decode_fine512", "tiny"])
     ap.add_argument("--group-size", type=int, default=128, choices=[64, 128, 256],
@@ -327,19 +334,38 @@ def main():
                 layer.forward(x, bufs, T, rmsnorm=True, eps=cfg.rms_eps, out=nxt)
                 x = nxt
 
-    # algorithmic bytes of the FFN stage per (weight set, batch) combination,
-    # counted from the offsets each combination produces (first layer)
-    bytes_per_combo = []
-    u_per_combo = []
+    # One untimed pass per (weight set, batch) combination that keeps every
+    # layer's input and routing: the algorithmic expert bytes of each layer
+    # are counted from that layer's own offsets, and the FFN-only loop below
+    # replays the FFN calls of exactly these layers.
+    def routing_buffers():
+        return dataclasses.replace(bufs, topk_idx=torch.empty_like(bufs.topk_idx),
+                                   topk_w=torch.empty_like(bufs.topk_w),
+                                   offsets=torch.empty_like(bufs.offsets),
+                                   perm_src=torch.empty_like(bufs.perm_src),
+                                   inv_pos=torch.empty_like(bufs.inv_pos))
+
+    plans = []          # per combination: [(layer, layer input, routing buffers)]
+    layer_bytes = []    # per combination: expert bytes of each layer
+    layer_u = []        # per combination: distinct routed experts of each layer
     for c in range(n_combo):
-        layer = sets[c % n_sets][0]
         x = xs[(c // n_sets) % args.batches]
-        layer.route_permute(x, bufs, T)
-        torch.cuda.synchronize()
-        cnt = np.diff(bufs.offsets.cpu().numpy())
-        U = int((cnt > 0).sum())
-        u_per_combo.append(U)
-        bytes_per_combo.append(U * cfg.expert_bytes() + cfg.shared_bytes())
+        plan, lb, lu = [], [], []
+        for li, layer in enumerate(sets[c % n_sets]):
+            x_in = x.clone()
+            b = routing_buffers()
+            nxt = torch.empty_like(x_in)
+            layer.forward(x_in, b, T, rmsnorm=layers_per_step > 1, eps=cfg.rms_eps, out=nxt)
+            torch.cuda.synchronize()
+            U = int((np.diff(b.offsets.cpu().numpy()) > 0).sum())
+            plan.append((layer, x_in, b))
+            lu.append(U)
+            lb.append(U * cfg.expert_bytes() + cfg.shared_bytes())
+            x = nxt
+        plans.append(plan)
+        layer_bytes.append(lb)
+        layer_u.append(lu)
+    step_bytes = [float(sum(lb)) for lb in layer_bytes]
 
     for i in range(args.warmup):
         step(i)
@@ -359,31 +385,26 @@ def main():
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / K
 
-    # The FFN stage alone: the same K calls (same weight sets, batches and
-    # routing as the steps) back to back between one pair of events, so that
-    # the per-call figure carries no event-processing gaps.
-    ffn_bufs = []
-    for c in range(n_combo):   # own routing per combination; outputs and workspace shared
-        b = dataclasses.replace(bufs, topk_idx=torch.empty_like(bufs.topk_idx),
-                                topk_w=torch.empty_like(bufs.topk_w),
-                                offsets=torch.empty_like(bufs.offsets),
-                                perm_src=torch.empty_like(bufs.perm_src),
-                                inv_pos=torch.empty_like(bufs.inv_pos))
-        sets[c % n_sets][0].route_permute(xs[(c // n_sets) % args.batches], b, T)
-        ffn_bufs.append(b)
-    for i in range(min(args.warmup, n_combo)):
-        sets[i % n_sets][0].ffn(xs[(i // n_sets) % args.batches], ffn_bufs[i % n_combo], T)
+    # The FFN stage alone: the FFN calls of the steps' layers (their weight
+    # sets, inputs and routing, every layer of the stack in turn), back to
+    # back between one pair of events, so that the per-call figure carries no
+    # event-processing gaps.  K * layers_per_step calls.
+    calls = [(pl, lb) for plan, lbs in zip(plans, layer_bytes) for pl, lb in zip(plan, lbs)]
+    n_ffn = K * layers_per_step
+    for i in range(min(args.warmup * layers_per_step, len(calls))):
+        (layer, x_in, b), _ = calls[i % len(calls)]
+        layer.ffn(x_in, b, T)
     f_start = torch.cuda.Event(enable_timing=True)
     f_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     f_start.record(stream)
-    for i in range(K):
-        c = i % n_combo
-        sets[c % n_sets][0].ffn(xs[(c // n_sets) % args.batches], ffn_bufs[c], T)
+    for i in range(n_ffn):
+        (layer, x_in, b), _ = calls[i % len(calls)]
+        layer.ffn(x_in, b, T)
     f_end.record(stream)
     torch.cuda.synchronize()
-    ffn_ms_mean = f_start.elapsed_time(f_end) / K
-    del ffn_bufs
+    ffn_ms_mean = f_start.elapsed_time(f_end) / n_ffn
+    ffn_bytes = np.array([calls[i % len(calls)][1] for i in range(n_ffn)], dtype=np.float64)
 
     # Spread of single steps: a third loop with an event pair around each
     # step (event processing adds to each figure; the headline is the
@@ -398,7 +419,6 @@ def main():
         pairs[i][1].record(stream)
     torch.cuda.synchronize()
     single_ms = np.array([a.elapsed_time(b) for a, b in pairs])
-    ffn_bytes = np.array([bytes_per_combo[i % n_combo] for i in range(K)], dtype=np.float64)
     achieved_gbs = float(ffn_bytes.mean() / (ffn_ms_mean * 1e-3) / 1e9)
     tokens_per_s = T * K / (ms_total * 1e-3)
     # algorithmic FFN FLOPs: every (token, chosen expert) pair costs 6*H*F
@@ -413,7 +433,21 @@ def main():
     else:
         roofline = {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic}
-    roofline.update({"kernel": "moe_w4_grouped_ffn (gate/up launch + down launch)",
+    # the whole step against the same roofline: every layer's algorithmic
+    # expert bytes (decode) or FLOPs (prefill) over the mean step time of the
+    # timed region, route, permutation and combine included
+    mean_step_bytes = float(np.mean([step_bytes[i % n_combo] for i in range(K)]))
+    layer_gbs = mean_step_bytes / (ms_step * 1e-3) / 1e9
+    layer_tflops = ffn_flops * layers_per_step / (ms_step * 1e-3) / 1e12
+    if cfg.name == "prefill":
+        roofline.update({"layer_achieved": layer_tflops,
+                         "layer_frac": layer_tflops / MFMA_F16_PEAK_TFLOPS})
+    else:
+        roofline.update({"layer_achieved": layer_gbs, "layer_frac": layer_gbs / HBM_PEAK_GBS})
+    roofline.update({"layer_scope": (f"whole step ({layers_per_step} layer(s): route, permute, "
+                                     "FFN, combine) in the timed region"),
+                     "step_expert_bytes_mean": mean_step_bytes,
+                     "kernel": "moe_w4_grouped_ffn (gate/up launch + down launch)",
                      "ffn_us_mean": float(ffn_ms_mean * 1e3),
                      "ffn_bytes_mean": float(ffn_bytes.mean()), "ffn_flops": ffn_flops,
                      "ffn_tflops": achieved_tflops, "ffn_gbs": achieved_gbs})
@@ -458,7 +492,7 @@ def main():
             "group_size": cfg.group_size, "shared_bits": cfg.shared_bits,
             "weights": (f"int4 g{cfg.group_size} (fp16 scales), router fp16, shared expert "
                         + ("fp16" if cfg.shared_bits == 16 else "8-bit g128")),
-            "distinct_experts_per_step_mean": float(np.mean(u_per_combo)),
+            "distinct_experts_per_layer_mean": float(np.mean(layer_u)),
         },
         "roofline": roofline,
         "wall_s_timed": wall,

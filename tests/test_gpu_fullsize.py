@@ -1,10 +1,16 @@
 """Full-size parity in the launch configuration the benchmark times
-(moe_route_permute -> moe_w4_grouped_ffn reading rows through perm_src ->
-moe_unpermute_combine), against the float64 oracle on sampled tokens (every
-token of the decode workloads).  Tokens are independent in an MoE layer, so
-sampled outputs are checked exactly as in a full run.  Expert weights are
-packed codes + scales drawn directly on the device; the oracle reads back the
-experts it needs and evaluates them with the C reference products."""
+(moe_layer_forward: the one-launch router and permutation for decode
+batches, the grouped FFN reading rows through perm_src, the combine),
+against the float64 oracle.
+
+Expert weights are packed codes + scales drawn on the device with the law of
+quantized N(0, sigma) weights (workloads.gen_torch); the oracle reads back the
+experts it needs and evaluates them with the C reference products (decode) or
+numpy (whole prefill segments).  Top-k indices must equal the oracle's except
+at reported ties (oracle.tie_excused); outputs are then compared against the
+oracle evaluated on the GPU's own selection, so no token is skipped.
+"""
+
 import numpy as np
 import pytest
 import torch
@@ -56,9 +62,10 @@ class DeviceExperts:
         return self.cache[e]
 
 
-def oracle_tokens(x64, wr, b, k, experts, shared):
-    """Float64 layer output for the given token rows (token-independent)."""
-    idx, w, logits = O.route(x64, wr, b, k)
+def oracle_tokens(x64, wr, b, k, experts, shared, idx=None):
+    """Float64 layer output for the given token rows (tokens are independent
+    in an MoE layer), optionally on a given selection idx [n, k]."""
+    idx, w, logits = O.route(x64, wr, b, k, idx=idx)
     out = O.swiglu_ffn(x64, *shared) if shared is not None else np.zeros((x64.shape[0], wr.shape[1]))
     for e in np.unique(idx):
         rows, slots = np.nonzero(idx == e)
@@ -67,8 +74,17 @@ def oracle_tokens(x64, wr, b, k, experts, shared):
     return out, idx, logits
 
 
+def checked_tokens(x64, wr, b, k, experts, shared, idx_gpu):
+    """The oracle's selection, then the GPU's checked against it under the
+    tie rule; the output of the oracle on the GPU's selection."""
+    logits = O.router_logits(x64, wr, b)
+    route_compare(idx_gpu, logits, k)
+    out, _, _ = oracle_tokens(x64, wr, b, k, experts, shared, idx=idx_gpu)
+    return out
+
+
 @pytest.mark.parametrize("name,n_sample", [("decode_fine", None), ("decode_coarse", None),
-                                           ("prefill", 48), ("decode_fine512", None)])
+                                           ("prefill", 256), ("decode_fine512", None)])
 def test_full_size_layer(name, n_sample):
     cfg = get_config(name)
     layer, mats, wr, b, shared = device_layer(cfg)
@@ -89,44 +105,90 @@ def test_full_size_layer(name, n_sample):
     else:
         toks = np.unique(np.concatenate([[0, T - 1],
                                          np.random.default_rng(5).choice(T, n_sample, False)]))
-    ref, idx_ref, logits = oracle_tokens(x[toks].astype(np.float64), wr, b, cfg.top_k,
-                                         DeviceExperts(mats), shared)
-    diff = route_compare(idx_gpu[toks], idx_ref, logits, cfg.top_k)
-    ok = ~diff
-    err, bound = tol_check(out[toks][ok], ref[ok], f"{name} full-size output")
-    print(f"[{name}] tokens checked {int(ok.sum())}/{len(toks)}  max err {err:.3e} (bound {bound:.3e})")
+    ref = checked_tokens(x[toks].astype(np.float64), wr, b, cfg.top_k, DeviceExperts(mats),
+                         shared, idx_gpu[toks])
+    err, bound = tol_check(out[toks], ref, f"{name} full-size output")
+    print(f"[{name}] tokens checked {len(toks)}/{T}  max err {err:.3e} (bound {bound:.3e})")
+
+
+def test_full_size_prefill_whole_segments():
+    """The prefill layer at full shape (8192 tokens, 128 experts): every row
+    of the FFN stage's output y_perm for whole segments: the largest, the
+    smallest non-empty one, and the two whose last 128-row tile is the most
+    and the least ragged, against the numpy oracle's expert FFN on the same
+    rows."""
+    cfg = get_config("prefill")
+    layer, mats, wr, b, shared = device_layer(cfg)
+    T, k = cfg.tokens, cfg.top_k
+    x = G.activations(cfg, batch=0)
+    buf = layer.alloc(T)
+    layer.forward(torch.from_numpy(x).cuda(), buf)
+    torch.cuda.synchronize()
+    off = _np(buf.offsets).astype(np.int64)
+    perm_src = _np(buf.perm_src).astype(np.int64)
+    cnt = np.diff(off)
+    live = np.nonzero(cnt > 0)[0]
+    largest = int(live[np.argmax(cnt[live])])
+    smallest = int(live[np.argmin(cnt[live])])
+    long_ = [e for e in live if cnt[e] > 128 and cnt[e] % 128]
+    most_ragged = int(max(long_, key=lambda e: (cnt[e] % 128, -e)))
+    least_ragged = int(min(long_, key=lambda e: (cnt[e] % 128, e)))
+    experts = DeviceExperts(mats)
+    for what, e in (("largest", largest), ("smallest", smallest),
+                    ("tail most ragged", most_ragged), ("tail least ragged", least_ragged)):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        rows = x[perm_src[r0:r1] // k].astype(np.float64)
+        ref = O.expert_ffn_w4(rows, *experts[e], group=cfg.group_size)
+        got = _np(buf.y_perm[r0:r1]).astype(np.float64)
+        err, bound = tol_check(got, ref, f"segment {e} ({what}, {r1 - r0} rows)")
+        print(f"[prefill] {what} segment e={e}: {r1 - r0} rows (last tile {(r1 - r0) % 128 or 128}),"
+              f" max err {err:.3e} (bound {bound:.3e})", flush=True)
+        experts.cache.clear()
 
 
 def test_full_size_decode_stack():
-    """42 layers, RMS norm between them, on the device end to end; the oracle
-    follows two tokens through all layers in float64 (no fp16 rounding of the
-    activations).  A token whose routing meets a reported near tie on the way
-    is not compared after it (routing is discrete)."""
+    """42 layers, RMS norm between them, on the device end to end, all 16
+    tokens.  Per layer, teacher-forced: the oracle's layer i runs on the GPU's
+    fp16 input to layer i; its top-k must match under the tie rule and its
+    RMS-normalised output (evaluated on the GPU's selection) must match the
+    GPU's fp16 input to layer i+1 within the tolerance.  End to end: the
+    oracle also carries its own float64 activations through all 42 layers;
+    the final error is checked for the tokens whose routing never left the
+    oracle's, and the routing flips are reported."""
     cfg = get_config("decode_stack")
-    T = cfg.tokens
-    layers = [device_layer(cfg, l) for l in range(cfg.layers)]
+    T, k = cfg.tokens, cfg.top_k
+    layers = [device_layer(cfg, li) for li in range(cfg.layers)]
     x = G.activations(cfg, batch=0)
     xd = torch.from_numpy(x).cuda()
     buf = layers[0][0].alloc(T)
-    act = [torch.empty_like(xd), torch.empty_like(xd)]
-    cur = xd
+    acts = [xd] + [torch.empty_like(xd) for _ in range(cfg.layers)]
     idx_gpu = []
     for li, (layer, *_r) in enumerate(layers):
-        nxt = act[li % 2]
-        layer.forward(cur, buf, rmsnorm=True, eps=cfg.rms_eps, out=nxt)
+        layer.forward(acts[li], buf, rmsnorm=True, eps=cfg.rms_eps, out=acts[li + 1])
         idx_gpu.append(_np(buf.topk_idx).copy())
-        cur = nxt
-    out = _np(cur).astype(np.float64)
-    toks = np.array([0, T - 1])
-    x64 = x[toks].astype(np.float64)
-    alive = np.ones(len(toks), dtype=bool)
+    torch.cuda.synchronize()
+    acts = [_np(a).astype(np.float64) for a in acts]    # the GPU's fp16 layer inputs
+    x_e2e = x.astype(np.float64)                         # the oracle's own activations
+    alive = np.ones(T, dtype=bool)
+    flips = 0
+    worst = 0.0
     for li, (layer, mats, wr, b, shared) in enumerate(layers):
-        y, idx_ref, logits = oracle_tokens(x64, wr, b, cfg.top_k, DeviceExperts(mats), shared)
-        same = (idx_gpu[li][toks] == idx_ref).all(axis=1)
-        ties = O.near_ties(logits, cfg.top_k)
-        assert (same | ties | ~alive).all(), f"layer {li}: top-k differs away from a near tie"
+        experts = DeviceExperts(mats)
+        # teacher-forced: the oracle's layer on the GPU's fp16 input
+        y = checked_tokens(acts[li], wr, b, k, experts, shared, idx_gpu[li])
+        err, bound = tol_check(acts[li + 1], O.rmsnorm(y, cfg.rms_eps), f"layer {li}")
+        worst = max(worst, err / bound)
+        # end to end on the oracle's own activations and routing
+        y_e2e, idx_ref, _ = oracle_tokens(x_e2e, wr, b, k, experts, shared)
+        same = (idx_ref == idx_gpu[li]).all(axis=1)
+        flips += int((alive & ~same).sum())
         alive &= same
-        x64 = O.rmsnorm(y, cfg.rms_eps)
-    assert alive.any(), "every sampled token met a near tie"
-    err, bound = tol_check(out[toks][alive], x64[alive], "42-layer stack output")
-    print(f"[decode_stack] tokens {int(alive.sum())}/{len(toks)} max err {err:.3e} (bound {bound:.3e})")
+        x_e2e = O.rmsnorm(y_e2e, cfg.rms_eps)
+        print(f"[decode_stack] layer {li}: teacher-forced max err {err:.3e} (bound {bound:.3e})",
+              flush=True)
+        del experts
+    print(f"[decode_stack] per-layer worst err/bound {worst:.3f}; end to end: {flips} token(s) "
+          f"left the oracle's routing, {int(alive.sum())}/{T} followed it through all layers")
+    if alive.any():
+        err, bound = tol_check(acts[-1][alive], x_e2e[alive], "42-layer stack output")
+        print(f"[decode_stack] end-to-end max err {err:.3e} (bound {bound:.3e})")

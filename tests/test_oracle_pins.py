@@ -266,10 +266,60 @@ def test_route_duplicate_rows_tie_lower_index_wins():
     np.testing.assert_allclose(O.softmax(l).sum(1), 1.0, rtol=1e-14)
 
 
-def test_near_ties_flags_only_close_pairs():
-    l = np.array([[3.0, 1.0, 1.0 + 5e-7, -2.0], [3.0, 2.0, 1.0, 0.0]])
-    m = O.near_ties(l, 2)
-    assert m.tolist() == [True, False]
+def test_tie_excused_hand_cases():
+    """The reported-tie rule on hand-built logits: which position differs and
+    by how much decides, not whether some pair of the token is close."""
+    l = np.array([
+        [3.0, 1.0, 1.0 + 5e-7, -2.0],   # experts 2, 1 within 5e-7
+        [3.0, 1.0, 1.0 + 5e-7, -2.0],
+        [3.0, 1.0, 1.0 + 5e-7, -2.0],
+        [3.0, 2.0, 2.0 - 4e-7, 0.0],    # 1, 2 close: the k-th and (k+1)-th
+        [3.0, 2.0, 1.0, 0.0],
+        [3.0, 3.0 - 2e-6, 1.0, 0.0],    # 2e-6 apart: beyond the gap
+    ])
+    other = np.array([
+        [0, 2],   # the oracle's own order: no difference
+        [0, 1],   # 1 for 2 at position 1, 5e-7 apart: excused
+        [2, 0],   # 2 at position 0 where the oracle has 0: 2 apart, failed
+        [0, 2],   # boundary swap with the (k+1)-th expert, 4e-7 apart: excused
+        [0, 2],   # 2 for 1: 1 apart, failed
+        [1, 0],   # a swap 2e-6 apart: failed
+    ])
+    differs, excused = O.tie_excused(other, l)
+    assert differs.tolist() == [False, True, True, True, True, True]
+    assert excused.tolist() == [False, True, False, True, False, False]
+    # a close pair elsewhere in the list does not excuse a wrong expert at
+    # another position (the close pair is 2, 1; the mistake is 3 for 2)
+    l2 = np.array([[5.0, 4.0, 4.0 + 1e-7, 1.0, 0.0]])
+    d, e = O.tie_excused(np.array([[0, 2, 3]]), l2)
+    assert d.tolist() == [True] and e.tolist() == [False]
+    # a repeated or out-of-range expert is never excused
+    l3 = np.array([[1.0, 1.0, 0.0]])
+    assert O.tie_excused(np.array([[1, 1]]), l3)[1].tolist() == [False]
+    assert O.tie_excused(np.array([[1, 7]]), l3)[1].tolist() == [False]
+
+
+def test_route_on_a_given_selection():
+    """route(..., idx=sel) returns the softmax probabilities of the given
+    experts, computed here by explicit exp sums; with the oracle's own
+    selection it equals the unforced route."""
+    cfg = get_config("tiny", num_experts=6, hidden=128, top_k=3)
+    wr, b = G.router(cfg)
+    x = G.activations(cfg, tokens=4, batch=2)
+    idx0, w0, l0 = O.route(x, wr, b, 3)
+    idx1, w1, _ = O.route(x, wr, b, 3, idx=idx0)
+    assert (idx1 == idx0).all() and np.array_equal(w1, w0)
+    sel = np.array([[5, 0, 2], [1, 2, 3], [4, 3, 0], [0, 1, 5]])
+    idx2, w2, l2 = O.route(x, wr, b, 3, idx=sel)
+    assert (idx2 == sel).all()
+    for t in range(4):
+        den = math.fsum(math.exp(v) for v in l2[t])
+        for j in range(3):
+            assert abs(w2[t, j] - math.exp(l2[t, sel[t, j]]) / den) <= 1e-15
+    with pytest.raises(ValueError):
+        O.route(x, wr, b, 3, idx=np.array([[0, 0, 1]] * 4))
+    with pytest.raises(ValueError):
+        O.route(x, wr, b, 3, idx=np.array([[0, 6, 1]] * 4))
 
 
 # ---------------------------------------------------------------- permutation
@@ -356,6 +406,27 @@ def test_layer_equals_dense_all_experts_then_mask():
         mask = (res["idx"] == e).any(axis=1)
         dense += (p[:, e] * mask)[:, None] * Ye
     np.testing.assert_allclose(res["out"], dense, rtol=0, atol=1e-12 * np.abs(dense).max())
+
+
+def test_layer_on_a_given_selection_equals_dense_then_mask():
+    """The layer evaluated on a forced selection (the path used at a reported
+    near tie): every expert on every token, masked by the given selection and
+    weighted by its softmax probability."""
+    cfg = get_config("tiny")
+    x, wr, b, experts = _tiny_layer(cfg)
+    g = np.random.default_rng(11)
+    sel = np.stack([g.choice(cfg.num_experts, cfg.top_k, replace=False)
+                    for _ in range(cfg.tokens)])
+    res = O.moe_layer(x, wr, b, experts, cfg.top_k, idx=sel)
+    p = O.softmax(O.router_logits(x, wr, b))
+    dense = np.zeros((cfg.tokens, cfg.hidden))
+    for e in range(cfg.num_experts):
+        Ye = O.expert_ffn_w4(x, *experts[e])
+        mask = (sel == e).any(axis=1)
+        dense += (p[:, e] * mask)[:, None] * Ye
+    np.testing.assert_allclose(res["out"], dense, rtol=0, atol=1e-12 * np.abs(dense).max())
+    off, perm_src, _ = O.permute(sel, cfg.num_experts)
+    assert (res["offsets"] == off).all() and (res["perm_src"] == perm_src).all()
 
 
 def test_layer_special_cases():

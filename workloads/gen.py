@@ -91,17 +91,31 @@ def shared_expert(cfg: MoEConfig, layer: int = 0):
                  for m, shp in ((GATE, (Fs, H)), (UP, (Fs, H)), (DOWN, (H, Fs))))
 
 
-def expert_codes(cfg: MoEConfig, layer: int, expert: int, matrix: int):
-    """Packed int4 bytes and fp16 scales drawn directly (no quantizer).
+# Code distribution of int4-quantized N(0, sigma) weights: with 128-weight
+# groups and scale max|w|/7, the code of a weight is about w * 7 / max|w|; the
+# largest of 128 |N(0,1)| draws is 2.7 on average (2.2 .. 3.5 in practice),
+# so the codes are close to a normal with standard deviation 7 / 2.7 = 2.6,
+# rounded and clipped, and the scales about sigma * 2.7 / 7 (sigma * 0.33 .. 0.48).
+CODE_STD = 2.6
+SCALE_LO, SCALE_HI = 0.33, 0.48
 
-    Every byte value is equally likely, so all sixteen codes -8..7 occur;
-    scales are weight_std * U(0.15, 0.30), which keeps the dequantized
-    weights' spread near weight_std.  Used for full-size runs where drawing
-    and quantizing fp16 masters on the host would take too long.
+
+def expert_codes(cfg: MoEConfig, layer: int, expert: int, matrix: int):
+    """Packed int4 bytes and fp16 scales drawn directly (no quantizer), with
+    the distribution that quantizing N(0, weight_std) masters produces.
+
+    Each nibble is an independent draw u = clip(rint(CODE_STD * z), -7, 7) + 8
+    with z ~ N(0, 1); a byte holds two such nibbles.  Because every nibble is
+    drawn independently with the same law, the bytes have that law in any
+    storage layout.  Scales are weight_std * U(SCALE_LO, SCALE_HI).  Used
+    where drawing and quantizing fp16 masters on the host would take too long
+    (full-size parity, the CPU baseline).
     """
     out_dim, in_dim = matrix_shape(cfg, matrix)
     g = rng(cfg, T_CODES, layer=layer, expert=expert, matrix=matrix)
-    packed = g.integers(0, 256, size=(out_dim, in_dim // 2), dtype=np.uint8)
-    s = (cfg.weight_std * g.uniform(0.15, 0.30, size=(out_dim, in_dim // cfg.group_size))
-         ).astype(np.float16)
+    z = g.standard_normal((2, out_dim, in_dim // 2), dtype=np.float32)
+    u = (np.clip(np.rint(z * np.float32(CODE_STD)), -7, 7) + 8).astype(np.uint8)
+    packed = u[0] | (u[1] << 4)
+    s = (cfg.weight_std * g.uniform(SCALE_LO, SCALE_HI,
+                                    size=(out_dim, in_dim // cfg.group_size))).astype(np.float16)
     return packed, s
