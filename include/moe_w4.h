@@ -14,7 +14,9 @@
  *
  * moe_route_permute does the first two in one call (one launch for small
  * batches) and moe_layer_forward all four.  moe_w4_quantize and
- * moe_w8_quantize write the weight formats below from fp16 matrices.
+ * moe_w8_quantize write the weight formats below from fp16 matrices;
+ * moe_w4_pack writes the int4 format from codes that are already quantized
+ * and stored plainly (row-major, two's-complement nibbles).
  *
  * Sources: symmetric int4 group quantization with 128 weights per group along
  * in_features, scale = max|w| / 7, codes clamped to [-8, 7]: lpnh.cn/news/
@@ -147,6 +149,10 @@ size_t moe_workspace_size(const moe_layer *layer, int32_t max_tokens);
 /* Router: l[t][e] = sum_h x[t][h] * router_w[e][h] + router_b[e] (fp32
  * accumulation), p = softmax over e (fp32, max subtracted), then the k largest
  * logits in descending order, ties to the lower expert index.
+ * Defined by zwxr.cn/news/276292 §3.2 (routing engine: softmax over the
+ * expert logits, descending partial sort for the first k) and lpnh.cn/news/
+ * 2730718 §2.3 (softmax and top-k fused in one kernel); the tie order is this
+ * library's (the page's partial sort leaves ties open).
  *   x         fp16 [T, H]
  *   topk_idx  int32 [T, k]  out: chosen experts, best first
  *   topk_w    fp32  [T, k]  out: p of the chosen experts (not renormalised)
@@ -158,7 +164,10 @@ moe_status moe_route(const moe_layer *layer, const uint16_t *x, int32_t T,
 
 /* Permutation of the T*k (token, slot) pairs into per-expert segments.
  * Flat index f = t*k + j; segment e holds the f with topk_idx[f] = e in
- * increasing f.
+ * increasing f.  The tokens that chose an expert are gathered so that each
+ * expert runs once over all of them (xdnf.cn/news/329730 §3.2, grouped GEMM
+ * over the selected experts); the stable order inside a segment is this
+ * library's.
  *   x         fp16 [T, H] (read only when x_perm is not NULL)
  *   topk_idx  int32 [T, k], each in [0, E)
  *   offsets   int32 [E+1] out: segment e is rows offsets[e]..offsets[e+1]-1
@@ -185,7 +194,11 @@ moe_status moe_route_permute(const moe_layer *layer, const uint16_t *x, int32_t 
                              int32_t *perm_src, int32_t *inv_pos, uint16_t *x_perm,
                              void *ws, size_t ws_bytes, void *stream);
 
-/* Grouped SwiGLU FFN over the routed segments and the shared expert.
+/* Grouped SwiGLU FFN over the routed segments and the shared expert: one
+ * grouped GEMM over the selected experts' segments (xdnf.cn/news/329730 §3.2)
+ * with the int4 weights of lpnh.cn/news/2730718 §2.1 dequantized inside the
+ * kernel, gate / up / down matrices per expert (haowenji.com/articles/
+ * x-2109226022155796480 §01).
  * For each expert e and each row r of its segment, with a = x_perm[r], or
  * a = x[perm_src[r] / k] when x_perm is NULL:
  *   g = deq(gate_e) a,  u = deq(up_e) a          (fp32 accumulation)
@@ -199,7 +212,14 @@ moe_status moe_route_permute(const moe_layer *layer, const uint16_t *x, int32_t 
  *             MOE_EUNSUPPORTED);  offsets int32 [E+1] as written by moe_permute
  *             (offsets[0] = 0, non-decreasing, offsets[E] = T*k)
  *   y_perm    fp16 [T*k, H] out
- *   y_shared  fp16 [T, H] out, or NULL when shared_ffn = 0 */
+ *   y_shared  fp16 [T, H] out, or NULL when shared_ffn = 0
+ * Kernel choice (results meet the same definition either way): the matrix-
+ * core prefill kernels run the routed experts when T*k >= 32*E (segments of
+ * 32 rows or more on average), hidden % 256 == 0 and T*k*H*2, T*k*F*2 and
+ * F*H/2 are all below 2^31 (they address activations and one expert's
+ * weights with 32-bit offsets); otherwise the decode kernels do, which are
+ * correct at any size but read each expert's weights once per 16 rows of its
+ * segment, so a large batch outside those limits runs far slower. */
 moe_status moe_w4_grouped_ffn(const moe_layer *layer, const uint16_t *x,
                               const uint16_t *x_perm, const int32_t *perm_src,
                               const int32_t *offsets, int32_t T,
@@ -210,7 +230,10 @@ moe_status moe_w4_grouped_ffn(const moe_layer *layer, const uint16_t *x,
 #define MOE_RENORM 2u
 
 /* Combine: out[t] = y_shared[t] + sum_j topk_w[t][j] * y_perm[inv_pos[t*k+j]]
- * in fp32 (y_shared may be NULL: then that term is 0).  With flags &
+ * in fp32 (y_shared may be NULL: then that term is 0): the k routed experts'
+ * outputs weighted by their routing probabilities plus the always-on shared
+ * expert with weight 1 (haowenji.com/articles/x-2109226022155796480 §01,
+ * "8 routed + 1 shared" experts per token).  With flags &
  * MOE_RENORM each topk_w[t][j] is first divided by the sum of the token's k
  * weights (the chosen experts' probabilities rescaled to sum to 1; an option
  * beyond the pages, whose routing keeps the plain softmax probabilities).
@@ -259,6 +282,21 @@ moe_status moe_w4_dequant(const uint8_t *q, const uint16_t *s, int64_t rows,
  * of 16, cols multiple of 128 and of group_size. */
 moe_status moe_w4_quantize(const uint16_t *w, int64_t rows, int64_t cols,
                            int32_t group_size, uint8_t *q, uint16_t *s, void *stream);
+
+/* Codes that are already quantized, stored plainly, into the packed int4
+ * format above (the page's quantizer returns int8 codes [out, in] with fp16
+ * scales [out, in/group], lpnh.cn/news/2730718 §2.1; this call takes them
+ * two codes per byte):
+ *   q_rowmajor  [rows, cols/2] bytes, row-major; byte c/2 of a row holds
+ *               column c (c even) in bits 0-3 and column c+1 in bits 4-7, each
+ *               as a two's-complement nibble (codes -8..7)
+ *   s_rowmajor  fp16 [rows, cols/group_size], row-major
+ *   q, s        out: the packed format above (same byte and scale counts)
+ * Bit-exact: codes and scales are moved, not recomputed.  rows multiple of 16,
+ * cols multiple of 128 and of group_size (64, 128 or 256); MOE_EUNSUPPORTED
+ * otherwise.  Inputs and outputs must not overlap. */
+moe_status moe_w4_pack(const uint8_t *q_rowmajor, const uint16_t *s_rowmajor, int64_t rows,
+                       int64_t cols, int32_t group_size, uint8_t *q, uint16_t *s, void *stream);
 
 /* 8-bit group quantization of an fp16 matrix w [rows, cols] for the shared
  * expert (128-weight groups; xdnf.cn/news/329730 §3.1): the 4-bit steps of

@@ -34,32 +34,48 @@ def _load():
             build()
         lib = ctypes.CDLL(LIB)
         P, I64 = ctypes.c_void_p, ctypes.c_int64
-        lib.w4_matvec.argtypes = [P, P, I64, I64, P, I64, P]
-        lib.w4_dequant_rows.argtypes = [P, P, I64, I64, I64, P]
+        lib.w4_matvec.argtypes = [P, P, I64, I64, I64, P, I64, P]
+        lib.w4_matvec.restype = ctypes.c_int
+        lib.w4_dequant_rows.argtypes = [P, P, I64, I64, I64, I64, P]
+        lib.w4_dequant_rows.restype = ctypes.c_int
         _lib = lib
     return _lib
 
 
+def _group(q, s):
+    """Group size from the stored shapes: q [out, in/2], s [out, in/gs]."""
+    in_dim = q.shape[1] * 2
+    gs = in_dim // s.shape[1]
+    if gs not in (64, 128, 256) or gs * s.shape[1] != in_dim or s.shape[0] != q.shape[0]:
+        raise ValueError(f"scales {s.shape} do not fit codes {q.shape} with a group of 64/128/256")
+    return in_dim, gs
+
+
 def w4_matvec(q: np.ndarray, s: np.ndarray, x: np.ndarray) -> np.ndarray:
-    """y[t, n] = sum_c q[n, c] s[n, c // 128] x[t, c] in float64, from the
-    stored arrays q (uint8 [out, in/2]) and s (fp16 [out, in/128])."""
+    """y[t, n] = sum_c q[n, c] s[n, c // gs] x[t, c] in float64, from the
+    stored arrays q (uint8 [out, in/2]) and s (fp16 [out, in/gs]); the group
+    size gs (64, 128 or 256) follows from the shapes."""
     q = np.ascontiguousarray(q, dtype=np.uint8)
     s = np.ascontiguousarray(s, dtype=np.float16)
     x = np.ascontiguousarray(np.atleast_2d(x), dtype=np.float64)
-    out_dim, in_dim = q.shape[0], q.shape[1] * 2
-    assert x.shape[1] == in_dim and s.shape == (out_dim, in_dim // 128)
+    out_dim = q.shape[0]
+    in_dim, gs = _group(q, s)
+    assert x.shape[1] == in_dim
     y = np.empty((x.shape[0], out_dim), dtype=np.float64)
-    _load().w4_matvec(q.ctypes.data, s.ctypes.data, out_dim, in_dim, x.ctypes.data, x.shape[0],
-                      y.ctypes.data)
+    if _load().w4_matvec(q.ctypes.data, s.ctypes.data, out_dim, in_dim, gs, x.ctypes.data,
+                         x.shape[0], y.ctypes.data) != 0:
+        raise ValueError(f"shape [{out_dim}, {in_dim}] with group {gs} not supported")
     return y
 
 
 def dequant_rows(q: np.ndarray, s: np.ndarray, r0: int, r1: int) -> np.ndarray:
     q = np.ascontiguousarray(q, dtype=np.uint8)
     s = np.ascontiguousarray(s, dtype=np.float16)
-    in_dim = q.shape[1] * 2
+    in_dim, gs = _group(q, s)
     out = np.empty((r1 - r0, in_dim), dtype=np.float64)
-    _load().w4_dequant_rows(q.ctypes.data, s.ctypes.data, in_dim, r0, r1, out.ctypes.data)
+    if _load().w4_dequant_rows(q.ctypes.data, s.ctypes.data, in_dim, gs, r0, r1,
+                               out.ctypes.data) != 0:
+        raise ValueError(f"shape [*, {in_dim}] with group {gs} not supported")
     return out
 
 

@@ -152,6 +152,23 @@ def unpack_w4(packed: np.ndarray) -> np.ndarray:
     return (u - 8).reshape(p.shape[0], -1)
 
 
+def unpack_plain_w4(b: np.ndarray) -> np.ndarray:
+    """Plain int4 storage -> int8 codes [out, in].
+
+    The plain layout is row-major [out, in/2] bytes; byte c/2 of a row holds
+    column c (c even) in bits 0-3 and column c+1 in bits 4-7, each as a
+    two's-complement nibble (a plain packing of the page's int8 codes,
+    [P2] §2.1, two per byte; the library's own format is pack_w4's).
+    """
+    b = np.asarray(b, dtype=np.uint8)
+    lo = (b & 0x0F).astype(np.int16)
+    hi = (b >> 4).astype(np.int16)
+    q = np.empty((b.shape[0], 2 * b.shape[1]), dtype=np.int8)
+    q[:, 0::2] = np.where(lo >= 8, lo - 16, lo)
+    q[:, 1::2] = np.where(hi >= 8, hi - 16, hi)
+    return q
+
+
 def pack_w8(q: np.ndarray) -> np.ndarray:
     """int8 codes [out, in] -> stored bytes [out, in]: the offset-binary byte
     q + 128, rows in tiles of 16 with each 16-column chunk of the 16 rows side

@@ -189,3 +189,16 @@ def test_status_strings():
     for s in (OK, EINVAL, EUNSUP, EWS, -4):
         assert N.moe_status_str(s)
     assert "unknown" in N.moe_status_str(-99)
+
+
+def test_pack_arguments():
+    pack = N.lib.moe_w4_pack
+    assert pack(FAKE, FAKE, 16, 200, 128, FAKE, FAKE, None) == EUNSUP      # cols % 128
+    assert pack(FAKE, FAKE, 8, 256, 128, FAKE, FAKE, None) == EUNSUP       # rows % 16
+    assert pack(FAKE, FAKE, 16, 384, 256, FAKE, FAKE, None) == EUNSUP      # cols % group
+    assert pack(FAKE, FAKE, 16, 256, 32, FAKE, FAKE, None) == EUNSUP       # group size
+    assert pack(FAKE, FAKE, -16, 256, 128, FAKE, FAKE, None) == EINVAL
+    assert pack(None, FAKE, 16, 256, 128, FAKE, FAKE, None) == EINVAL
+    assert pack(FAKE, MISALIGNED, 16, 256, 128, FAKE, FAKE, None) == EINVAL
+    assert pack(FAKE, FAKE, 16, 256, 128, FAKE, None, None) == EINVAL
+    assert pack(None, None, 0, 256, 128, None, None, None) == OK            # nothing to do

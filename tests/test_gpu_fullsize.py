@@ -116,7 +116,8 @@ def test_full_size_prefill_whole_segments():
     of the FFN stage's output y_perm for whole segments: the largest, the
     smallest non-empty one, and the two whose last 128-row tile is the most
     and the least ragged, against the numpy oracle's expert FFN on the same
-    rows."""
+    rows; then segments of 1, 5 and 17 rows at the same shape (the layer's
+    routing with a few choices moved to otherwise unchosen experts)."""
     cfg = get_config("prefill")
     layer, mats, wr, b, shared = device_layer(cfg)
     T, k = cfg.tokens, cfg.top_k
@@ -144,6 +145,32 @@ def test_full_size_prefill_whole_segments():
         print(f"[prefill] {what} segment e={e}: {r1 - r0} rows (last tile {(r1 - r0) % 128 or 128}),"
               f" max err {err:.3e} (bound {bound:.3e})", flush=True)
         experts.cache.clear()
+    # Near-empty segments at the same shape: the layer's routing with the last
+    # choice of a few tokens moved to experts no token chose (segments of 1, 5
+    # and 17 rows), then the permutation and the FFN stage on that routing.
+    idx = _np(buf.topk_idx).copy()
+    dead = [int(e) for e in np.nonzero(cnt == 0)[0]]
+    assert len(dead) >= 3, "the prefill layer has experts no token chooses"
+    t0 = 0
+    for e, n in zip(dead, (1, 5, 17)):
+        idx[t0:t0 + n, k - 1] = e
+        t0 += n
+    xd = torch.from_numpy(x).cuda()
+    buf.topk_idx.copy_(torch.from_numpy(idx))
+    layer.permute(xd, buf, T, gather=False)
+    layer.ffn(xd, buf, T)
+    torch.cuda.synchronize()
+    off2, perm2, _ = O.permute(idx, cfg.num_experts)
+    np.testing.assert_array_equal(_np(buf.offsets), off2)
+    np.testing.assert_array_equal(_np(buf.perm_src), perm2)
+    for e, n in zip(dead, (1, 5, 17)):
+        r0, r1 = int(off2[e]), int(off2[e + 1])
+        assert r1 - r0 == n
+        rows = x[perm2[r0:r1].astype(np.int64) // k].astype(np.float64)
+        ref = O.expert_ffn_w4(rows, *experts[e], group=cfg.group_size)
+        err, bound = tol_check(_np(buf.y_perm[r0:r1]), ref, f"segment {e} ({n} rows)")
+        print(f"[prefill] near-empty segment e={e}: {n} rows, max err {err:.3e} "
+              f"(bound {bound:.3e})", flush=True)
 
 
 def test_full_size_decode_stack():
@@ -170,7 +197,7 @@ def test_full_size_decode_stack():
     acts = [_np(a).astype(np.float64) for a in acts]    # the GPU's fp16 layer inputs
     x_e2e = x.astype(np.float64)                         # the oracle's own activations
     alive = np.ones(T, dtype=bool)
-    flips = 0
+    left_at = np.full(T, -1)
     worst = 0.0
     for li, (layer, mats, wr, b, shared) in enumerate(layers):
         experts = DeviceExperts(mats)
@@ -181,14 +208,16 @@ def test_full_size_decode_stack():
         # end to end on the oracle's own activations and routing
         y_e2e, idx_ref, _ = oracle_tokens(x_e2e, wr, b, k, experts, shared)
         same = (idx_ref == idx_gpu[li]).all(axis=1)
-        flips += int((alive & ~same).sum())
+        left_at[alive & ~same] = li
         alive &= same
         x_e2e = O.rmsnorm(y_e2e, cfg.rms_eps)
         print(f"[decode_stack] layer {li}: teacher-forced max err {err:.3e} (bound {bound:.3e})",
               flush=True)
         del experts
-    print(f"[decode_stack] per-layer worst err/bound {worst:.3f}; end to end: {flips} token(s) "
-          f"left the oracle's routing, {int(alive.sum())}/{T} followed it through all layers")
+    print(f"[decode_stack] per-layer worst err/bound {worst:.3f}; end to end: "
+          f"{int((~alive).sum())} token(s) left the oracle's own routing (first layer where the "
+          f"selections differ: {left_at.tolist()}), {int(alive.sum())}/{T} followed it through "
+          f"all layers")
     if alive.any():
         err, bound = tol_check(acts[-1][alive], x_e2e[alive], "42-layer stack output")
         print(f"[decode_stack] end-to-end max err {err:.3e} (bound {bound:.3e})")

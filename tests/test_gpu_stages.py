@@ -76,6 +76,24 @@ def test_quantize_w8_bitexact(shape):
     np.testing.assert_array_equal(_np(q), O.pack_w8(q_ref))
 
 
+@pytest.mark.parametrize("shape,gs", [((16, 128), 128), ((48, 1024), 64), ((64, 4096), 256),
+                                      ((32, 512), 128)])
+def test_pack_plain_codes_bitexact(shape, gs):
+    """moe_w4_pack: plain row-major two's-complement codes (every byte value)
+    and row-major scales -> the packed format, byte for byte what the oracle
+    packs from the same codes."""
+    from w4_group_quantized_amd import pack_plain
+    g = np.random.default_rng(shape[1] + gs)
+    plain = g.integers(0, 256, size=(shape[0], shape[1] // 2), dtype=np.uint8)
+    plain[0, :128] = np.arange(128, dtype=np.uint8)
+    plain[1, :128] = np.arange(128, 256, dtype=np.uint8)
+    s = g.uniform(1e-4, 5e-2, size=(shape[0], shape[1] // gs)).astype(np.float16)
+    q, st = pack_plain(to_dev(plain), to_dev(s), gs)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(_np(q), O.pack_w4(O.unpack_plain_w4(plain)))
+    np.testing.assert_array_equal(_np(st).view(np.uint16), O.pack_scales(s).view(np.uint16))
+
+
 @pytest.mark.parametrize("gs", [64, 128, 256])
 def test_dequant_bitexact_all_codes(gs):
     from w4_group_quantized_amd import dequantize
@@ -382,6 +400,39 @@ def test_combine(T, k, H, with_shared, rms, renorm):
     layer.combine(buf, T, rmsnorm=rms, renorm=renorm)
     torch.cuda.synchronize()
     tol_check(_np(buf.out), ref, "combine")
+
+
+def test_combine_rows_past_4_gib():
+    """Hidden 65536 and 32784 tokens: the shared expert's rows and the output
+    rows of the last tokens start more than 2^32 bytes into their buffers
+    (t * H * 2 >= 2^32 from t = 32768); the combine must still read each
+    token's own shared row.  Checked on the first and the last 16 tokens."""
+    from types import SimpleNamespace
+    T, k, H = 32784, 1, 65536
+    cfg = get_config("tiny", num_experts=8, top_k=k, hidden=H, shared_ffn=128)
+    layer = _router_only_layer(cfg, np.zeros((8, H), np.float16), None)
+    layer.Fs = 128
+    layer.desc.shared_ffn = 128
+    g = torch.Generator(device=dev())
+    g.manual_seed(1234)
+    f16 = torch.float16
+    bufs = SimpleNamespace(
+        y_perm=(torch.randn((T * k, H), generator=g, device=dev()) * 0.3).to(f16),
+        y_shared=(torch.randn((T, H), generator=g, device=dev()) * 0.3).to(f16),
+        inv_pos=torch.randperm(T * k, generator=g, device=dev()).to(torch.int32),
+        topk_w=torch.rand((T, k), generator=g, device=dev()) * 0.3,
+        out=torch.empty((T, H), dtype=f16, device=dev()))
+    layer.combine(bufs, T)
+    torch.cuda.synchronize()
+    toks = np.r_[0:16, T - 16:T]
+    inv = _np(bufs.inv_pos).astype(np.int64)
+    w = _np(bufs.topk_w).astype(np.float64)
+    for t in toks:
+        ys = _np(bufs.y_shared[t]).astype(np.float64)
+        yp = _np(bufs.y_perm[inv[t]]).astype(np.float64)
+        ref = O.combine(yp[None], ys[None], np.zeros(1, np.int64), w[t:t + 1], 1, 1)[0]
+        tol_check(_np(bufs.out[t]), ref, f"token {t}")
+    del bufs
 
 
 # ---------------------------------------------------------------- exact-arithmetic probe

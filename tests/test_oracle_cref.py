@@ -72,3 +72,31 @@ def test_expert_ffn_matches_numpy_oracle():
     X = g.standard_normal((4, H))
     np.testing.assert_allclose(C.expert_ffn_w4_c(X, *mats), O.expert_ffn_w4(X, *mats),
                                rtol=1e-11, atol=1e-13)
+
+
+@pytest.mark.parametrize("gs", [64, 256])
+def test_matvec_and_dequant_other_group_sizes(gs):
+    """Groups of 64 and 256 columns: the C decoder reads the group size off
+    the scale shape and agrees with the numpy oracle (exactly for the
+    dequantized weights), and with exact arithmetic on integer inputs."""
+    g = np.random.default_rng(gs)
+    out_dim, in_dim = 32, 512
+    q = g.integers(0, 256, size=(out_dim, in_dim // 2), dtype=np.uint8)
+    s = g.uniform(1e-3, 3e-2, size=(out_dim, in_dim // gs)).astype(np.float16)
+    np.testing.assert_array_equal(C.dequant_rows(q, s, 0, out_dim), O.dequant(q, s, gs))
+    x = g.standard_normal((3, in_dim))
+    np.testing.assert_allclose(C.w4_matvec(q, s, x), x @ O.dequant(q, s, gs).T,
+                               rtol=1e-12, atol=1e-13)
+    qi = g.integers(-8, 8, size=(out_dim, in_dim)).astype(np.int8)
+    sl = (2.0 ** g.integers(-6, 0, size=(out_dim, in_dim // gs))).astype(np.float16)
+    xi = g.integers(-3, 4, size=(4, in_dim)).astype(np.float64)
+    W = qi.astype(np.float64) * np.repeat(sl.astype(np.float64), gs, axis=1)
+    np.testing.assert_array_equal(C.w4_matvec(O.pack_w4(qi), O.pack_scales(sl), xi), xi @ W.T)
+
+
+def test_unsupported_shapes_are_refused():
+    q = np.zeros((16, 64), np.uint8)
+    with pytest.raises(ValueError):
+        C.w4_matvec(q, np.zeros((16, 3), np.float16), np.zeros((1, 128)))   # 128/3 columns
+    with pytest.raises(ValueError):
+        C.w4_matvec(q, np.zeros((16, 4), np.float16), np.zeros((1, 128)))   # groups of 32

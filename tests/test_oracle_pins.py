@@ -132,6 +132,19 @@ def test_pack_layout_exhaustive():
         np.testing.assert_array_equal(O.pack_w4(q).reshape(-1), flat)
 
 
+def test_plain_int4_layout_hand_example():
+    """Plain row-major storage: low nibble = even column, two's complement."""
+    b = np.zeros((1, 4), np.uint8)
+    b[0] = [0x8F, 0x07, 0x71, 0xF8]
+    assert O.unpack_plain_w4(b).tolist() == [[-1, -8, 7, 0, 1, 7, -8, -1]]
+    # every byte value: the two nibbles decode independently
+    allb = np.arange(256, dtype=np.uint8).reshape(16, 16)
+    q = O.unpack_plain_w4(allb).reshape(-1, 2)
+    for v in range(256):
+        lo, hi = v & 15, v >> 4
+        assert q[v, 0] == (lo - 16 if lo >= 8 else lo) and q[v, 1] == (hi - 16 if hi >= 8 else hi)
+
+
 def test_scale_layout():
     """offset(row n, group g) = (n//16)*16*G + g*16 + n%16."""
     rows, G = 32, 3

@@ -31,7 +31,7 @@ MOE_RENORM = 2
 
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_route_permute",
            "moe_w4_grouped_ffn", "moe_unpermute_combine", "moe_layer_forward",
-           "moe_w4_dequant", "moe_w4_quantize", "moe_w8_quantize", "moe_status_str",
+           "moe_w4_dequant", "moe_w4_quantize", "moe_w4_pack", "moe_w8_quantize", "moe_status_str",
            "moe_last_hip_error")
 
 
@@ -84,6 +84,7 @@ _sigs = {
     "moe_w4_dequant": (ctypes.c_int, [_P, _P, _I64, _I64, _I32, _P, _P]),
     "moe_w4_quantize": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P]),
     "moe_w8_quantize": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
+    "moe_w4_pack": (ctypes.c_int, [_P, _P, _I64, _I64, _I32, _P, _P, _P]),
     "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_last_hip_error": (ctypes.c_char_p, []),
 }
@@ -191,6 +192,11 @@ def moe_layer_forward(layer, x, T, topk_idx, topk_w, offsets, perm_src, inv_pos,
 def moe_w4_dequant(q, s, rows, cols, group_size, out, stream=None):
     _check("moe_w4_dequant", lib.moe_w4_dequant(_ptr(q), _ptr(s), rows, cols, group_size,
                                                 _ptr(out), _stream(stream)))
+
+
+def moe_w4_pack(q_rowmajor, s_rowmajor, rows, cols, group_size, q, s, stream=None):
+    _check("moe_w4_pack", lib.moe_w4_pack(_ptr(q_rowmajor), _ptr(s_rowmajor), rows, cols,
+                                          group_size, _ptr(q), _ptr(s), _stream(stream)))
 
 
 def moe_w8_quantize(w, rows, cols, q, s, stream=None):

@@ -131,10 +131,12 @@ __global__ __launch_bounds__(64) void combine_cols_kernel(const f16 *__restrict_
   const int t = blockIdx.x / chunks;
   const int c = (blockIdx.x % chunks) * 512 + threadIdx.x * 8;
   if (c >= H) return;
-  // the shared expert's piece through a buffer that is empty without one,
-  // so it loads (as zeros) with the row indices and no branch
-  const rsrc_t yrs = make_rsrc(ys, ys ? (uint32_t)(t + 1) * (uint32_t)H * 2u : 0u);
-  const u32x4 yraw = bload16(yrs, ((uint32_t)t * H + c) * 2u, 0);
+  // the shared expert's piece through a buffer over this token's row (empty
+  // without a shared expert), so it loads (as zeros) with the row indices
+  // and no branch; the row base is a 64-bit address, the offset within the
+  // row at most 2 * 65536 bytes
+  const rsrc_t yrs = make_rsrc(ys ? ys + (size_t)t * H : ys, ys ? (uint32_t)H * 2u : 0u);
+  const u32x4 yraw = bload16(yrs, (uint32_t)c * 2u, 0);
   float wsum = 1.0f;
   if (renorm) {
     wsum = 0.0f;

@@ -32,6 +32,8 @@ WsLayout ws_layout(const moe_layer &L, int32_t T);
 
 hipError_t launch_quantize(const uint16_t *w, int64_t rows, int64_t cols, int gs, uint8_t *q,
                            uint16_t *s, hipStream_t st);
+hipError_t launch_pack(const uint8_t *q_rm, const uint16_t *s_rm, int64_t rows, int64_t cols,
+                       int gs, uint8_t *q, uint16_t *s, hipStream_t st);
 hipError_t launch_dequant(const uint8_t *q, const uint16_t *s, int64_t rows, int64_t cols, int gs,
                           float *out, hipStream_t st);
 hipError_t launch_quantize8(const uint16_t *w, int64_t rows, int64_t cols, uint8_t *q,

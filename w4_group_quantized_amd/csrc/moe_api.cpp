@@ -310,6 +310,19 @@ moe_status moe_w4_quantize(const uint16_t *w, int64_t rows, int64_t cols, int32_
   return hip_status(launch_quantize(w, rows, cols, group_size, q, s, (hipStream_t)stream));
 }
 
+moe_status moe_w4_pack(const uint8_t *q_rowmajor, const uint16_t *s_rowmajor, int64_t rows,
+                       int64_t cols, int32_t group_size, uint8_t *q, uint16_t *s, void *stream) {
+  if (rows < 0 || cols < 0) return MOE_EINVAL;
+  if (!supported_group_size(group_size)) return MOE_EUNSUPPORTED;
+  if (cols % 128 || cols % group_size || rows % 16) return MOE_EUNSUPPORTED;
+  if (rows == 0 || cols == 0) return MOE_OK;
+  if ((rows * (cols / 8) + 255) / 256 > 0x7fffffffLL) return MOE_EUNSUPPORTED;
+  if (!ok_ptr(q_rowmajor) || !ok_ptr(s_rowmajor) || !ok_ptr(q) || !ok_ptr(s)) return MOE_EINVAL;
+  clear_stale_hip_error();
+  return hip_status(launch_pack(q_rowmajor, s_rowmajor, rows, cols, group_size, q, s,
+                                (hipStream_t)stream));
+}
+
 moe_status moe_w8_quantize(const uint16_t *w, int64_t rows, int64_t cols, uint8_t *q, uint16_t *s,
                            void *stream) {
   if (rows < 0 || cols < 0) return MOE_EINVAL;

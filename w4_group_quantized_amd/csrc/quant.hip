@@ -71,6 +71,34 @@ __global__ __launch_bounds__(256) void quantize_kernel(const f16 *__restrict__ w
   if (word % glanes == 0) s[scale_offset(row, word / glanes, cols, gs)] = s16;
 }
 
+// Codes already quantized, in the plain row-major layout (byte c/2 of a row
+// holds column c in bits 0-3 and column c+1 in bits 4-7, two's-complement
+// nibbles; scales row-major [rows, cols/gs]) -> the stored format.  One thread
+// per 8 columns: the input word's low nibbles are columns 0,2,4,6 and its high
+// nibbles 1,3,5,7, which is the stored word's nibble order once each half is
+// compacted; XOR 0x8 per nibble turns two's complement into offset binary.
+__global__ __launch_bounds__(256) void pack_kernel(const uint32_t *__restrict__ q_rm,
+                                                   const f16 *__restrict__ s_rm,
+                                                   int64_t rows, int64_t cols, int gs,
+                                                   uint8_t *__restrict__ q,
+                                                   f16 *__restrict__ s) {
+  const int64_t words_per_row = cols / 8;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= rows * words_per_row) return;
+  const int64_t row = t / words_per_row, word = t % words_per_row;
+  const uint32_t in = q_rm[t];                  // row-major: word t is row `row`, word `word`
+  uint32_t lo = in & 0x0F0F0F0Fu;               // columns 0,2,4,6 in the low nibble of each byte
+  uint32_t hi = (in >> 4) & 0x0F0F0F0Fu;        // columns 1,3,5,7
+  lo = (lo | (lo >> 4)) & 0x00FF00FFu;
+  lo = (lo | (lo >> 8)) & 0x0000FFFFu;
+  hi = (hi | (hi >> 4)) & 0x00FF00FFu;
+  hi = (hi | (hi >> 8)) & 0x0000FFFFu;
+  *reinterpret_cast<uint32_t *>(q + word_offset(row, word, cols)) = (lo | (hi << 16)) ^ 0x88888888u;
+  const int glanes = gs / 8;
+  if (word % glanes == 0)
+    s[scale_offset(row, word / glanes, cols, gs)] = s_rm[row * (cols / gs) + word / glanes];
+}
+
 // out[n][c] = q[n][c] * s[n][c/gs] in fp32 (exact), decoding with the same
 // unpack8() the FFN kernels use.  One thread per stored 32-bit word.
 __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t *__restrict__ q,
@@ -156,6 +184,16 @@ hipError_t launch_quantize(const uint16_t *w, int64_t rows, int64_t cols, int gs
   hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
                      reinterpret_cast<const f16 *>(w), rows, cols, gs, q,
                      reinterpret_cast<f16 *>(s));
+  return hipGetLastError();
+}
+
+hipError_t launch_pack(const uint8_t *q_rm, const uint16_t *s_rm, int64_t rows, int64_t cols,
+                       int gs, uint8_t *q, uint16_t *s, hipStream_t st) {
+  const int64_t total = rows * (cols / 8);
+  const int64_t blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
+                     reinterpret_cast<const uint32_t *>(q_rm), reinterpret_cast<const f16 *>(s_rm),
+                     rows, cols, gs, q, reinterpret_cast<f16 *>(s));
   return hipGetLastError();
 }
 

@@ -158,6 +158,19 @@ def quantize_fp16(w: torch.Tensor, group_size: int = 128, stream=None):
     return q, s
 
 
+def pack_plain(q_rowmajor: torch.Tensor, s_rowmajor: torch.Tensor, group_size: int = 128,
+               stream=None):
+    """Already-quantized codes stored plainly (uint8 [rows, cols/2], byte c/2
+    = column c in bits 0-3 and c+1 in bits 4-7 as two's-complement nibbles;
+    scales fp16 [rows, cols/group_size]) -> (packed uint8 [rows, cols/2],
+    scales fp16 [rows, cols/group_size]) in the library's format."""
+    rows, half = q_rowmajor.shape
+    q = torch.empty_like(q_rowmajor)
+    s = torch.empty_like(s_rowmajor)
+    N.moe_w4_pack(q_rowmajor, s_rowmajor, rows, half * 2, group_size, q, s, stream)
+    return q, s
+
+
 def quantize_w8(w: torch.Tensor, stream=None):
     """8-bit g128 quantization of an fp16 device matrix [rows, cols] (the
     shared expert's format).  Returns (codes uint8 [rows, cols], scales fp16
