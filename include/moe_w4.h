@@ -43,9 +43,12 @@
  *  - Arguments are checked on the host before anything is launched; a failed
  *    check launches nothing and returns a negative moe_status.  T = 0 returns
  *    MOE_OK and launches nothing.
- *  - Two calls that share a workspace must not run concurrently.  Zero-fill a
- *    workspace once before its first use: it holds a synchronization counter
- *    that every call leaves at zero.
+ *  - Two calls that share a workspace must not run concurrently.  Prepare a
+ *    workspace once before its first use with moe_workspace_init (or zero-fill
+ *    its first 256 bytes): they hold a synchronization counter that every call
+ *    leaves at zero.  A workspace whose counter is not zero makes
+ *    moe_route_permute and moe_layer_forward write no routing (no error can be
+ *    reported without reading device memory on the host).
  *
  * Packed int4 weight format (this library's choice; the page stores int8
  * codes).  A matrix [out, in] with group size gs (out a multiple of 16, in a
@@ -145,6 +148,13 @@ typedef struct moe_layer {
  * tokens of `layer` (one workspace serves all four calls).  Returns 0 when
  * the layer description is invalid.  `layer` is a host pointer. */
 size_t moe_workspace_size(const moe_layer *layer, int32_t max_tokens);
+
+/* Prepare a workspace for its first use: zero-fills its first 256 bytes (the
+ * counter block) with a kernel on `stream` (no memset, so the call may also be
+ * captured into a graph).  ws_bytes below 256: MOE_EWORKSPACE; ws NULL or
+ * misaligned: MOE_EINVAL.  Calls after the first leave the block at zero, so
+ * one init per workspace is enough (again after a run that was aborted). */
+moe_status moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
 /* Router: l[t][e] = sum_h x[t][h] * router_w[e][h] + router_b[e] (fp32
  * accumulation), p = softmax over e (fp32, max subtracted), then the k largest

@@ -202,3 +202,10 @@ def test_pack_arguments():
     assert pack(FAKE, MISALIGNED, 16, 256, 128, FAKE, FAKE, None) == EINVAL
     assert pack(FAKE, FAKE, 16, 256, 128, FAKE, None, None) == EINVAL
     assert pack(None, None, 0, 256, 128, None, None, None) == OK            # nothing to do
+
+
+def test_workspace_init_arguments():
+    init = N.lib.moe_workspace_init
+    assert init(FAKE, 255, None) == EWS
+    assert init(None, 256, None) == EINVAL
+    assert init(MISALIGNED, 4096, None) == EINVAL

@@ -85,8 +85,7 @@ def test_pack_plain_codes_bitexact(shape, gs):
     from w4_group_quantized_amd import pack_plain
     g = np.random.default_rng(shape[1] + gs)
     plain = g.integers(0, 256, size=(shape[0], shape[1] // 2), dtype=np.uint8)
-    plain[0, :128] = np.arange(128, dtype=np.uint8)
-    plain[1, :128] = np.arange(128, 256, dtype=np.uint8)
+    plain.reshape(-1)[:256] = np.arange(256, dtype=np.uint8)      # every byte value
     s = g.uniform(1e-4, 5e-2, size=(shape[0], shape[1] // gs)).astype(np.float16)
     q, st = pack_plain(to_dev(plain), to_dev(s), gs)
     torch.cuda.synchronize()

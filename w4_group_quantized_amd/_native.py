@@ -29,7 +29,7 @@ lib = ctypes.CDLL(LIB_PATH)
 MOE_RMSNORM = 1
 MOE_RENORM = 2
 
-EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_route_permute",
+EXPORTS = ("moe_workspace_size", "moe_workspace_init", "moe_route", "moe_permute", "moe_route_permute",
            "moe_w4_grouped_ffn", "moe_unpermute_combine", "moe_layer_forward",
            "moe_w4_dequant", "moe_w4_quantize", "moe_w4_pack", "moe_w8_quantize", "moe_status_str",
            "moe_last_hip_error")
@@ -73,6 +73,7 @@ _LP = ctypes.POINTER(MoeLayer)
 
 _sigs = {
     "moe_workspace_size": (_SZ, [_LP, _I32]),
+    "moe_workspace_init": (ctypes.c_int, [_P, _SZ, _P]),
     "moe_route": (ctypes.c_int, [_LP, _P, _I32, _P, _P, _P, _SZ, _P]),
     "moe_permute": (ctypes.c_int, [_LP, _P, _P, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_route_permute": (ctypes.c_int, [_LP, _P, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -142,6 +143,10 @@ def make_layer(num_experts, hidden, ffn, top_k, router_w, router_b, gate_q, gate
 
 def moe_workspace_size(layer: MoeLayer, max_tokens: int) -> int:
     return lib.moe_workspace_size(ctypes.byref(layer), max_tokens)
+
+
+def moe_workspace_init(ws, ws_bytes, stream=None):
+    _check("moe_workspace_init", lib.moe_workspace_init(_ptr(ws), ws_bytes, _stream(stream)))
 
 
 def moe_route(layer, x, T, topk_idx, topk_w, ws, ws_bytes, stream=None):

@@ -17,6 +17,10 @@ constexpr int kRouterWideMinT = 256;   // 32-token x 128-expert router tiles fro
 constexpr int kFusedMaxKsb = 16;  // K parts of the fused router's logits
 constexpr int kFusedMaxLogits = 8192;   // T * E held in LDS by the fused router
 
+// The counter block at the start of every workspace (moe_workspace_init
+// zero-fills it; every call leaves it at zero).
+constexpr size_t kWsSyncBytes = 256;
+
 // Byte offsets of the per-call scratch regions inside the caller's workspace.
 struct WsLayout {
   size_t sync;      // uint32 counters; zero between calls

@@ -6,6 +6,7 @@
 #include <stddef.h>
 
 #include "../../include/moe_w4.h"
+#include "common.h"
 #include "kernels.h"
 
 namespace moe {
@@ -23,7 +24,7 @@ WsLayout ws_layout(const moe_layer &L, int32_t T) {
   const size_t N = Tz * k;
   const size_t nch = (N + kPermChunk - 1) / kPermChunk;
   size_t off = 0;
-  w.sync = off;     off += 256;
+  w.sync = off;     off += kWsSyncBytes;
   const bool fused = Tz <= (size_t)kFusedMaxT && Tz * E <= (size_t)kFusedMaxLogits;
   // the fused router's K parts each padded to a multiple of 4 logits
   const size_t nlog = fused ? (size_t)kFusedMaxKsb * ((Tz * E + 3) & ~(size_t)3) : Tz * E;
@@ -130,6 +131,13 @@ static moe_status check_combine_args(const uint16_t *y_perm, const uint16_t *y_s
   return MOE_OK;
 }
 
+// Zero-fills n 16-byte words (a kernel, not a memset node, so that the call
+// can sit in a captured graph).
+__global__ __launch_bounds__(256) void zero_words_kernel(u32x4 *p, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = (u32x4){0u, 0u, 0u, 0u};
+}
+
 static inline bool fused_route(const moe_layer &L, int32_t T) {
   return T <= kFusedMaxT && (int64_t)T * L.num_experts <= kFusedMaxLogits;
 }
@@ -166,6 +174,15 @@ extern "C" {
 size_t moe_workspace_size(const moe_layer *layer, int32_t max_tokens) {
   if (check_layer(layer) != MOE_OK || max_tokens < 0) return 0;
   return ws_layout(*layer, max_tokens).total;
+}
+
+moe_status moe_workspace_init(void *ws, size_t ws_bytes, void *stream) {
+  if (ws_bytes < kWsSyncBytes) return MOE_EWORKSPACE;
+  if (!ok_ptr(ws)) return MOE_EINVAL;
+  clear_stale_hip_error();
+  hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(kWsSyncBytes / 16), 0, (hipStream_t)stream,
+                     static_cast<u32x4 *>(ws), (size_t)(kWsSyncBytes / 16));
+  return hip_status(hipGetLastError());
 }
 
 moe_status moe_route(const moe_layer *L, const uint16_t *x, int32_t T, int32_t *topk_idx,

@@ -75,6 +75,8 @@ class W4MoELayer:
     def alloc(self, max_tokens: int) -> MoEBuffers:
         d, T, k, H, E = self.device, max_tokens, self.k, self.H, self.E
         i32, f16 = torch.int32, torch.float16
+        ws = torch.empty((max(self.workspace_size(T), 256),), dtype=torch.uint8, device=d)
+        N.moe_workspace_init(ws, ws.numel())   # its counter block starts at zero
         return MoEBuffers(
             max_tokens=T,
             topk_idx=torch.empty((T, k), dtype=i32, device=d),
@@ -86,8 +88,7 @@ class W4MoELayer:
             y_perm=torch.empty((T * k, H), dtype=f16, device=d),
             y_shared=torch.empty((T if self.Fs else 0, H), dtype=f16, device=d),
             out=torch.empty((T, H), dtype=f16, device=d),
-            # zero-filled once: it holds the fused router's completion counter
-            ws=torch.zeros((max(self.workspace_size(T), 256),), dtype=torch.uint8, device=d),
+            ws=ws,
         )
 
     # the stages, each one C call
