@@ -277,6 +277,27 @@ moe_status moe_layer_forward(const moe_layer *layer, const uint16_t *x, int32_t 
                              float eps, uint16_t *out, void *ws, size_t ws_bytes,
                              void *stream);
 
+/* moe_layer_forward for callers that cannot allocate device memory (code
+ * under graph capture without a memory pool, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments and outputs without ws and
+ * ws_bytes.  The workspace is instead a fixed array inside the library,
+ * 16 MiB on every GPU the library is loaded on (held until the process
+ * ends): a call whose moe_workspace_size(layer, T) exceeds 16 MiB returns
+ * MOE_EWORKSPACE and launches nothing (decode batches fit: the 288-expert
+ * hidden-4096 ffn-1536 top-8 layer with its shared expert up to 581 tokens,
+ * the 16-expert hidden-12288 ffn-65536 top-4 layer up to 31; the 8192-token
+ * prefill layer needs 260 MiB and does not).  The call allocates and frees nothing.  The first call on
+ * a GPU looks up that GPU's copy of the array and zero-fills its counter
+ * block on `stream`; `stream` must belong to the calling thread's current
+ * device.  Every call on one GPU uses that GPU's one array: calls that
+ * overlap on one GPU (other streams, other threads) race and must be
+ * serialised by the caller. */
+moe_status moe_layer_forward_noalloc(const moe_layer *layer, const uint16_t *x, int32_t T,
+                                     int32_t *topk_idx, float *topk_w, int32_t *offsets,
+                                     int32_t *perm_src, int32_t *inv_pos, uint16_t *x_perm,
+                                     uint16_t *y_perm, uint16_t *y_shared, uint32_t flags,
+                                     float eps, uint16_t *out, void *stream);
+
 /* Test hook: out[n][c] = q[n][c] * s[n][c/gs] in fp32 (exact, row-major
  * [rows, cols]) for one matrix in the packed format above with group size
  * gs = group_size (64, 128 or 256); rows multiple of 16, cols multiple of 128

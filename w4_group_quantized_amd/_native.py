@@ -31,6 +31,7 @@ MOE_RENORM = 2
 
 EXPORTS = ("moe_workspace_size", "moe_workspace_init", "moe_route", "moe_permute", "moe_route_permute",
            "moe_w4_grouped_ffn", "moe_unpermute_combine", "moe_layer_forward",
+           "moe_layer_forward_noalloc",
            "moe_w4_dequant", "moe_w4_quantize", "moe_w4_pack", "moe_w8_quantize", "moe_status_str",
            "moe_last_hip_error")
 
@@ -82,6 +83,8 @@ _sigs = {
                                              ctypes.c_float, _P, _P]),
     "moe_layer_forward": (ctypes.c_int, [_LP, _P, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
                                          ctypes.c_uint32, ctypes.c_float, _P, _P, _SZ, _P]),
+    "moe_layer_forward_noalloc": (ctypes.c_int, [_LP, _P, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
+                                                 ctypes.c_uint32, ctypes.c_float, _P, _P]),
     "moe_w4_dequant": (ctypes.c_int, [_P, _P, _I64, _I64, _I32, _P, _P]),
     "moe_w4_quantize": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P]),
     "moe_w8_quantize": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
@@ -192,6 +195,15 @@ def moe_layer_forward(layer, x, T, topk_idx, topk_w, offsets, perm_src, inv_pos,
                                  _ptr(offsets), _ptr(perm_src), _ptr(inv_pos), _ptr(x_perm),
                                  _ptr(y_perm), _ptr(y_shared), flags, eps, _ptr(out), _ptr(ws),
                                  ws_bytes, _stream(stream)))
+
+
+def moe_layer_forward_noalloc(layer, x, T, topk_idx, topk_w, offsets, perm_src, inv_pos, x_perm,
+                              y_perm, y_shared, flags, eps, out, stream=None):
+    _check("moe_layer_forward_noalloc",
+           lib.moe_layer_forward_noalloc(ctypes.byref(layer), _ptr(x), T, _ptr(topk_idx),
+                                         _ptr(topk_w), _ptr(offsets), _ptr(perm_src),
+                                         _ptr(inv_pos), _ptr(x_perm), _ptr(y_perm),
+                                         _ptr(y_shared), flags, eps, _ptr(out), _stream(stream)))
 
 
 def moe_w4_dequant(q, s, rows, cols, group_size, out, stream=None):

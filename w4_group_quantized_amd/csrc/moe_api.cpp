@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <stddef.h>
 
+#include <mutex>
+
 #include "../../include/moe_w4.h"
 #include "common.h"
 #include "kernels.h"
@@ -165,6 +167,75 @@ static hipError_t run_route_permute(const moe_layer &L, const uint16_t *x, int32
   return e;
 }
 
+// The whole layer on `st` with a prepared workspace of ws_bytes at `base`;
+// every argument already checked.
+static moe_status run_layer(const moe_layer &L, const uint16_t *x, int32_t T, int32_t *topk_idx,
+                            float *topk_w, int32_t *offsets, int32_t *perm_src, int32_t *inv_pos,
+                            uint16_t *x_perm, uint16_t *y_perm, uint16_t *ys, uint32_t flags,
+                            float eps, uint16_t *out, char *base, hipStream_t st) {
+  const WsLayout w = ws_layout(L, T);
+  hipError_t e = run_route_permute(L, x, T, topk_idx, topk_w, offsets, perm_src, inv_pos, x_perm,
+                                   base, w, st);
+  if (e == hipSuccess)
+    e = launch_ffn(L, x, x_perm, perm_src, offsets, T, y_perm, ys,
+                   reinterpret_cast<uint16_t *>(base + w.h),
+                   reinterpret_cast<uint16_t *>(base + w.h_shared), st);
+  if (e == hipSuccess)
+    e = launch_combine(L, y_perm, ys, inv_pos, topk_w, T, flags, eps, out, st);
+  return hip_status(e);
+}
+
+// Every argument of a whole-layer call but the workspace.
+static moe_status check_layer_call(const moe_layer *L, const uint16_t *x, int32_t T,
+                                   const int32_t *topk_idx, const float *topk_w,
+                                   const int32_t *offsets, const int32_t *perm_src,
+                                   const int32_t *inv_pos, const uint16_t *x_perm,
+                                   const uint16_t *y_perm, const uint16_t *y_shared,
+                                   uint32_t flags, float eps, const uint16_t *out) {
+  moe_status s;
+  if ((s = check_route_args(L, x, topk_idx, topk_w)) != MOE_OK) return s;
+  if ((s = check_permute_args(x, topk_idx, offsets, perm_src, inv_pos, x_perm)) != MOE_OK)
+    return s;
+  if ((s = check_ffn_args(L, T, x, x_perm, perm_src, offsets, y_perm, y_shared)) != MOE_OK)
+    return s;
+  const uint16_t *ys = L->shared_ffn > 0 ? y_shared : nullptr;
+  return check_combine_args(y_perm, ys, inv_pos, topk_w, flags, eps, out);
+}
+
+// Fixed scratch of moe_layer_forward_noalloc: a __device__ array exists once
+// on every GPU the library is loaded on.  Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in for the symbol): it
+// looks up each device's address once, with that device current, and passes
+// that address.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+static char *g_scratch_ptr[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+// The current device's scratch address.  On the first call for a device:
+// look it up and zero-fill the counter block at its start on `st` (a fill
+// kernel; later calls leave the block at zero).
+static moe_status device_scratch(hipStream_t st, char **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return MOE_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (ptr == nullptr || (reinterpret_cast<uintptr_t>(ptr) & 255u)) return MOE_EHIP;
+    hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(kWsSyncBytes / 16), 0, st,
+                       static_cast<u32x4 *>(ptr), (size_t)(kWsSyncBytes / 16));
+    if ((e = hipGetLastError()) != hipSuccess) return hip_status(e);
+    g_scratch_ptr[dev] = static_cast<char *>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -280,27 +351,35 @@ moe_status moe_layer_forward(const moe_layer *L, const uint16_t *x, int32_t T, i
   if ((s = check_layer(L)) != MOE_OK) return s;
   if ((s = check_tokens(L, T)) != MOE_OK) return s;
   if (T == 0) return MOE_OK;
-  if ((s = check_route_args(L, x, topk_idx, topk_w)) != MOE_OK) return s;
-  if ((s = check_permute_args(x, topk_idx, offsets, perm_src, inv_pos, x_perm)) != MOE_OK)
+  if ((s = check_layer_call(L, x, T, topk_idx, topk_w, offsets, perm_src, inv_pos, x_perm,
+                            y_perm, y_shared, flags, eps, out)) != MOE_OK)
     return s;
-  if ((s = check_ffn_args(L, T, x, x_perm, perm_src, offsets, y_perm, y_shared)) != MOE_OK)
-    return s;
-  uint16_t *ys = L->shared_ffn > 0 ? y_shared : nullptr;
-  if ((s = check_combine_args(y_perm, ys, inv_pos, topk_w, flags, eps, out)) != MOE_OK) return s;
   if ((s = check_ws(L, T, ws, ws_bytes)) != MOE_OK) return s;
-  const WsLayout w = ws_layout(*L, T);
-  char *base = static_cast<char *>(ws);
+  clear_stale_hip_error();
+  return run_layer(*L, x, T, topk_idx, topk_w, offsets, perm_src, inv_pos, x_perm, y_perm,
+                   L->shared_ffn > 0 ? y_shared : nullptr, flags, eps, out,
+                   static_cast<char *>(ws), (hipStream_t)stream);
+}
+
+moe_status moe_layer_forward_noalloc(const moe_layer *L, const uint16_t *x, int32_t T,
+                                     int32_t *topk_idx, float *topk_w, int32_t *offsets,
+                                     int32_t *perm_src, int32_t *inv_pos, uint16_t *x_perm,
+                                     uint16_t *y_perm, uint16_t *y_shared, uint32_t flags,
+                                     float eps, uint16_t *out, void *stream) {
+  moe_status s;
+  if ((s = check_layer(L)) != MOE_OK) return s;
+  if ((s = check_tokens(L, T)) != MOE_OK) return s;
+  if (T == 0) return MOE_OK;
+  if ((s = check_layer_call(L, x, T, topk_idx, topk_w, offsets, perm_src, inv_pos, x_perm,
+                            y_perm, y_shared, flags, eps, out)) != MOE_OK)
+    return s;
+  if (ws_layout(*L, T).total > kScratchBytes) return MOE_EWORKSPACE;
   const hipStream_t st = (hipStream_t)stream;
   clear_stale_hip_error();
-  hipError_t e = run_route_permute(*L, x, T, topk_idx, topk_w, offsets, perm_src, inv_pos, x_perm,
-                                   base, w, st);
-  if (e == hipSuccess)
-    e = launch_ffn(*L, x, x_perm, perm_src, offsets, T, y_perm, ys,
-                   reinterpret_cast<uint16_t *>(base + w.h),
-                   reinterpret_cast<uint16_t *>(base + w.h_shared), st);
-  if (e == hipSuccess)
-    e = launch_combine(*L, y_perm, ys, inv_pos, topk_w, T, flags, eps, out, st);
-  return hip_status(e);
+  char *base = nullptr;
+  if ((s = device_scratch(st, &base)) != MOE_OK) return s;
+  return run_layer(*L, x, T, topk_idx, topk_w, offsets, perm_src, inv_pos, x_perm, y_perm,
+                   L->shared_ffn > 0 ? y_shared : nullptr, flags, eps, out, base, st);
 }
 
 moe_status moe_w4_dequant(const uint8_t *q, const uint16_t *s, int64_t rows, int64_t cols,
