@@ -4,8 +4,10 @@
 
 A step is one forward of the workload (moe_layer_forward per layer: route +
 permute -> grouped W4 FFN -> combine) over one batch of synthetic tokens
-already resident in HBM; by default the largest configuration, the decode
-step through 42 stacked layers (288 experts + 1 shared, hidden 4096, ffn
+already resident in HBM, timed as a HIP-graph replay (each step's launches
+captured once after the warm-up, as the pages run the grouped expert GEMM in
+a fixed captured graph; --eager times the same calls launched one by one); by
+default the largest configuration, the decode step through 42 stacked layers (288 experts + 1 shared, hidden 4096, ffn
 1536, top-8, 16 tokens, RMS norm between layers, 119 GB of weights).  The
 single-layer workloads rotate several independently drawn weight sets so
 that no expert byte is served from the 256 MB Infinity Cache across steps.
@@ -70,9 +72,9 @@ def parse():
                     help="shared expert weights: fp16, or 8-bit g128")
     ap.add_argument("--weight-sets", type=int, default=0, help="0 = workload default")
     ap.add_argument("--batches", type=int, default=4, help="distinct token batches rotated")
-    ap.add_argument("--graph", action="store_true",
-                    help="time the steps as HIP-graph replays: each (weight set, batch) step "
-                         "captured once after the warm-up, replayed in the timed region")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the steps as eager launches (one C call per layer) instead of "
+                         "HIP-graph replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -373,7 +375,7 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    if args.graph:
+    if not args.eager:
         # every library call is asynchronous with no host reads, so a whole
         # step (all its layers) is captured as launched; nothing allocates
         graphs = []
@@ -510,7 +512,7 @@ def main():
             "hidden": cfg.hidden, "ffn": cfg.ffn, "top_k": cfg.top_k, "tokens": T,
             "layers_per_step": layers_per_step, "weight_sets": n_sets, "batches": args.batches,
             "group_size": cfg.group_size, "shared_bits": cfg.shared_bits,
-            "launch": "HIP graph replay" if args.graph else "eager (one C call per layer)",
+            "launch": "eager (one C call per layer)" if args.eager else "HIP graph replay",
             "weights": (f"int4 g{cfg.group_size} (fp16 scales), router fp16, shared expert "
                         + ("fp16" if cfg.shared_bits == 16 else "8-bit g128")),
             "distinct_experts_per_layer_mean": float(np.mean(layer_u)),
