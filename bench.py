@@ -7,8 +7,9 @@ permute -> grouped W4 FFN -> combine) over one batch of synthetic tokens
 already resident in HBM, timed as a HIP-graph replay (each step's launches
 captured once after the warm-up, as the pages run the grouped expert GEMM in
 a fixed captured graph; --eager times the same calls launched one by one); by
-default the largest configuration, the decode step through 42 stacked layers (288 experts + 1 shared, hidden 4096, ffn
-1536, top-8, 16 tokens, RMS norm between layers, 119 GB of weights).  The
+default the largest configuration, the decode step through 42 stacked layers
+(288 experts + 1 shared, hidden 4096, ffn 1536, top-8, 16 tokens, RMS norm
+between layers, 119 GB of weights).  The
 single-layer workloads rotate several independently drawn weight sets so
 that no expert byte is served from the 256 MB Infinity Cache across steps.
 Prints ONE JSON line.
@@ -72,6 +73,7 @@ def parse():
                     help="shared expert weights: fp16, or 8-bit g128")
     ap.add_argument("--weight-sets", type=int, default=0, help="0 = workload default")
     ap.add_argument("--batches", type=int, default=4, help="distinct token batches rotated")
+    ap.add_argument("--tokens", type=int, default=0, help="tokens per step (0 = the workload's)")
     ap.add_argument("--eager", action="store_true",
                     help="time the steps as eager launches (one C call per layer) instead of "
                          "HIP-graph replays")
@@ -308,7 +310,9 @@ def main():
     import torch
     import w4_group_quantized_amd  # noqa: F401  (fails loudly without the HIP library)
 
-    cfg = get_config(args.workload, group_size=args.group_size, shared_bits=args.shared_bits)
+    over = {"tokens": args.tokens} if args.tokens else {}
+    cfg = get_config(args.workload, group_size=args.group_size, shared_bits=args.shared_bits,
+                     **over)
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     layers_per_step = cfg.layers
@@ -488,7 +492,8 @@ def main():
     if not args.no_cpu_baseline:
         layer_cfg = cfg if cfg.layers == 1 else get_config(cfg.name, layers=1,
                                                            group_size=cfg.group_size,
-                                                           shared_bits=cfg.shared_bits)
+                                                           shared_bits=cfg.shared_bits,
+                                                           tokens=cfg.tokens)
         cpu = cpu_baseline(layer_cfg, args.cpu_budget_s)
         if cfg.layers > 1:       # one oracle layer of the 42: scale to a whole step
             cpu["value"] /= cfg.layers

@@ -79,7 +79,15 @@ struct W4Stage {
   f16 s[S][NT];
 };
 
-template <int NT, int S, int GM, class A>
+// Code loads: streamed (non-temporal) when no other tile of the launch reads
+// the same weight lines, cached when segments span several 16-row tiles that
+// each read the expert's weights (STREAM, chosen by the host).
+template <bool STREAM>
+__device__ __forceinline__ u32x4 ld16_codes(const void *p) {
+  return STREAM ? ld16_stream(p) : ld16(p);
+}
+
+template <int NT, int S, int GM, bool STREAM, class A>
 __device__ __forceinline__ void w4_load(W4Stage<NT, S> &st, const A &a,
                                         const uint8_t *const (&qrow)[NT],
                                         const f16 *const (&srow)[NT], int g, int G) {
@@ -88,7 +96,7 @@ __device__ __forceinline__ void w4_load(W4Stage<NT, S> &st, const A &a,
     const int gg = min(g + i, G - 1);   // past the end: reload the last group (never used)
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      st.q[i][t] = ld16_stream(qrow[t] + (size_t)gg * 1024);   // 1 KB: 8 whole lines
+      st.q[i][t] = ld16_codes<STREAM>(qrow[t] + (size_t)gg * 1024);   // 1 KB: 8 whole lines
       st.s[i][t] = srow[t][(size_t)scale_group<GM>(gg) * 16];
     }
     if (!A::kDeferred) {
@@ -139,22 +147,22 @@ __device__ __forceinline__ void w4_compute(const W4Stage<NT, S> &st, const A &a,
 struct NoOp {
   __device__ __forceinline__ void operator()() const {}
 };
-template <int NT, int S, int GM, class A, class F = NoOp>
+template <int NT, int S, int GM, bool STREAM, class A, class F = NoOp>
 __device__ __forceinline__ void w4_tiles(const A &arow, const uint8_t *const (&qrow)[NT],
                                          const f16 *const (&srow)[NT], int g0, int g1,
                                          f32x4 (&acc)[NT], F after_first = F()) {
   if (g0 >= g1) return;
   const UnpackConsts magic = unpack_consts();
   W4Stage<NT, S> a, b;
-  w4_load<NT, S, GM>(a, arow, qrow, srow, g0, g1);
+  w4_load<NT, S, GM, STREAM>(a, arow, qrow, srow, g0, g1);
   after_first();
   int g = g0;
   for (; g + 2 * S <= g1; g += 2 * S) {
-    w4_load<NT, S, GM>(b, arow, qrow, srow, g + S, g1);
+    w4_load<NT, S, GM, STREAM>(b, arow, qrow, srow, g + S, g1);
     sched_fence();
     w4_compute<NT, S, GM>(a, arow, g, S, magic, acc);
     sched_fence();
-    w4_load<NT, S, GM>(a, arow, qrow, srow, g + 2 * S, g1);
+    w4_load<NT, S, GM, STREAM>(a, arow, qrow, srow, g + 2 * S, g1);
     sched_fence();
     w4_compute<NT, S, GM>(b, arow, g + S, S, magic, acc);
     sched_fence();
@@ -163,7 +171,7 @@ __device__ __forceinline__ void w4_tiles(const A &arow, const uint8_t *const (&q
   if (rest > 0) {
     w4_compute<NT, S, GM>(a, arow, g, rest, magic, acc);
     if (rest > S) {
-      w4_load<NT, S, GM>(b, arow, qrow, srow, g + S, g1);
+      w4_load<NT, S, GM, STREAM>(b, arow, qrow, srow, g + S, g1);
       w4_compute<NT, S, GM>(b, arow, g + S, rest - S, magic, acc);
     }
   }
@@ -244,7 +252,7 @@ struct W8Stage {
   f16 s[NT];
 };
 
-template <int NT>
+template <int NT, bool STREAM>
 __device__ __forceinline__ void w8_load(W8Stage<NT> &st, const ARows &arow,
                                         const uint8_t *const (&qrow)[NT],
                                         const f16 *const (&srow)[NT], int g, int G) {
@@ -253,8 +261,8 @@ __device__ __forceinline__ void w8_load(W8Stage<NT> &st, const ARows &arow,
   for (int m = 0; m < 4; ++m) st.x[m] = arow.load(gg, m);
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    st.q[t][0] = ld16_stream(qrow[t] + (size_t)gg * 2048);   // whole lines each
-    st.q[t][1] = ld16_stream(qrow[t] + (size_t)gg * 2048 + 256);
+    st.q[t][0] = ld16_codes<STREAM>(qrow[t] + (size_t)gg * 2048);   // whole lines each
+    st.q[t][1] = ld16_codes<STREAM>(qrow[t] + (size_t)gg * 2048 + 256);
     st.s[t] = srow[t][(size_t)gg * 16];
   }
 }
@@ -276,20 +284,20 @@ __device__ __forceinline__ void w8_compute(const W8Stage<NT> &st, f32x4 (&acc)[N
 // 8-bit weights: acc[t] += sum_g scale[t][g] * sum_{k in g} A[tok][k] * q[t][k]
 // over blocks [g0, g1); qrow[t]: tile base + 2kb*256 + r*16 (block g at
 // + g*2048); srow[t]: the tile's scales + r (block g at srow[t][g*16]).
-template <int NT>
+template <int NT, bool STREAM>
 __device__ __forceinline__ void w8_tiles(const ARows &arow, const uint8_t *const (&qrow)[NT],
                                          const f16 *const (&srow)[NT], int g0, int g1,
                                          f32x4 (&acc)[NT]) {
   if (g0 >= g1) return;
   W8Stage<NT> a, b;
-  w8_load<NT>(a, arow, qrow, srow, g0, g1);
+  w8_load<NT, STREAM>(a, arow, qrow, srow, g0, g1);
   int g = g0;
   for (; g + 2 <= g1; g += 2) {
-    w8_load<NT>(b, arow, qrow, srow, g + 1, g1);
+    w8_load<NT, STREAM>(b, arow, qrow, srow, g + 1, g1);
     sched_fence();
     w8_compute<NT>(a, acc);
     sched_fence();
-    w8_load<NT>(a, arow, qrow, srow, g + 2, g1);
+    w8_load<NT, STREAM>(a, arow, qrow, srow, g + 2, g1);
     sched_fence();
     w8_compute<NT>(b, acc);
     sched_fence();
