@@ -163,35 +163,50 @@ __device__ __forceinline__ void prefill_gemm(f16 *sA, rsrc_t a_rs, rsrc_t b_rs0,
   const UnpackConsts kc = unpack_consts();
   // step `step` uses register stage u; the codes of step + D go to stage
   // (u + D) % NS, which held those of step - 1
+  auto unpack_b = [&](int u, int w, f16x8 (&bf)[2]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const f16x8 q = unpack8(rb[u][j][w], kc);
+      const f16x2 sc = {rs[u][j], rs[u][j]};
+      u32x4 v;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const f16x2 pr = {q[2 * t], q[2 * t + 1]};
+        v[t] = as_u32(pr * sc);                    // RN16(q * s)
+      }
+      bf[j] = as_f16x8(v);
+    }
+  };
+  auto read_a = [&](const f16 *as, int w, f16x8 (&af)[MI]) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+      af[i] = *reinterpret_cast<const f16x8 *>(as + i * 32 * kPK + o.a_rd[w]);
+  };
+  // Software pipeline over the 4 k16 sub-steps: the region of sub-step w
+  // holds the LDS operand reads and the weight unpack of sub-step w + 1 and
+  // the MFMAs of sub-step w (scheduling fences keep the regions apart, so
+  // the reads and the unpack overlap the matrix-core work).
   auto body = [&](int step, int u) {
     lds_barrier();      // stage step % 2 is complete; stage (step+1) % 2 is free
+    const f16 *as = sA + (step & 1) * kPStage;
+    f16x8 af[2][MI], bf[2][2];
+    read_a(as, 0, af[0]);
     load_a(min(step + 1, nsteps - 1));
     load_b(min(step + D, nsteps - 1), (u + D) % NS);
-    __builtin_amdgcn_sched_barrier(0);   // keep the loads at the top of the step
-    const f16 *as = sA + (step & 1) * kPStage;
+    unpack_b(u, 0, bf[0]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      f16x8 bf[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const f16x8 q = unpack8(rb[u][j][w], kc);
-        const f16x2 sc = {rs[u][j], rs[u][j]};
-        u32x4 v;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const f16x2 pr = {q[2 * t], q[2 * t + 1]};
-          v[t] = as_u32(pr * sc);                    // RN16(q * s)
-        }
-        bf[j] = as_f16x8(v);
+      if (w + 1 < 4) {
+        read_a(as, w + 1, af[(w + 1) & 1]);
+        unpack_b(u, w + 1, bf[(w + 1) & 1]);
       }
-      f16x8 af[MI];
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-        af[i] = *reinterpret_cast<const f16x8 *>(as + i * 32 * kPK + o.a_rd[w]);
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_32x32x16(bf[j], af[i], acc[i][j]);
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = mfma_32x32x16(bf[w & 1][j], af[w & 1][i], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (step + 1 < nsteps) store_a(step + 1);
   };
