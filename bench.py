@@ -2,14 +2,17 @@
 
     python bench.py [--steps K] [--warmup W] [--workload decode_stack]
 
-A step is one forward of the workload (moe_layer_forward per layer: route +
-permute -> grouped W4 FFN -> combine) over one batch of synthetic tokens
-already resident in HBM, timed as a HIP-graph replay (each step's launches
-captured once after the warm-up, as the pages run the grouped expert GEMM in
-a fixed captured graph; --eager times the same calls launched one by one); by
-default the largest configuration, the decode step through 42 stacked layers
-(288 experts + 1 shared, hidden 4096, ffn 1536, top-8, 16 tokens, RMS norm
-between layers, 119 GB of weights).  The
+A step is one forward of the workload (per layer: route + permute -> grouped
+W4 FFN -> combine) over one batch of synthetic tokens already resident in
+HBM: one moe_layer_forward call for a single layer, one
+moe_decode_stack_forward call for the stacked decode step (layer i's combine
+and layer i+1's routing in one launch; --per-layer makes it one
+moe_layer_forward call per layer).  Steps are timed as HIP-graph replays
+(each step's launches captured once after the warm-up, as the pages run the
+grouped expert GEMM in a fixed captured graph; --eager times the same calls
+launched one by one).  By default the largest configuration, the decode step
+through 42 stacked layers (288 experts + 1 shared, hidden 4096, ffn 1536,
+top-8, 16 tokens, RMS norm between layers, 119 GB of weights).  The
 single-layer workloads rotate several independently drawn weight sets so
 that no expert byte is served from the 256 MB Infinity Cache across steps.
 Prints ONE JSON line.
@@ -74,6 +77,9 @@ def parse():
     ap.add_argument("--weight-sets", type=int, default=0, help="0 = workload default")
     ap.add_argument("--batches", type=int, default=4, help="distinct token batches rotated")
     ap.add_argument("--tokens", type=int, default=0, help="tokens per step (0 = the workload's)")
+    ap.add_argument("--per-layer", action="store_true",
+                    help="stacked workloads: one moe_layer_forward call per layer instead of "
+                         "one moe_decode_stack_forward call per step")
     ap.add_argument("--eager", action="store_true",
                     help="time the steps as eager launches (one C call per layer) instead of "
                          "HIP-graph replays")
@@ -331,10 +337,19 @@ def main():
     torch.cuda.synchronize()
 
     n_combo = n_sets * args.batches
+    # a stacked step is one moe_decode_stack_forward call (layer i's combine
+    # and layer i+1's routing share a launch), unless --per-layer
+    use_stack = layers_per_step > 1 and not args.per_layer
+    stacks = [w4_group_quantized_amd.W4MoEStack(layers) for layers in sets] if use_stack else None
+    acts = (torch.empty((layers_per_step, T, cfg.hidden), dtype=torch.float16, device=dev)
+            if use_stack else None)
 
     def step(i):
-        layers = sets[i % n_sets]
         x = xs[(i // n_sets) % args.batches]
+        if use_stack:
+            stacks[i % n_sets].forward(x, bufs, acts=acts, T=T, rmsnorm=True, eps=cfg.rms_eps)
+            return
+        layers = sets[i % n_sets]
         for li, layer in enumerate(layers):
             if li == len(layers) - 1:
                 layer.forward(x, bufs, T, rmsnorm=layers_per_step > 1, eps=cfg.rms_eps)
@@ -360,11 +375,21 @@ def main():
     for c in range(n_combo):
         x = xs[(c // n_sets) % args.batches]
         plan, lb, lu = [], [], []
+        if use_stack:
+            # the stack's own layer inputs; a call over the first n layers
+            # leaves layer n-1's routing (as the full call computes it)
+            full = stacks[c % n_sets].forward(x, bufs, T=T, rmsnorm=True, eps=cfg.rms_eps)
         for li, layer in enumerate(sets[c % n_sets]):
-            x_in = x.clone()
             b = routing_buffers()
-            nxt = torch.empty_like(x_in)
-            layer.forward(x_in, b, T, rmsnorm=layers_per_step > 1, eps=cfg.rms_eps, out=nxt)
+            if use_stack:
+                x_in = x.clone() if li == 0 else full[li - 1].clone()
+                stacks[c % n_sets].forward(x, b, T=T, rmsnorm=True, eps=cfg.rms_eps,
+                                           n_layers=li + 1)
+                nxt = x            # every prefix call starts from the step's input
+            else:
+                x_in = x.clone()
+                nxt = torch.empty_like(x_in)
+                layer.forward(x_in, b, T, rmsnorm=layers_per_step > 1, eps=cfg.rms_eps, out=nxt)
             torch.cuda.synchronize()
             U = int((np.diff(b.offsets.cpu().numpy()) > 0).sum())
             plan.append((layer, x_in, b))
@@ -517,7 +542,9 @@ def main():
             "hidden": cfg.hidden, "ffn": cfg.ffn, "top_k": cfg.top_k, "tokens": T,
             "layers_per_step": layers_per_step, "weight_sets": n_sets, "batches": args.batches,
             "group_size": cfg.group_size, "shared_bits": cfg.shared_bits,
-            "launch": "eager (one C call per layer)" if args.eager else "HIP graph replay",
+            "launch": "eager" if args.eager else "HIP graph replay",
+            "call": ("moe_decode_stack_forward per step" if use_stack else
+                     "moe_layer_forward per layer"),
             "weights": (f"int4 g{cfg.group_size} (fp16 scales), router fp16, shared expert "
                         + ("fp16" if cfg.shared_bits == 16 else "8-bit g128")),
             "distinct_experts_per_layer_mean": float(np.mean(layer_u)),

@@ -13,7 +13,8 @@
  *                          the shared expert's output (optional RMS norm)
  *
  * moe_route_permute does the first two in one call (one launch for small
- * batches) and moe_layer_forward all four.  moe_w4_quantize and
+ * batches) and moe_layer_forward all four; moe_decode_stack_forward runs a
+ * decode step through a stack of layers.  moe_w4_quantize and
  * moe_w8_quantize write the weight formats below from fp16 matrices;
  * moe_w4_pack writes the int4 format from codes that are already quantized
  * and stored plainly (row-major, two's-complement nibbles).
@@ -276,6 +277,43 @@ moe_status moe_layer_forward(const moe_layer *layer, const uint16_t *x, int32_t 
                              uint16_t *y_perm, uint16_t *y_shared, uint32_t flags,
                              float eps, uint16_t *out, void *ws, size_t ws_bytes,
                              void *stream);
+
+/* A decode step through n_layers stacked layers, the output of layer i being
+ * the input of layer i + 1 (haowenji.com/articles/x-2109226022155796480 §01:
+ * a decode step runs the token through 42 MoE layers).  Computes
+ *     acts[0] = layer_0(x),  acts[i] = layer_i(acts[i-1]),
+ * each layer_i being moe_layer_forward of layers[i] with x_perm NULL and the
+ * given flags and eps (MOE_RMSNORM between stacked layers).
+ *   layers    HOST array of n_layers (>= 1) host pointers; every layer has
+ *             the same num_experts, hidden, ffn, top_k and shared_ffn
+ *             (MOE_EUNSUPPORTED otherwise); group sizes and shared_bits may
+ *             differ
+ *   x         fp16 [T, H], the input of layer 0; T*H*2 below 2^31
+ *   acts      fp16 [n_layers, T, H] out: every layer's output, the last one
+ *             being the step's output
+ *   topk_idx, topk_w, offsets, perm_src, inv_pos, y_perm, y_shared
+ *             as in moe_layer_forward; reused by every layer, they hold the
+ *             last layer's values when the call returns
+ *   flags, eps, ws, ws_bytes, stream  as in moe_layer_forward; the workspace
+ *             is moe_workspace_size(layers[0], T) bytes
+ * Launches: for T <= 32 tokens and hidden <= 8192 the combine of layer i and
+ * the router, top-k and permutation of layer i + 1 run in one launch (one
+ * block per token and tile of experts forms the token's combined row, the
+ * last block of each token runs its top-k, the last of those the
+ * permutation; the counter block of the workspace must start at zero, and
+ * every call leaves it so).  The combined rows are bitwise those of
+ * moe_unpermute_combine; the logits of layers 1 .. n-1 are fp32 dot products
+ * summed in another order than moe_route's, so a token whose k-th and
+ * (k+1)-th logits agree to the last bits may choose differently and the
+ * combine weights may differ in the last bits.  Larger batches run each
+ * layer as moe_layer_forward does, bitwise.  All arguments are checked
+ * before the first launch. */
+moe_status moe_decode_stack_forward(const moe_layer *const *layers, int32_t n_layers,
+                                    const uint16_t *x, int32_t T, int32_t *topk_idx,
+                                    float *topk_w, int32_t *offsets, int32_t *perm_src,
+                                    int32_t *inv_pos, uint16_t *y_perm, uint16_t *y_shared,
+                                    uint32_t flags, float eps, uint16_t *acts, void *ws,
+                                    size_t ws_bytes, void *stream);
 
 /* moe_layer_forward for callers that cannot allocate device memory (code
  * under graph capture without a memory pool, tight serving loops, harnesses

@@ -158,6 +158,47 @@ def test_layer_forward_argument_errors():
                 a13=None, a14=None, a15=0) == OK            # T = 0: no-op
 
 
+def test_decode_stack_argument_errors():
+    """The stacked decode step checks every layer and every buffer before
+    launching: no layers, layers of different shapes, and each stage's
+    argument errors."""
+    L0, L1 = layer(), layer()
+    big = 1 << 30
+    fwd = N.lib.moe_decode_stack_forward
+    arr = N.layer_array([L0, L1])
+    # (layers, n, x, T, idx, w, offsets, perm_src, inv_pos, y_perm, y_shared, flags, eps, acts,
+    #  ws, ws_bytes, stream)
+    args = [arr, 2, FAKE, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 1e-6, FAKE, FAKE, big,
+            None]
+
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return fwd(*a)
+
+    assert call(a0=None) == EINVAL                      # no layer array
+    assert call(a1=0) == EINVAL                         # no layers
+    assert call(a2=None) == EINVAL                      # no x
+    assert call(a4=MISALIGNED) == EINVAL                # topk_idx misaligned
+    assert call(a7=None) == EINVAL                      # no perm_src
+    assert call(a9=None) == EINVAL                      # no y_perm
+    assert call(a11=4) == EINVAL                        # unknown flag
+    assert call(a11=1, a12=-1.0) == EINVAL              # negative eps
+    assert call(a13=None) == EINVAL                     # no acts
+    assert call(a15=64) == EWS
+    assert call(a3=(1 << 31) // (2 * L0.hidden)) == EUNSUP   # rows of x gathered with 32-bit offsets
+    for kw in (dict(ffn=256), dict(hidden=512), dict(num_experts=16), dict(top_k=4),
+               dict(shared_ffn=256, shared_gate=FAKE, shared_up=FAKE, shared_down=FAKE)):
+        assert call(a0=N.layer_array([L0, layer(**kw)])) == EUNSUP, kw   # shapes differ
+    # group sizes may differ: the call gets as far as the workspace check
+    assert call(a0=N.layer_array([L0, layer(group_size=64)]), a15=64) == EWS
+    assert call(a0=N.layer_array([L0, layer(top_k=9)])) == EUNSUP        # an invalid layer
+    assert call(a0=N.layer_array([L0, layer(gate_q=None)])) == EINVAL    # a layer's weights
+    assert call(a3=0, a2=None, a4=None, a5=None, a6=None, a7=None, a8=None, a9=None,
+                a13=None, a14=None, a15=0) == OK            # T = 0: no-op
+
+
 def test_8bit_shared_expert_arguments():
     big = 1 << 30
     ffn = N.lib.moe_w4_grouped_ffn

@@ -1,7 +1,8 @@
 """Full-size parity in the launch configuration the benchmark times
-(moe_layer_forward: the one-launch router and permutation for decode
-batches, the grouped FFN reading rows through perm_src, the combine),
-against the float64 oracle.
+(moe_layer_forward for single layers: the one-launch router and permutation
+for decode batches, the grouped FFN reading rows through perm_src, the
+combine; moe_decode_stack_forward for the 42-layer decode step), against the
+float64 oracle.
 
 Expert weights are packed codes + scales drawn on the device with the law of
 quantized N(0, sigma) weights (workloads.gen_torch); the oracle reads back the
@@ -174,27 +175,40 @@ def test_full_size_prefill_whole_segments():
 
 
 def test_full_size_decode_stack():
-    """42 layers, RMS norm between them, on the device end to end, all 16
-    tokens.  Per layer, teacher-forced: the oracle's layer i runs on the GPU's
-    fp16 input to layer i; its top-k must match under the tie rule and its
-    RMS-normalised output (evaluated on the GPU's selection) must match the
-    GPU's fp16 input to layer i+1 within the tolerance.  End to end: the
-    oracle also carries its own float64 activations through all 42 layers;
-    the final error is checked for the tokens whose routing never left the
-    oracle's, and the routing flips are reported."""
+    """42 layers, RMS norm between them, all 16 tokens, through
+    moe_decode_stack_forward as the benchmark runs it (layer i's combine and
+    layer i+1's routing in one launch).  A call over the first n layers must
+    reproduce the full call's first n outputs bit for bit (its last combine is
+    the standalone one) and leaves layer n-1's routing in the buffers, whose
+    permutation must be exactly that of its selection.  Per layer,
+    teacher-forced: the oracle's layer i runs on the GPU's fp16 input to layer
+    i; its top-k must match under the tie rule and its RMS-normalised output
+    (evaluated on the GPU's selection) must match the GPU's fp16 input to
+    layer i+1 within the tolerance.  End to end: the oracle also carries its
+    own float64 activations through all 42 layers; the final error is checked
+    for the tokens whose routing never left the oracle's, and the routing
+    flips are reported."""
+    from w4_group_quantized_amd import W4MoEStack
     cfg = get_config("decode_stack")
     T, k = cfg.tokens, cfg.top_k
     layers = [device_layer(cfg, li) for li in range(cfg.layers)]
+    stack = W4MoEStack([lay[0] for lay in layers])
     x = G.activations(cfg, batch=0)
     xd = torch.from_numpy(x).cuda()
-    buf = layers[0][0].alloc(T)
-    acts = [xd] + [torch.empty_like(xd) for _ in range(cfg.layers)]
+    buf = stack.alloc(T)
+    full = _np(stack.forward(xd, buf, rmsnorm=True, eps=cfg.rms_eps))
     idx_gpu = []
-    for li, (layer, *_r) in enumerate(layers):
-        layer.forward(acts[li], buf, rmsnorm=True, eps=cfg.rms_eps, out=acts[li + 1])
-        idx_gpu.append(_np(buf.topk_idx).copy())
-    torch.cuda.synchronize()
-    acts = [_np(a).astype(np.float64) for a in acts]    # the GPU's fp16 layer inputs
+    for n in range(1, cfg.layers + 1):
+        part = _np(stack.forward(xd, buf, rmsnorm=True, eps=cfg.rms_eps, n_layers=n))
+        assert part.tobytes() == full[:n].tobytes(), f"first {n} layers differ from the full call"
+        idx = _np(buf.topk_idx).copy()
+        off, perm_src, inv_pos = O.permute(idx, cfg.num_experts)
+        np.testing.assert_array_equal(_np(buf.offsets), off)
+        np.testing.assert_array_equal(_np(buf.perm_src), perm_src)
+        np.testing.assert_array_equal(_np(buf.inv_pos), inv_pos)
+        idx_gpu.append(idx)
+    acts = [x] + [full[li] for li in range(cfg.layers)]
+    acts = [a.astype(np.float64) for a in acts]          # the GPU's fp16 layer inputs
     x_e2e = x.astype(np.float64)                         # the oracle's own activations
     alive = np.ones(T, dtype=bool)
     left_at = np.full(T, -1)

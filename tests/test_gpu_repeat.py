@@ -149,3 +149,32 @@ def test_decode_stack_graph_replay_bitwise():
     other_buf = layers[0].alloc(T)
     _replay_check(g, {f"layer {li}": acts[li + 1] for li in range(cfg.layers)}, eager,
                   lambda: step(other_acts, other_buf), replays=3)
+
+
+def test_decode_stack_call_graph_replay_bitwise():
+    """moe_decode_stack_forward over the 42 layers (the fused combine + next
+    router launches) captured into one graph: every layer's output and the
+    last layer's routing after each replay equal eager execution."""
+    from w4_group_quantized_amd import W4MoEStack
+    cfg = get_config("decode_stack")
+    T = cfg.tokens
+    stack = W4MoEStack([device_layer(cfg, li) for li in range(cfg.layers)])
+    x = to_dev(G.activations(cfg, batch=72))
+    buf = stack.alloc(T)
+    acts = torch.empty((cfg.layers, T, cfg.hidden), dtype=torch.float16, device=x.device)
+    stack.forward(x, buf, acts=acts, eps=cfg.rms_eps)
+    torch.cuda.synchronize()
+    names = ("topk_idx", "topk_w", "offsets", "perm_src", "inv_pos")
+    eager = {"acts": _np(acts).tobytes()}
+    eager.update({n: _np(getattr(buf, n)).tobytes() for n in names})
+    acts.zero_()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        stack.forward(x, buf, acts=acts, eps=cfg.rms_eps)
+    other_x = to_dev(G.activations(cfg, batch=73))
+    other_buf = stack.alloc(T)
+    static = {"acts": acts}
+    static.update({n: getattr(buf, n) for n in names})
+    _replay_check(g, static, eager, lambda: stack.forward(other_x, other_buf, eps=cfg.rms_eps),
+                  replays=3)

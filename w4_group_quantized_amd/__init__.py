@@ -6,5 +6,5 @@ fails if the library has not been built: there is no fallback.
 """
 from . import _native  # noqa: F401  (raises ImportError when libmoe_w4.so is missing)
 from ._native import MoeError, MOE_RMSNORM  # noqa: F401
-from .layer import (W4MoELayer, MoEBuffers, quantize_fp16, quantize_w8, dequantize,  # noqa: F401
-                    pack_plain)
+from .layer import (W4MoELayer, W4MoEStack, MoEBuffers, quantize_fp16, quantize_w8,  # noqa: F401
+                    dequantize, pack_plain)

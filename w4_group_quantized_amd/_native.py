@@ -31,7 +31,7 @@ MOE_RENORM = 2
 
 EXPORTS = ("moe_workspace_size", "moe_workspace_init", "moe_route", "moe_permute", "moe_route_permute",
            "moe_w4_grouped_ffn", "moe_unpermute_combine", "moe_layer_forward",
-           "moe_layer_forward_noalloc",
+           "moe_decode_stack_forward", "moe_layer_forward_noalloc",
            "moe_w4_dequant", "moe_w4_quantize", "moe_w4_pack", "moe_w8_quantize", "moe_status_str",
            "moe_last_hip_error")
 
@@ -83,6 +83,9 @@ _sigs = {
                                              ctypes.c_float, _P, _P]),
     "moe_layer_forward": (ctypes.c_int, [_LP, _P, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
                                          ctypes.c_uint32, ctypes.c_float, _P, _P, _SZ, _P]),
+    "moe_decode_stack_forward": (ctypes.c_int, [ctypes.POINTER(_LP), _I32, _P, _I32, _P, _P, _P,
+                                                _P, _P, _P, _P, ctypes.c_uint32, ctypes.c_float,
+                                                _P, _P, _SZ, _P]),
     "moe_layer_forward_noalloc": (ctypes.c_int, [_LP, _P, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
                                                  ctypes.c_uint32, ctypes.c_float, _P, _P]),
     "moe_w4_dequant": (ctypes.c_int, [_P, _P, _I64, _I64, _I32, _P, _P]),
@@ -195,6 +198,26 @@ def moe_layer_forward(layer, x, T, topk_idx, topk_w, offsets, perm_src, inv_pos,
                                  _ptr(offsets), _ptr(perm_src), _ptr(inv_pos), _ptr(x_perm),
                                  _ptr(y_perm), _ptr(y_shared), flags, eps, _ptr(out), _ptr(ws),
                                  ws_bytes, _stream(stream)))
+
+
+def layer_array(layers):
+    """A host array of pointers to the given MoeLayer descriptions (keep the
+    returned object alive while a call uses it)."""
+    arr = (_LP * len(layers))(*[ctypes.pointer(d) for d in layers])
+    arr._keep = list(layers)
+    return arr
+
+
+def moe_decode_stack_forward(layers, x, T, topk_idx, topk_w, offsets, perm_src, inv_pos, y_perm,
+                             y_shared, flags, eps, acts, ws, ws_bytes, stream=None, n_layers=None):
+    """layers: a sequence of MoeLayer, or an array made by layer_array."""
+    arr = layers if isinstance(layers, ctypes.Array) else layer_array(layers)
+    n = len(arr) if n_layers is None else n_layers
+    _check("moe_decode_stack_forward",
+           lib.moe_decode_stack_forward(arr, n, _ptr(x), T, _ptr(topk_idx), _ptr(topk_w),
+                                        _ptr(offsets), _ptr(perm_src), _ptr(inv_pos),
+                                        _ptr(y_perm), _ptr(y_shared), flags, eps, _ptr(acts),
+                                        _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def moe_layer_forward_noalloc(layer, x, T, topk_idx, topk_w, offsets, perm_src, inv_pos, x_perm,

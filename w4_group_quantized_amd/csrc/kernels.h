@@ -20,6 +20,12 @@ constexpr int kFusedMaxLogits = 8192;   // T * E held in LDS by the fused router
 // The counter block at the start of every workspace (moe_workspace_init
 // zero-fills it; every call leaves it at zero).
 constexpr size_t kWsSyncBytes = 256;
+// Words of that block: word 0 is the one-launch router's counter; the launch
+// that fuses a layer's combine with the next layer's router uses word 1 (all
+// tokens) and words 32 .. 32+T-1 (one per token), hence at most 32 tokens.
+constexpr int kStackAllCounter = 1;
+constexpr int kStackTokCounter = 32;
+constexpr int kStackMaxT = 32;
 
 // Byte offsets of the per-call scratch regions inside the caller's workspace.
 struct WsLayout {
@@ -63,5 +69,17 @@ hipError_t launch_ffn_prefill_phase(const moe_layer &L, int phase, const uint16_
 hipError_t launch_combine(const moe_layer &L, const uint16_t *y_perm, const uint16_t *y_shared,
                           const int32_t *inv_pos, const float *w, int32_t T, uint32_t flags,
                           float eps, uint16_t *out, hipStream_t st);
+// Whether a stacked decode step can fuse layer i's combine with layer i+1's
+// router for T tokens of layers shaped like L.
+bool stack_fused(const moe_layer &L, int32_t T);
+// Layer cur's combine (flags, eps as in launch_combine) into out, then layer
+// next's router, top-k and permutation on out, in one launch.  inv_pos and
+// topk_w are read as layer cur's and overwritten with layer next's.
+hipError_t launch_combine_route(const moe_layer &cur, const moe_layer &next,
+                                const uint16_t *y_perm, const uint16_t *y_shared,
+                                int32_t *inv_pos, float *topk_w, int32_t T, uint32_t flags,
+                                float eps, uint16_t *out, int32_t *topk_idx, int32_t *offsets,
+                                int32_t *perm_src, float *logits, unsigned int *sync,
+                                hipStream_t st);
 
 }  // namespace moe

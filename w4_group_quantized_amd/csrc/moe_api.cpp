@@ -185,6 +185,45 @@ static moe_status run_layer(const moe_layer &L, const uint16_t *x, int32_t T, in
   return hip_status(e);
 }
 
+// A decode step through n stacked layers of one shape on `st` (arguments
+// checked): layer i reads in_i (x, then the previous layer's output) and
+// writes acts[i].  When stack_fused allows, layer i's combine and layer i+1's
+// routing share one launch; otherwise each layer runs as run_layer does.
+static moe_status run_stack(const moe_layer *const *layers, int32_t n, const uint16_t *x,
+                            int32_t T, int32_t *topk_idx, float *topk_w, int32_t *offsets,
+                            int32_t *perm_src, int32_t *inv_pos, uint16_t *y_perm, uint16_t *ys,
+                            uint32_t flags, float eps, uint16_t *acts, char *base,
+                            hipStream_t st) {
+  const moe_layer &L0 = *layers[0];
+  const WsLayout w = ws_layout(L0, T);
+  const size_t HT = (size_t)T * (size_t)L0.hidden;
+  const bool fused = stack_fused(L0, T);
+  uint16_t *h = reinterpret_cast<uint16_t *>(base + w.h);
+  uint16_t *hs = reinterpret_cast<uint16_t *>(base + w.h_shared);
+  hipError_t e = run_route_permute(L0, x, T, topk_idx, topk_w, offsets, perm_src, inv_pos,
+                                   nullptr, base, w, st);
+  const uint16_t *in = x;
+  for (int32_t i = 0; i < n && e == hipSuccess; ++i) {
+    const moe_layer &L = *layers[i];
+    uint16_t *out = acts + (size_t)i * HT;
+    e = launch_ffn(L, in, nullptr, perm_src, offsets, T, y_perm, ys, h, hs, st);
+    if (e != hipSuccess) break;
+    if (fused && i + 1 < n) {
+      e = launch_combine_route(L, *layers[i + 1], y_perm, ys, inv_pos, topk_w, T, flags, eps,
+                               out, topk_idx, offsets, perm_src,
+                               reinterpret_cast<float *>(base + w.logits),
+                               reinterpret_cast<unsigned int *>(base + w.sync), st);
+    } else {
+      e = launch_combine(L, y_perm, ys, inv_pos, topk_w, T, flags, eps, out, st);
+      if (e == hipSuccess && i + 1 < n)
+        e = run_route_permute(*layers[i + 1], out, T, topk_idx, topk_w, offsets, perm_src,
+                              inv_pos, nullptr, base, w, st);
+    }
+    in = out;
+  }
+  return hip_status(e);
+}
+
 // Every argument of a whole-layer call but the workspace.
 static moe_status check_layer_call(const moe_layer *L, const uint16_t *x, int32_t T,
                                    const int32_t *topk_idx, const float *topk_w,
@@ -358,6 +397,35 @@ moe_status moe_layer_forward(const moe_layer *L, const uint16_t *x, int32_t T, i
   clear_stale_hip_error();
   return run_layer(*L, x, T, topk_idx, topk_w, offsets, perm_src, inv_pos, x_perm, y_perm,
                    L->shared_ffn > 0 ? y_shared : nullptr, flags, eps, out,
+                   static_cast<char *>(ws), (hipStream_t)stream);
+}
+
+moe_status moe_decode_stack_forward(const moe_layer *const *layers, int32_t n_layers,
+                                    const uint16_t *x, int32_t T, int32_t *topk_idx,
+                                    float *topk_w, int32_t *offsets, int32_t *perm_src,
+                                    int32_t *inv_pos, uint16_t *y_perm, uint16_t *y_shared,
+                                    uint32_t flags, float eps, uint16_t *acts, void *ws,
+                                    size_t ws_bytes, void *stream) {
+  if (!layers || n_layers < 1) return MOE_EINVAL;
+  moe_status s;
+  const moe_layer *L0 = layers[0];
+  for (int32_t i = 0; i < n_layers; ++i) {
+    const moe_layer *L = layers[i];
+    if ((s = check_layer(L)) != MOE_OK) return s;
+    if (L->num_experts != L0->num_experts || L->hidden != L0->hidden || L->ffn != L0->ffn ||
+        L->top_k != L0->top_k || L->shared_ffn != L0->shared_ffn)
+      return MOE_EUNSUPPORTED;
+  }
+  if ((s = check_tokens(L0, T)) != MOE_OK) return s;
+  if (T == 0) return MOE_OK;
+  for (int32_t i = 0; i < n_layers; ++i)
+    if ((s = check_layer_call(layers[i], x, T, topk_idx, topk_w, offsets, perm_src, inv_pos,
+                              nullptr, y_perm, y_shared, flags, eps, acts)) != MOE_OK)
+      return s;
+  if ((s = check_ws(L0, T, ws, ws_bytes)) != MOE_OK) return s;
+  clear_stale_hip_error();
+  return run_stack(layers, n_layers, x, T, topk_idx, topk_w, offsets, perm_src, inv_pos, y_perm,
+                   L0->shared_ffn > 0 ? y_shared : nullptr, flags, eps, acts,
                    static_cast<char *>(ws), (hipStream_t)stream);
 }
 

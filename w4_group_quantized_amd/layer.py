@@ -148,6 +148,50 @@ class W4MoELayer:
         return buf.out[:T] if out is None else out
 
 
+class W4MoEStack:
+    """Stacked layers of one shape (the same experts, hidden, ffn, top-k and
+    shared ffn) run as one decode step, the output of each layer being the
+    input of the next: moe_decode_stack_forward."""
+
+    def __init__(self, layers):
+        self.layers = list(layers)
+        if not self.layers:
+            raise ValueError("a stack needs at least one layer")
+        l0 = self.layers[0]
+        for layer in self.layers:
+            if (layer.E, layer.H, layer.F, layer.k, layer.Fs) != (l0.E, l0.H, l0.F, l0.k, l0.Fs):
+                raise ValueError("stacked layers must share experts, hidden, ffn, top-k and "
+                                 "shared ffn")
+        self.arr = N.layer_array([layer.desc for layer in self.layers])
+
+    def alloc(self, max_tokens: int) -> MoEBuffers:
+        return self.layers[0].alloc(max_tokens)
+
+    def forward(self, x, buf, acts=None, T=None, rmsnorm=True, eps=1e-6, renorm=False,
+                n_layers=None, stream=None):
+        """x fp16 [T, H] on the device -> acts fp16 [n_layers, T, H], every
+        layer's output (the last one is the step's output).  The routing
+        buffers of `buf` hold the last layer's routing afterwards."""
+        T = x.shape[0] if T is None else T
+        if T > buf.max_tokens:
+            raise ValueError("more tokens than the buffers were allocated for")
+        n = len(self.layers) if n_layers is None else n_layers
+        if not 1 <= n <= len(self.layers):
+            raise ValueError("n_layers out of range")
+        H = self.layers[0].H
+        if acts is None:
+            acts = torch.empty((n, T, H), dtype=torch.float16, device=x.device)
+        if acts.dtype != torch.float16 or not acts.is_contiguous() or \
+                tuple(acts.shape[1:]) != (T, H) or acts.shape[0] < n:
+            raise ValueError("acts must be contiguous fp16 [n_layers, T, H]")
+        flags = (N.MOE_RMSNORM if rmsnorm else 0) | (N.MOE_RENORM if renorm else 0)
+        N.moe_decode_stack_forward(self.arr, x, T, buf.topk_idx, buf.topk_w, buf.offsets,
+                                   buf.perm_src, buf.inv_pos, buf.y_perm,
+                                   buf.y_shared if self.layers[0].Fs else None, flags, eps, acts,
+                                   buf.ws, buf.ws.numel(), stream, n_layers=n)
+        return acts
+
+
 def quantize_fp16(w: torch.Tensor, group_size: int = 128, stream=None):
     """Group-quantize an fp16 device matrix [rows, cols] with the HIP kernel.
 
