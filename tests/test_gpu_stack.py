@@ -110,6 +110,40 @@ def test_stack_group_size_64_and_8bit_shared_expert():
     check_stack(get_config("decode_fine", **FINE), 3, 16, w8=True, batch=5)
 
 
+def test_stack_mixed_group_sizes_and_shared_formats():
+    """Layers of one stack may differ in group size and in the shared
+    expert's format (only the shapes must agree)."""
+    from w4_group_quantized_amd import W4MoEStack
+    T = 10
+    cfgs = [get_config("decode_fine", group_size=gs, **FINE) for gs in (128, 64, 256)]
+    layers, refs = [], []
+    for li, cfg in enumerate(cfgs):
+        mats, experts = quantized_experts(cfg, layer=li)
+        wr, b = G.router(cfg, li)
+        shared = G.shared_expert(cfg, li)
+        if li == 1:
+            stored, deq = shared_w8(shared)
+            layers.append(make_gpu_layer(cfg, mats, wr, b, None, w8=stored))
+            refs.append((cfg, wr, b, experts, deq))
+        else:
+            layers.append(make_gpu_layer(cfg, mats, wr, b, shared))
+            refs.append((cfg, wr, b, experts, shared))
+    stack = W4MoEStack(layers)
+    x = G.activations(cfgs[0], tokens=T, batch=11)
+    buf = stack.alloc(T)
+    acts = _np(stack.forward(to_dev(x), buf, eps=cfgs[0].rms_eps))
+    for n in range(1, len(layers) + 1):
+        part = _np(stack.forward(to_dev(x), buf, eps=cfgs[0].rms_eps, n_layers=n))
+        assert part.tobytes() == acts[:n].tobytes()
+        cfg, wr, b, experts, sh = refs[n - 1]
+        xin = x if n == 1 else acts[n - 2]
+        idx = _np(buf.topk_idx)[:T]
+        ref = on_gpu_selection(oracle_layer(xin, wr, b, experts, cfg, sh), idx,
+                               lambda i: oracle_layer(xin, wr, b, experts, cfg, sh, idx=i),
+                               cfg.top_k)
+        tol_check(acts[n - 1], O.rmsnorm(ref["out"], cfg.rms_eps), f"mixed stack layer {n - 1}")
+
+
 def test_stack_without_shared_expert():
     """16 experts, top-4, no shared expert (the coarse layer's routing law)."""
     check_stack(get_config("decode_coarse", num_experts=16, hidden=512, ffn=256, top_k=4), 3, 16,
@@ -118,8 +152,10 @@ def test_stack_without_shared_expert():
 
 @pytest.mark.parametrize("E,k,T", [(288, 8, 16), (288, 8, 32), (1024, 32, 4), (40, 1, 11)])
 def test_stack_expert_tiles(E, k, T):
-    """The 288-expert router's tiles (32 experts per block, 9 tiles, tile 8
-    sharing XCD 0), 1024 experts at top-32 (64 per block), and top-1."""
+    """Expert tiles sized to give every CU one block: 288 experts at 16
+    tokens (18 per block, 16 tiles, two per XCD) and at 32 (36 per block, 8
+    tiles, more than one expert per wave), 1024 experts at top-32 (16 per
+    block, 64 tiles), and top-1 over 40 experts."""
     cfg = get_config("decode_fine", num_experts=E, hidden=256, ffn=128, top_k=k, shared_ffn=128)
     check_stack(cfg, 3, T, batch=7 + T)
 
