@@ -93,8 +93,9 @@ __global__ __launch_bounds__(kStackWaves *kWave) void combine_route_kernel(Combi
   // The router rows do not depend on the combine: the first 512 chunks (8
   // per lane) of the wave's first two experts are loaded as soon as the
   // combine's own row loads are out (a CU serves its loads in issue order,
-  // and the 256 KB of router rows would otherwise hold the combine's loads
-  // back).  Wave w takes experts e0 + w, e0 + w + 16, ...; lane l the
+  // and the block's router rows, 144 KB at 16 tokens, would otherwise hold
+  // the combine's loads back).  Wave w takes experts e0 + w, e0 + w + 16,
+  // ...; lane l the
   // 8-column chunks l, l + 64, ... of the row (each load instruction reads
   // 1 KB of a router row).
   const int e0 = et * p.eb, e_end = min(e0 + p.eb, E);
