@@ -46,8 +46,8 @@
  *    MOE_OK and launches nothing.
  *  - Two calls that share a workspace must not run concurrently.  Prepare a
  *    workspace once before its first use with moe_workspace_init (or zero-fill
- *    its first 256 bytes): they hold a synchronization counter that every call
- *    leaves at zero.  A workspace whose counter is not zero makes
+ *    its first 16384 bytes): they hold synchronization counters that every
+ *    call leaves at zero.  A workspace whose counter is not zero makes
  *    moe_route_permute and moe_layer_forward write no routing (no error can be
  *    reported without reading device memory on the host).
  *
@@ -150,9 +150,9 @@ typedef struct moe_layer {
  * the layer description is invalid.  `layer` is a host pointer. */
 size_t moe_workspace_size(const moe_layer *layer, int32_t max_tokens);
 
-/* Prepare a workspace for its first use: zero-fills its first 256 bytes (the
+/* Prepare a workspace for its first use: zero-fills its first 16384 bytes (the
  * counter block) with a kernel on `stream` (no memset, so the call may also be
- * captured into a graph).  ws_bytes below 256: MOE_EWORKSPACE; ws NULL or
+ * captured into a graph).  ws_bytes below 16384: MOE_EWORKSPACE; ws NULL or
  * misaligned: MOE_EINVAL.  Calls after the first leave the block at zero, so
  * one init per workspace is enough (again after a run that was aborted). */
 moe_status moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
@@ -230,7 +230,10 @@ moe_status moe_route_permute(const moe_layer *layer, const uint16_t *x, int32_t 
  * F*H/2 are all below 2^31 (they address activations and one expert's
  * weights with 32-bit offsets); otherwise the decode kernels do, which are
  * correct at any size but read each expert's weights once per 16 rows of its
- * segment, so a large batch outside those limits runs far slower. */
+ * segment, so a large batch outside those limits runs far slower.  For up to
+ * 16 tokens the decode kernels may split the in_features of each product over
+ * several blocks whose fp32 partial sums are added in a fixed order (the
+ * workspace holds them; outputs stay bitwise reproducible). */
 moe_status moe_w4_grouped_ffn(const moe_layer *layer, const uint16_t *x,
                               const uint16_t *x_perm, const int32_t *perm_src,
                               const int32_t *offsets, int32_t T,

@@ -247,6 +247,6 @@ def test_pack_arguments():
 
 def test_workspace_init_arguments():
     init = N.lib.moe_workspace_init
-    assert init(FAKE, 255, None) == EWS
-    assert init(None, 256, None) == EINVAL
-    assert init(MISALIGNED, 4096, None) == EINVAL
+    assert init(FAKE, 16383, None) == EWS
+    assert init(None, 16384, None) == EINVAL
+    assert init(MISALIGNED, 16384, None) == EINVAL

@@ -22,7 +22,7 @@ from workloads import get_config
 from workloads import gen as G
 from workloads import gen_torch as GT
 
-from gpu_util import gpu, require_gpu, tol_check, route_compare
+from gpu_util import gpu, require_gpu, tol_check, route_compare, shared_w8
 
 pytestmark = gpu
 
@@ -36,16 +36,23 @@ def _np(t):
     return t.detach().cpu().numpy()
 
 
-def device_layer(cfg, layer_idx=0):
+def device_layer(cfg, layer_idx=0, w8=False):
+    """w8: the shared expert stored in 8 bits (quantized by the oracle); the
+    returned shared weights are then its float64 dequantized matrices."""
     from w4_group_quantized_amd import W4MoELayer
     dev = torch.device("cuda:0")
     mats = GT.layer_codes(cfg, layer_idx, dev)
     wr, b = G.router(cfg, layer_idx)
     shared = G.shared_expert(cfg, layer_idx)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    s8 = None
+    if w8:
+        stored, shared = shared_w8(shared)
+        s8 = tuple((t(q), t(sc)) for q, sc in stored)
     layer = W4MoELayer(cfg.top_k, t(wr), t(b) if b is not None else None, mats["gate_q"],
                        mats["gate_s"], mats["up_q"], mats["up_s"], mats["down_q"], mats["down_s"],
-                       shared=tuple(t(w) for w in shared) if shared is not None else None)
+                       shared=tuple(t(w) for w in shared) if shared is not None and not w8
+                       else None, shared_w8=s8)
     return layer, mats, wr, b, shared
 
 
@@ -112,6 +119,34 @@ def test_full_size_layer(name, n_sample):
     print(f"[{name}] tokens checked {len(toks)}/{T}  max err {err:.3e} (bound {bound:.3e})")
 
 
+@pytest.mark.parametrize("name,T,w8", [("decode_fine", 1, False), ("decode_fine", 1, True),
+                                       ("decode_fine", 2, False), ("decode_fine", 3, False),
+                                       ("decode_fine512", 1, False), ("decode_fine512", 2, False),
+                                       ("decode_fine512", 4, False), ("decode_coarse", 1, False)])
+def test_full_size_small_batches(name, T, w8):
+    """Batches of a few tokens.  Where whole items would leave some CUs
+    streaming two of them while others idle, the decode FFN splits each
+    item's in_features over several blocks and adds their fp32 partial sums
+    in a fixed order: the gate/up launch at one token on the 288-expert layer,
+    the down launch at one token on the coarse layer; the other cases run
+    whole.  Every token against the oracle, after the permutation check."""
+    cfg = get_config(name, tokens=T)
+    layer, mats, wr, b, shared = device_layer(cfg, w8=w8)
+    x = G.activations(cfg, batch=20 + T)
+    buf = layer.alloc(T)
+    out = _np(layer.forward(torch.from_numpy(x).cuda(), buf)).astype(np.float64)
+    torch.cuda.synchronize()
+    idx_gpu = _np(buf.topk_idx)
+    off, perm_src, inv_pos = O.permute(idx_gpu, cfg.num_experts)
+    np.testing.assert_array_equal(_np(buf.offsets), off)
+    np.testing.assert_array_equal(_np(buf.perm_src), perm_src)
+    np.testing.assert_array_equal(_np(buf.inv_pos), inv_pos)
+    ref = checked_tokens(x.astype(np.float64), wr, b, cfg.top_k, DeviceExperts(mats), shared,
+                         idx_gpu)
+    err, bound = tol_check(out, ref, f"{name} {T} token(s)")
+    print(f"[{name} T={T}] max err {err:.3e} (bound {bound:.3e})")
+
+
 def test_full_size_prefill_whole_segments():
     """The prefill layer at full shape (8192 tokens, 128 experts): every row
     of the FFN stage's output y_perm for whole segments: the largest, the
@@ -174,8 +209,10 @@ def test_full_size_prefill_whole_segments():
               f"(bound {bound:.3e})", flush=True)
 
 
-def test_full_size_decode_stack():
-    """42 layers, RMS norm between them, all 16 tokens, through
+@pytest.mark.parametrize("T", [16, 1])
+def test_full_size_decode_stack(T):
+    """42 layers, RMS norm between them, all 16 tokens (and one token: the
+    K-split FFN in every layer), through
     moe_decode_stack_forward as the benchmark runs it (layer i's combine and
     layer i+1's routing in one launch).  A call over the first n layers must
     reproduce the full call's first n outputs bit for bit (its last combine is
@@ -189,8 +226,8 @@ def test_full_size_decode_stack():
     for the tokens whose routing never left the oracle's, and the routing
     flips are reported."""
     from w4_group_quantized_amd import W4MoEStack
-    cfg = get_config("decode_stack")
-    T, k = cfg.tokens, cfg.top_k
+    cfg = get_config("decode_stack", tokens=T)
+    k = cfg.top_k
     layers = [device_layer(cfg, li) for li in range(cfg.layers)]
     stack = W4MoEStack([lay[0] for lay in layers])
     x = G.activations(cfg, batch=0)

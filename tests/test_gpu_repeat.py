@@ -87,6 +87,27 @@ def test_route_permute_thousand_calls_bitwise_stable(T):
         assert bad.numel() == 0, f"{n}: call {int(bad[0])} of {n_calls} differs from the first"
 
 
+@pytest.mark.parametrize("name,T", [("decode_fine", 1), ("decode_coarse", 1)])
+def test_split_ffn_repeated_calls_bitwise(name, T):
+    """The decode FFN's K-split blocks hand their partial sums across the XCDs
+    through per-item tickets that every call leaves at zero: 300 whole-layer
+    calls in a row give the first call's outputs bit for bit."""
+    cfg = get_config(name, tokens=T)
+    layer = device_layer(cfg)
+    x = to_dev(G.activations(cfg, batch=70 + T))
+    buf = layer.alloc(T)
+    first = layer.forward(x, buf).clone()
+    n_calls = 300
+    hist = torch.empty((n_calls,) + tuple(first.shape), dtype=first.dtype, device=x.device)
+    for i in range(n_calls):
+        hist[i].copy_(layer.forward(x, buf))
+    torch.cuda.synchronize()
+    same = (hist.view(n_calls, -1).view(torch.int16) ==
+            first.view(1, -1).view(torch.int16)).all(dim=1)
+    bad = torch.nonzero(~same)
+    assert bad.numel() == 0, f"call {int(bad[0])} of {n_calls} differs from the first"
+
+
 def _replay_check(g, static_out, eager_out, eager_work, replays=4):
     for r in range(replays):
         eager_work()                     # the program's own eager launches in between
@@ -97,10 +118,11 @@ def _replay_check(g, static_out, eager_out, eager_work, replays=4):
             assert _np(got).tobytes() == eager_out[name], f"replay {r}: {name} differs"
 
 
-@pytest.mark.parametrize("T", [8, 16])
+@pytest.mark.parametrize("T", [1, 8, 16])
 def test_layer_graph_replay_bitwise(T):
     """moe_layer_forward at the fine-grained decode shape (288 experts + shared,
-    hidden 4096, ffn 1536) captured once, replayed four times."""
+    hidden 4096, ffn 1536) captured once, replayed four times (at one token
+    with the FFN's K split over blocks and its per-item tickets)."""
     cfg = get_config("decode_fine", tokens=T)
     layer = device_layer(cfg)
     x = to_dev(G.activations(cfg, batch=60 + T))

@@ -69,8 +69,9 @@ def test_noalloc_matches_layer_forward_scaled_down():
 
 @gpu
 def test_noalloc_matches_layer_forward_full_decode_shape():
-    """288 experts + shared expert, hidden 4096, ffn 1536, top-8: 16 then 8
-    tokens, with the RMS norm of the stacked layers."""
+    """288 experts + shared expert, hidden 4096, ffn 1536, top-8: 16, 8, then
+    1 token (whose FFN keeps its K-split partial sums and tickets in the fixed
+    array), with the RMS norm of the stacked layers."""
     require_gpu()
     from w4_group_quantized_amd import W4MoELayer
     cfg = get_config("decode_stack", layers=1)
@@ -82,7 +83,7 @@ def test_noalloc_matches_layer_forward_full_decode_shape():
                        mats["up_q"], mats["up_s"], mats["down_q"], mats["down_s"],
                        shared=tuple(to_dev(w) for w in shared))
     buf_ref, buf_na = layer.alloc(16), layer.alloc(16)
-    for T in (16, 8):
+    for T in (16, 8, 1):
         xd = to_dev(G.activations(cfg, tokens=T, batch=90 + T))
         layer.forward(xd, buf_ref, T, rmsnorm=True, eps=cfg.rms_eps)
         noalloc_forward(layer, xd, buf_na, T, rmsnorm=True, eps=cfg.rms_eps)

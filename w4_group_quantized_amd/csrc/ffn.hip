@@ -29,6 +29,13 @@
 // The grid is sized for the worst case on the host; items past the live
 // segment tiles exit right after locating themselves (nothing is read back to
 // the host between calls).
+//
+// Batches of a few tokens whose items would leave some CUs streaming two of
+// them while others idle after one split each item's K range over several
+// blocks (the host's rule is with launch_ffn), so that every CU streams about
+// the same number of bytes: a CU reads ~20 GB/s whether it holds one block or
+// three.  The item's last block to finish adds the fp32 partial sums of its
+// parts in the fixed order 0, 1, ..., P-1.
 #include "common.h"
 #include "kernels.h"
 #include "tiles.h"
@@ -56,9 +63,81 @@ struct FfnArgs {
   int shared_w8;
   f16 *out_routed;                  // phase 1: h [N, F];      phase 2: y_perm [N, H]
   f16 *out_shared;                  // phase 1: h_shared;      phase 2: y_shared
-  int shared_items;                 // shared-expert items (blocks 0 .. shared_items-1)
-  int routed_items;                 // worst-case number of routed items (the blocks after)
+  int shared_items;                 // shared-expert items (their blocks first)
+  int routed_items;                 // worst-case number of routed items (their blocks after)
+  int rparts, sparts;               // blocks per routed / shared item (K parts; 1 = whole K)
+  int tm;                           // token rows per tile kept in the partial sums
+  float *part;                      // K-split partial sums: [block][wave][tile][tm][16]
+  unsigned int *ticket;             // per item (shared items first): parts done, zero between calls
 };
+
+constexpr int kMaxParts = 8;
+
+// K split over blocks: every block of an item stores the partial sums of the
+// tile rows of its live tokens, and the last block of the item to take a
+// ticket adds the parts in the fixed order 0 .. nparts-1 into acc.  The stores
+// are agent-scope atomic stores (written through to the device coherence
+// point); waiting for them before the barrier that precedes the ticket orders
+// them before it, and the last block reads them with coherent (sc1) loads, as
+// the one-launch router does with its logits.  Every wave of the block calls
+// this; has_acc: this wave holds partial sums (with the K range split over the
+// waves inside the block, only wave 0 after the in-block reduction).  Returns
+// false in every block but the last, which also resets the ticket.
+template <int NTL>
+__device__ bool split_sum(f32x4 (&acc)[NTL], bool has_acc, int rows, int tm, float *item_part,
+                          int blk_floats, int kpart, int nparts, unsigned int *ticket) {
+  __shared__ int s_last;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  const int r = lane & 15, kb = lane >> 4;
+  const int wave_floats = NTL * tm * 16;
+  if (has_acc) {
+    float *dst = item_part + (size_t)kpart * blk_floats + wid * wave_floats;
+#pragma unroll
+    for (int i = 0; i < NTL; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tok = 4 * kb + j;
+        if (tok < rows)
+          __hip_atomic_store(dst + (i * tm + tok) * 16 + r, acc[i][j], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (unsigned)(nparts - 1);
+  __syncthreads();
+  if (!s_last) return false;
+  if (threadIdx.x == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (has_acc) {
+    const rsrc_t rs = make_rsrc(item_part, (uint32_t)(nparts * blk_floats) * 4u);
+#pragma unroll
+    for (int i = 0; i < NTL; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tok = 4 * kb + j;
+        // parts past nparts and rows past the tile read zeros (out of range)
+        float v[kMaxParts];
+#pragma unroll
+        for (int q = 0; q < kMaxParts; ++q) {
+          const uint32_t off = tok < rows && q < nparts
+                                   ? (uint32_t)(q * blk_floats + wid * wave_floats +
+                                                (i * tm + tok) * 16 + r) * 4u
+                                   : ARows::kPadOffset;
+          v[q] = __builtin_bit_cast(float,
+                                    __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, kBufCoherent));
+        }
+        float sum = v[0];
+#pragma unroll
+        for (int q = 1; q < kMaxParts; ++q)
+          if (q < nparts) sum += v[q];
+        acc[i][j] = sum;
+      }
+  }
+  return true;
+}
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
@@ -115,8 +194,12 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
   __shared__ float red[3 * 2 * 4 * kWave];
   __shared__ u32x4 s_act[kActLdsVec];
 
-  if ((int)blockIdx.x >= p.shared_items) {
-    const int item = blockIdx.x - p.shared_items;
+  const int sblocks = p.shared_items * p.sparts;
+  // partial-sum floats per block (routed and shared blocks alike)
+  const int blk_floats = 4 * kMats * NT * p.tm * 16;
+  if ((int)blockIdx.x >= sblocks) {
+    const int rb = blockIdx.x - sblocks;
+    const int item = rb / p.rparts, kpart = rb - item * p.rparts;
     const int ntiles = Nrows / (64 * NT);
     const int slot = item / ntiles, nt = item % ntiles;
     int e, mt;
@@ -145,6 +228,7 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
     f32x4 acc[kMats * NT];
 #pragma unroll
     for (int t = 0; t < kMats * NT; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    const int g0 = kpart * G / p.rparts, g1 = (kpart + 1) * G / p.rparts;
     const int KB = K * 2;                 // bytes per activation row
     if (rows * KB <= kActLdsBytes) {      // block-uniform
       // Stage the tile's token rows in LDS once for the four waves: the
@@ -179,7 +263,7 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
 #pragma unroll
       for (int j = 0; j < kStagePieces; ++j) stg[j] = bload16(rs, voff[j], 0);
       const ALds<kActLdsVec> al(s_act, min(r, rows - 1), stride, kb);
-      w4_tiles<kMats * NT, S, GM, STREAM>(al, qrow, srow, 0, G, acc, [&] {
+      w4_tiles<kMats * NT, S, GM, STREAM>(al, qrow, srow, g0, g1, acc, [&] {
 #pragma unroll
         for (int j = 0; j < kStagePieces; ++j) {
           const int i = j * 256 + tid;
@@ -201,8 +285,13 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
       const ARows arow = p.perm_src
                              ? ARows(p.a_routed, p.T, K, tok, live, kb)
                              : ARows(p.a_routed + (size_t)seg0 * K, rows, K, tok, live, kb);
-      w4_tiles<kMats * NT, S, GM, STREAM>(arow, qrow, srow, 0, G, acc);
+      w4_tiles<kMats * NT, S, GM, STREAM>(arow, qrow, srow, g0, g1, acc);
     }
+    if (p.rparts > 1 &&
+        !split_sum<kMats * NT>(acc, true, rows, p.tm,
+                               p.part + (size_t)(sblocks + item * p.rparts) * blk_floats,
+                               blk_floats, kpart, p.rparts, p.ticket + p.shared_items + item))
+      return;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -220,7 +309,7 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
   const int Ks = kPair ? p.H : p.Fs;
   const int Ns = kPair ? p.Fs : p.H;
   const int Gs = Ks / kGroup;
-  const int sitem = blockIdx.x;
+  const int sitem = blockIdx.x / p.sparts, spart = blockIdx.x - sitem * p.sparts;
   const int sntiles = Ns / 16;
   const int mt = sitem / sntiles, nt = sitem % sntiles;
   const int tok0 = mt * kTileM;
@@ -231,7 +320,9 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
   f32x4 acc[kMats];
 #pragma unroll
   for (int t = 0; t < kMats; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  const int g0 = wid * Gs / 4, g1 = (wid + 1) * Gs / 4;
+  // this block's part of K, split again over its 4 waves
+  const int lo = spart * Gs / p.sparts, hi = (spart + 1) * Gs / p.sparts;
+  const int g0 = lo + wid * (hi - lo) / 4, g1 = lo + (wid + 1) * (hi - lo) / 4;
   if (p.shared_w8) {     // block-uniform: 8-bit codes, 16-row tile nt
     const size_t tile = (size_t)nt * 16;
     const uint8_t *qrow[kMats];
@@ -250,6 +341,11 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
     f16_tiles<kMats>(arow, wrow, kb, g0, g1, acc);
   }
   ksplit_reduce<kMats>(acc, red);
+  if (p.sparts > 1 &&
+      !split_sum<kMats>(acc, wid == 0, rows, p.tm,
+                        p.part + (size_t)sitem * p.sparts * blk_floats, blk_floats, spart,
+                        p.sparts, p.ticket + sitem))
+    return;
   if (wid != 0) return;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -297,25 +393,179 @@ bool ffn_prefill_mode(const moe_layer &L, int32_t T) {
          N * H * 2 < max_bytes && N * F * 2 < max_bytes && F * H / 2 < max_bytes;
 }
 
+// K split for small batches.  The dispatcher places the first blocks of a
+// launch round-robin, block b on CU b % kCus, as many per CU as fit (3 for
+// these kernels, 4 for the 256-row down tiles), and each CU streams ~18-22
+// GB/s however many of its slots are busy, so a launch takes about as long
+// as its busiest CU needs for its bytes.  One token on the 288-expert layer
+// gives 288 gate/up items of ~260 KB: 32 CUs stream two of them while the
+// rest idle after one.  For up to kSplitMaxT tokens, when the unsplit live
+// items fit one round of slots, the parts (routed, shared) that minimise the
+// busiest CU's bytes, counting kSplitCostBytes for the block starts and the
+// partial-sum round trip of a split, are chosen among those whose blocks
+// still fit one round and hold at least kSplitMinBytes.  Measured at one
+// token (interleaved A/B): the 42-layer step 2.21 -> 1.92 ms (gate/up 3
+// routed x 2 shared parts, its launch 26.4 -> 21-22 us), the coarse layer
+// 0.885 -> 0.847 ms (down in 2 parts).  Left whole by the rule, and slower
+// when split: the balanced down launch of the 288-expert layer, the
+// 512-expert layer's launches (fewer items than CUs) and the gate/up launch
+// with the 8-bit shared expert (2-5% slower in 2 routed parts), which sets
+// kSplitCostBytes.
+constexpr int kCus = 256;
+constexpr int kSplitMaxT = 4;
+constexpr int64_t kSplitMinBytes = 48 << 10;
+constexpr int64_t kSplitCostBytes = 160 << 10;
+
+// Bytes of the busiest CU when ns blocks of sb bytes and then nr blocks of rb
+// bytes (at most slots * kCus in all) are placed on CU b % kCus.  A CU's load
+// only changes where c + j * kCus crosses ns or ns + nr, so those points (and
+// 0) are the only ones to evaluate.
+static int64_t busiest_cu(int64_t ns, int64_t sb, int64_t nr, int64_t rb, int slots) {
+  const int64_t n = ns + nr;
+  auto load = [&](int64_t c) {
+    int64_t v = 0;
+    for (int j = 0; j < slots; ++j) {
+      const int64_t b = c + (int64_t)j * kCus;
+      v += b < ns ? sb : (b < n ? rb : 0);
+    }
+    return v;
+  };
+  int64_t m = load(0);
+  for (int j = 0; j < slots; ++j)
+    for (int64_t edge : {ns, n})
+      for (int64_t c : {edge - (int64_t)j * kCus - 1, edge - (int64_t)j * kCus})
+        if (c >= 0 && c < kCus) {
+          const int64_t v = load(c);
+          m = v > m ? v : m;
+        }
+  return m;
+}
+
+// nr live routed items of rb bytes (at most max_rp parts) and ns shared items
+// of sb bytes (at most max_sp parts) -> parts per item.
+static void split_parts(int64_t nr, int64_t rb, int max_rp, int64_t ns, int64_t sb, int max_sp,
+                        int slots, int *rp, int *sp) {
+  *rp = *sp = 1;
+  const int64_t round = (int64_t)slots * kCus;
+  if (nr + ns > round) return;
+  int64_t best = busiest_cu(ns, sb, nr, rb, slots);
+  for (int r = 1; r <= max_rp && r <= kMaxParts; ++r)
+    for (int q = 1; q <= (ns ? max_sp : 1) && q <= kMaxParts; ++q) {
+      if ((r == 1 && q == 1) || nr * r + ns * q > round) continue;
+      if ((r > 1 && rb / r < kSplitMinBytes) || (q > 1 && sb / q < kSplitMinBytes)) continue;
+      const int64_t c = busiest_cu(ns * q, ns ? sb / q : 0, nr * r, rb / r, slots) + kSplitCostBytes;
+      if (c < best) {
+        best = c;
+        *rp = r;
+        *sp = q;
+      }
+    }
+}
+
+// Partial-sum floats of a split launch: one round of slots * kCus blocks, each
+// 4 waves x `tiles` 16-row tiles x tm token rows x 16 weight rows.
+static size_t split_floats(int slots, int tiles, int tm) {
+  return (size_t)slots * kCus * 4 * tiles * tm * 16;
+}
+
+// The decode launches of a layer at T tokens: tile shapes, worst-case item
+// counts and K parts of the two phases.
+struct DecodePlan {
+  bool prefill, wide, stream, wide2;
+  int routed1, shared1, routed2, shared2;   // items
+  int rparts1, sparts1, rparts2, sparts2;   // blocks per item
+  int tm;                                   // token rows per tile in the partial sums
+};
+
+static DecodePlan decode_plan(const moe_layer &L, int32_t T) {
+  DecodePlan d{};
+  const int64_t E = L.num_experts, H = L.hidden, F = L.ffn, Fs = L.shared_ffn, k = L.top_k;
+  const int64_t N = (int64_t)T * k;
+  d.prefill = ffn_prefill_mode(L, T);
+  // worst case number of 16-row segment tiles: every non-empty segment adds at
+  // most one partial tile
+  const int64_t max_tiles = (E < N ? E : N) + (N + kTileM - 1) / kTileM;
+  const int64_t mtiles_shared = (T + kTileM - 1) / kTileM;
+  d.wide = N >= kWideMinAvgRows * E;
+  // Code loads are streamed past the caches unless a segment can span several
+  // 16-row tiles (T > 16) that all read the expert's weights and the segments
+  // are long on average (the wide shapes): measured on the 288-expert layer,
+  // streaming is 9% / 4% / 1.4% faster at 8 / 32 / 64 tokens, caching 2.4%
+  // faster at 150 tokens; a layer with T <= 16 never reads a weight twice.
+  d.stream = T <= kTileM || !d.wide;
+  // Down tiles of 256 rows (NT 4) also when its K, the ffn width, is short:
+  // at 640 columns (5 groups) per row the 128-row shape's blocks are mostly
+  // start-up (measured on the 512-expert layer: 37.0-37.6 against 37.9 us
+  // per FFN call; at 1536 columns the 128-row shape stays 1.5% faster).
+  d.wide2 = (d.wide || F <= 1024) && H % 256 == 0;
+  const int nt1 = d.wide ? 2 : 1, nt2 = d.wide2 ? 4 : 2;
+  d.routed1 = d.prefill ? 0 : (int)(max_tiles * (F / (64 * nt1)));   // F % 128 == 0
+  d.shared1 = Fs ? (int)(mtiles_shared * (Fs / 16)) : 0;
+  d.routed2 = d.prefill ? 0 : (int)(max_tiles * (H / (64 * nt2)));   // H % 128 == 0
+  d.shared2 = Fs ? (int)(mtiles_shared * (H / 16)) : 0;
+  d.rparts1 = d.sparts1 = d.rparts2 = d.sparts2 = 1;
+  d.tm = T < kTileM ? (T > 0 ? T : 1) : kTileM;
+  if (d.prefill || T > kSplitMaxT) return d;
+  // Routed items that can be live: with T <= 16 every segment is one tile, so
+  // at most min(E, N) tiles (the grid's last items exit on locating
+  // themselves), and split blocks index their partial sums among those.
+  const int64_t live = E < N ? E : N;
+  const int64_t sh_elem = L.shared_bits == 8 ? 1 : 2;
+  auto plan_phase = [&](int64_t K, int64_t Ks, int nt, int kmats, int routed, int shared,
+                        int slots, int *rp, int *sp) {
+    const int64_t rb = 64 * nt * kmats * (K / 2 + K / L.group_size * 2);   // codes + scales
+    const int64_t sb = 16 * kmats * Ks * sh_elem;
+    const int64_t nr = live * (routed / max_tiles);
+    // at least two quantization groups per routed block and per shared wave
+    split_parts(nr, rb, (int)(K / kGroup / 2), shared, sb, (int)(Ks / kGroup / 8), slots, rp, sp);
+    if ((int64_t)routed + shared > kFfnMaxTickets ||
+        (size_t)(nr * *rp + (int64_t)shared * *sp) * 4 * nt * kmats * d.tm * 16 >
+            split_floats(slots, nt * kmats, d.tm))
+      *rp = *sp = 1;
+  };
+  plan_phase(H, H, nt1, 2, d.routed1, d.shared1, 3, &d.rparts1, &d.sparts1);
+  plan_phase(F, Fs, nt2, 1, d.routed2, d.shared2, nt2 == 4 ? 4 : 3, &d.rparts2, &d.sparts2);
+  return d;
+}
+
+size_t ffn_split_floats(const moe_layer &L, int32_t T) {
+  // The largest need of any batch up to T tokens, so that a workspace sized
+  // for T tokens serves every smaller batch.  It depends on neither the group
+  // size nor the shared expert's format, so one workspace serves every layer
+  // of a stack whose layers agree in experts, widths and top-k.
+  size_t m = 0;
+  for (int32_t t = 1; t <= T && t <= kSplitMaxT; ++t) {
+    if (ffn_prefill_mode(L, t)) continue;
+    const int64_t N = (int64_t)t * L.top_k;
+    const bool wide = N >= kWideMinAvgRows * L.num_experts;     // as decode_plan
+    const bool wide2 = (wide || L.ffn <= 1024) && L.hidden % 256 == 0;
+    const int nt1 = wide ? 2 : 1, nt2 = wide2 ? 4 : 2;
+    const size_t f1 = split_floats(3, 2 * nt1, t);
+    const size_t f2 = split_floats(nt2 == 4 ? 4 : 3, nt2, t);
+    m = f1 > m ? f1 : m;
+    m = f2 > m ? f2 : m;
+  }
+  return m;
+}
+
 hipError_t launch_ffn(const moe_layer &L, const uint16_t *x, const uint16_t *x_perm,
                       const int32_t *perm_src, const int32_t *offsets, int32_t T,
                       uint16_t *y_perm, uint16_t *y_shared, uint16_t *h, uint16_t *h_shared,
-                      hipStream_t st) {
+                      float *split, unsigned int *tickets, hipStream_t st) {
   const int E = L.num_experts, H = L.hidden, F = L.ffn, Fs = L.shared_ffn, k = L.top_k;
   const int N = T * k;
-  const bool prefill = ffn_prefill_mode(L, T);
-  // worst case number of 16-row segment tiles: every non-empty segment adds at
-  // most one partial tile
-  const int max_tiles = (E < N ? E : N) + (N + kTileM - 1) / kTileM;
-  const int mtiles_shared = (T + kTileM - 1) / kTileM;
+  const DecodePlan d = decode_plan(L, T);
 
   FfnArgs a{};
   a.E = E; a.H = H; a.F = F; a.Fs = Fs; a.T = T; a.N = N; a.k = k;
   a.offsets = offsets;
+  a.tm = d.tm;
+  a.part = split;
+  a.ticket = tickets;
 
   // phase 1: token rows from x_perm, or from x through perm_src
   hipError_t err;
-  if (prefill) {
+  if (d.prefill) {
     err = launch_ffn_prefill_phase(L, 1, x_perm ? x_perm : x, x_perm ? nullptr : perm_src,
                                    offsets, T, h, st);
     if (err != hipSuccess) return err;
@@ -334,27 +584,23 @@ hipError_t launch_ffn(const moe_layer &L, const uint16_t *x, const uint16_t *x_p
   a.ws1 = reinterpret_cast<const f16 *>(L.shared_up_s);
   a.out_routed = reinterpret_cast<f16 *>(h);
   a.out_shared = reinterpret_cast<f16 *>(h_shared);
-  const bool wide = N >= kWideMinAvgRows * E;
-  // Code loads are streamed past the caches unless a segment can span several
-  // 16-row tiles (T > 16) that all read the expert's weights and the segments
-  // are long on average (the wide shapes): measured on the 288-expert layer,
-  // streaming is 9% / 4% / 1.4% faster at 8 / 32 / 64 tokens, caching 2.4%
-  // faster at 150 tokens; a layer with T <= 16 never reads a weight twice.
-  const bool stream = T <= kTileM || !wide;
-  a.routed_items = prefill ? 0 : max_tiles * (F / (wide ? 128 : 64));   // F % 128 == 0
-  a.shared_items = Fs ? mtiles_shared * (Fs / 16) : 0;
-  if (a.routed_items + a.shared_items > 0) {
-    if (wide && stream)
-      launch_decode<1, 2, 1, true>(L.group_size, a.routed_items + a.shared_items, a, st);
-    else if (wide)
-      launch_decode<1, 2, 1, false>(L.group_size, a.routed_items + a.shared_items, a, st);
+  a.routed_items = d.routed1;
+  a.shared_items = d.shared1;
+  a.rparts = d.rparts1;
+  a.sparts = d.sparts1;
+  int blocks = a.routed_items * a.rparts + a.shared_items * a.sparts;
+  if (blocks > 0) {
+    if (d.wide && d.stream)
+      launch_decode<1, 2, 1, true>(L.group_size, blocks, a, st);
+    else if (d.wide)
+      launch_decode<1, 2, 1, false>(L.group_size, blocks, a, st);
     else
-      launch_decode<1, 1, 2, true>(L.group_size, a.routed_items + a.shared_items, a, st);
+      launch_decode<1, 1, 2, true>(L.group_size, blocks, a, st);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
 
   // phase 2
-  if (prefill) {
+  if (d.prefill) {
     err = launch_ffn_prefill_phase(L, 2, h, nullptr, offsets, T, y_perm, st);
     if (err != hipSuccess) return err;
   }
@@ -368,22 +614,20 @@ hipError_t launch_ffn(const moe_layer &L, const uint16_t *x, const uint16_t *x_p
   a.ws0 = reinterpret_cast<const f16 *>(L.shared_down_s); a.ws1 = nullptr;
   a.out_routed = reinterpret_cast<f16 *>(y_perm);
   a.out_shared = reinterpret_cast<f16 *>(y_shared);
-  // Down tiles of 256 rows (NT 4) also when its K, the ffn width, is short:
-  // at 640 columns (5 groups) per row the 128-row shape's blocks are mostly
-  // start-up (measured on the 512-expert layer: 37.0-37.6 against 37.9 us
-  // per FFN call; at 1536 columns the 128-row shape stays 1.5% faster).
-  const bool wide2 = (wide || F <= 1024) && H % 256 == 0;
-  a.routed_items = prefill ? 0 : max_tiles * (H / (wide2 ? 256 : 128));   // H % 128 == 0
-  a.shared_items = Fs ? mtiles_shared * (H / 16) : 0;
-  if (a.routed_items + a.shared_items > 0) {
-    if (wide2 && stream)
-      launch_decode<2, 4, 1, true>(L.group_size, a.routed_items + a.shared_items, a, st);
-    else if (wide2)
-      launch_decode<2, 4, 1, false>(L.group_size, a.routed_items + a.shared_items, a, st);
-    else if (stream)
-      launch_decode<2, 2, 2, true>(L.group_size, a.routed_items + a.shared_items, a, st);
+  a.routed_items = d.routed2;
+  a.shared_items = d.shared2;
+  a.rparts = d.rparts2;
+  a.sparts = d.sparts2;
+  blocks = a.routed_items * a.rparts + a.shared_items * a.sparts;
+  if (blocks > 0) {
+    if (d.wide2 && d.stream)
+      launch_decode<2, 4, 1, true>(L.group_size, blocks, a, st);
+    else if (d.wide2)
+      launch_decode<2, 4, 1, false>(L.group_size, blocks, a, st);
+    else if (d.stream)
+      launch_decode<2, 2, 2, true>(L.group_size, blocks, a, st);
     else
-      launch_decode<2, 2, 2, false>(L.group_size, a.routed_items + a.shared_items, a, st);
+      launch_decode<2, 2, 2, false>(L.group_size, blocks, a, st);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   return hipSuccess;

@@ -19,13 +19,16 @@ constexpr int kFusedMaxLogits = 8192;   // T * E held in LDS by the fused router
 
 // The counter block at the start of every workspace (moe_workspace_init
 // zero-fills it; every call leaves it at zero).
-constexpr size_t kWsSyncBytes = 256;
+constexpr size_t kWsSyncBytes = 16384;   // a multiple of 4 KB (zero-filled by 256-thread blocks)
 // Words of that block: word 0 is the one-launch router's counter; the launch
 // that fuses a layer's combine with the next layer's router uses word 1 (all
-// tokens) and words 32 .. 32+T-1 (one per token), hence at most 32 tokens.
+// tokens) and words 32 .. 32+T-1 (one per token), hence at most 32 tokens;
+// the decode FFN's K-split items take one word each from word 64 on.
 constexpr int kStackAllCounter = 1;
 constexpr int kStackTokCounter = 32;
 constexpr int kStackMaxT = 32;
+constexpr int kFfnTicket = 64;
+constexpr int kFfnMaxTickets = (int)(kWsSyncBytes / 4) - kFfnTicket;
 
 // Byte offsets of the per-call scratch regions inside the caller's workspace.
 struct WsLayout {
@@ -36,9 +39,12 @@ struct WsLayout {
   size_t bases;     // int32 [nchunks, E]
   size_t h;         // fp16 [T*k, F]
   size_t h_shared;  // fp16 [T, Fs]
+  size_t split;     // fp32 partial sums of the decode FFN's K-split blocks
   size_t total;
 };
 WsLayout ws_layout(const moe_layer &L, int32_t T);
+// Floats of partial sums the decode FFN needs for T tokens (0: no K split).
+size_t ffn_split_floats(const moe_layer &L, int32_t T);
 
 hipError_t launch_quantize(const uint16_t *w, int64_t rows, int64_t cols, int gs, uint8_t *q,
                            uint16_t *s, hipStream_t st);
@@ -59,10 +65,12 @@ hipError_t launch_permute(const moe_layer &L, const uint16_t *x, const int32_t *
                           uint16_t *x_perm, int32_t *counts, int32_t *bases, hipStream_t st);
 hipError_t launch_gather(const moe_layer &L, const uint16_t *x, const int32_t *perm_src, int32_t T,
                          uint16_t *x_perm, hipStream_t st);
+// split: the workspace's partial-sum region (ffn_split_floats floats);
+// tickets: its counter words from kFfnTicket on.
 hipError_t launch_ffn(const moe_layer &L, const uint16_t *x, const uint16_t *x_perm,
                       const int32_t *perm_src, const int32_t *offsets, int32_t T,
                       uint16_t *y_perm, uint16_t *y_shared, uint16_t *h, uint16_t *h_shared,
-                      hipStream_t st);
+                      float *split, unsigned int *tickets, hipStream_t st);
 hipError_t launch_ffn_prefill_phase(const moe_layer &L, int phase, const uint16_t *a,
                                     const int32_t *perm_src, const int32_t *offsets, int32_t T,
                                     uint16_t *out, hipStream_t st);

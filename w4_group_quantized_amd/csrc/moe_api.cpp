@@ -35,6 +35,7 @@ WsLayout ws_layout(const moe_layer &L, int32_t T) {
   w.bases = off;    off += align_up(nch * E * sizeof(int32_t));
   w.h = off;        off += align_up(N * (size_t)L.ffn * 2);
   w.h_shared = off; off += align_up(Tz * (size_t)L.shared_ffn * 2);
+  w.split = off;    off += align_up(ffn_split_floats(L, (int32_t)Tz) * sizeof(float));
   w.total = off;
   return w;
 }
@@ -140,6 +141,11 @@ __global__ __launch_bounds__(256) void zero_words_kernel(u32x4 *p, size_t n) {
   if (i < n) p[i] = (u32x4){0u, 0u, 0u, 0u};
 }
 
+// The decode FFN's per-item tickets in the workspace's counter block.
+static inline unsigned int *ffn_tickets(char *base, const WsLayout &w) {
+  return reinterpret_cast<unsigned int *>(base + w.sync) + kFfnTicket;
+}
+
 static inline bool fused_route(const moe_layer &L, int32_t T) {
   return T <= kFusedMaxT && (int64_t)T * L.num_experts <= kFusedMaxLogits;
 }
@@ -179,7 +185,8 @@ static moe_status run_layer(const moe_layer &L, const uint16_t *x, int32_t T, in
   if (e == hipSuccess)
     e = launch_ffn(L, x, x_perm, perm_src, offsets, T, y_perm, ys,
                    reinterpret_cast<uint16_t *>(base + w.h),
-                   reinterpret_cast<uint16_t *>(base + w.h_shared), st);
+                   reinterpret_cast<uint16_t *>(base + w.h_shared),
+                   reinterpret_cast<float *>(base + w.split), ffn_tickets(base, w), st);
   if (e == hipSuccess)
     e = launch_combine(L, y_perm, ys, inv_pos, topk_w, T, flags, eps, out, st);
   return hip_status(e);
@@ -206,7 +213,8 @@ static moe_status run_stack(const moe_layer *const *layers, int32_t n, const uin
   for (int32_t i = 0; i < n && e == hipSuccess; ++i) {
     const moe_layer &L = *layers[i];
     uint16_t *out = acts + (size_t)i * HT;
-    e = launch_ffn(L, in, nullptr, perm_src, offsets, T, y_perm, ys, h, hs, st);
+    e = launch_ffn(L, in, nullptr, perm_src, offsets, T, y_perm, ys, h, hs,
+                   reinterpret_cast<float *>(base + w.split), ffn_tickets(base, w), st);
     if (e != hipSuccess) break;
     if (fused && i + 1 < n) {
       e = launch_combine_route(L, *layers[i + 1], y_perm, ys, inv_pos, topk_w, T, flags, eps,
@@ -266,7 +274,7 @@ static moe_status device_scratch(hipStream_t st, char **out) {
     e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
     if (e != hipSuccess) return hip_status(e);
     if (ptr == nullptr || (reinterpret_cast<uintptr_t>(ptr) & 255u)) return MOE_EHIP;
-    hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(kWsSyncBytes / 16), 0, st,
+    hipLaunchKernelGGL(zero_words_kernel, dim3(kWsSyncBytes / 16 / 256), dim3(256), 0, st,
                        static_cast<u32x4 *>(ptr), (size_t)(kWsSyncBytes / 16));
     if ((e = hipGetLastError()) != hipSuccess) return hip_status(e);
     g_scratch_ptr[dev] = static_cast<char *>(ptr);
@@ -290,8 +298,8 @@ moe_status moe_workspace_init(void *ws, size_t ws_bytes, void *stream) {
   if (ws_bytes < kWsSyncBytes) return MOE_EWORKSPACE;
   if (!ok_ptr(ws)) return MOE_EINVAL;
   clear_stale_hip_error();
-  hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(kWsSyncBytes / 16), 0, (hipStream_t)stream,
-                     static_cast<u32x4 *>(ws), (size_t)(kWsSyncBytes / 16));
+  hipLaunchKernelGGL(zero_words_kernel, dim3(kWsSyncBytes / 16 / 256), dim3(256), 0,
+                     (hipStream_t)stream, static_cast<u32x4 *>(ws), (size_t)(kWsSyncBytes / 16));
   return hip_status(hipGetLastError());
 }
 
@@ -363,6 +371,7 @@ moe_status moe_w4_grouped_ffn(const moe_layer *L, const uint16_t *x, const uint1
                                L->shared_ffn > 0 ? y_shared : nullptr,
                                reinterpret_cast<uint16_t *>(base + w.h),
                                reinterpret_cast<uint16_t *>(base + w.h_shared),
+                               reinterpret_cast<float *>(base + w.split), ffn_tickets(base, w),
                                (hipStream_t)stream));
 }
 

@@ -75,7 +75,7 @@ class W4MoELayer:
     def alloc(self, max_tokens: int) -> MoEBuffers:
         d, T, k, H, E = self.device, max_tokens, self.k, self.H, self.E
         i32, f16 = torch.int32, torch.float16
-        ws = torch.empty((max(self.workspace_size(T), 256),), dtype=torch.uint8, device=d)
+        ws = torch.empty((max(self.workspace_size(T), 16384),), dtype=torch.uint8, device=d)
         N.moe_workspace_init(ws, ws.numel())   # its counter block starts at zero
         return MoEBuffers(
             max_tokens=T,
