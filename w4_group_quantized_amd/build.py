@@ -19,8 +19,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_w4.so")
-SOURCES = ["quant.hip", "route.hip", "permute.hip", "ffn.hip", "ffn_prefill.hip", "combine.hip",
-           "stack.hip", "moe_api.cpp"]
+SOURCES = ["quant.hip", "route.hip", "permute.hip", "ffn.hip", "ffn_split.hip", "ffn_prefill.hip",
+           "combine.hip", "stack.hip", "moe_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

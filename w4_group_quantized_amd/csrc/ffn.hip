@@ -36,147 +36,9 @@
 // the same number of bytes: a CU reads ~20 GB/s whether it holds one block or
 // three.  The item's last block to finish adds the fp32 partial sums of its
 // parts in the fixed order 0, 1, ..., P-1.
-#include "common.h"
-#include "kernels.h"
-#include "tiles.h"
+#include "ffn_decode.h"
 
 namespace moe {
-
-constexpr int kTileM = 16;   // tokens per MFMA tile
-// Token rows of a routed tile are staged in LDS when they take at most this
-// many bytes (each of the 256 threads moves kStagePieces 16-byte pieces).
-constexpr int kStagePieces = 8;
-constexpr int kActLdsBytes = kStagePieces * 256 * 16;
-constexpr int kActLdsVec = (kActLdsBytes + kTileM * 16) / 16;   // + row padding
-
-struct FfnArgs {
-  int E, H, F, Fs, T, N, k;         // N = T * k
-  const int32_t *offsets;           // [E+1]
-  const int32_t *perm_src;          // phase 1 without x_perm: rows of x via perm_src[r] / k
-  const f16 *a_routed;              // phase 1: x_perm [N, H] or x [T, H]; phase 2: h [N, F]
-  const f16 *a_shared;              // phase 1: x [T, H];      phase 2: h_shared [T, Fs]
-  const uint8_t *q0, *q1;           // phase 1: gate_q, up_q;  phase 2: down_q, unused
-  const f16 *s0, *s1;               // matching scales
-  const f16 *w0, *w1;               // shared expert fp16 weights (phase 2: w0 only)
-  const uint8_t *wq0, *wq1;         // or its 8-bit codes (shared_w8) ...
-  const f16 *ws0, *ws1;             // ... and their g128 scales
-  int shared_w8;
-  f16 *out_routed;                  // phase 1: h [N, F];      phase 2: y_perm [N, H]
-  f16 *out_shared;                  // phase 1: h_shared;      phase 2: y_shared
-  int shared_items;                 // shared-expert items (their blocks first)
-  int routed_items;                 // worst-case number of routed items (their blocks after)
-  int rparts, sparts;               // blocks per routed / shared item (K parts; 1 = whole K)
-  int tm;                           // token rows per tile kept in the partial sums
-  float *part;                      // K-split partial sums: [block][wave][tile][tm][16]
-  unsigned int *ticket;             // per item (shared items first): parts done, zero between calls
-};
-
-constexpr int kMaxParts = 8;
-
-// K split over blocks: every block of an item stores the partial sums of the
-// tile rows of its live tokens, and the last block of the item to take a
-// ticket adds the parts in the fixed order 0 .. nparts-1 into acc.  The stores
-// are agent-scope atomic stores (written through to the device coherence
-// point); waiting for them before the barrier that precedes the ticket orders
-// them before it, and the last block reads them with coherent (sc1) loads, as
-// the one-launch router does with its logits.  Every wave of the block calls
-// this; has_acc: this wave holds partial sums (with the K range split over the
-// waves inside the block, only wave 0 after the in-block reduction).  Returns
-// false in every block but the last, which also resets the ticket.
-template <int NTL>
-__device__ bool split_sum(f32x4 (&acc)[NTL], bool has_acc, int rows, int tm, float *item_part,
-                          int blk_floats, int kpart, int nparts, unsigned int *ticket) {
-  __shared__ int s_last;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wid = threadIdx.x / kWave;
-  const int r = lane & 15, kb = lane >> 4;
-  const int wave_floats = NTL * tm * 16;
-  if (has_acc) {
-    float *dst = item_part + (size_t)kpart * blk_floats + wid * wave_floats;
-#pragma unroll
-    for (int i = 0; i < NTL; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int tok = 4 * kb + j;
-        if (tok < rows)
-          __hip_atomic_store(dst + (i * tm + tok) * 16 + r, acc[i][j], __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-      }
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0)
-    s_last = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             (unsigned)(nparts - 1);
-  __syncthreads();
-  if (!s_last) return false;
-  if (threadIdx.x == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (has_acc) {
-    const rsrc_t rs = make_rsrc(item_part, (uint32_t)(nparts * blk_floats) * 4u);
-#pragma unroll
-    for (int i = 0; i < NTL; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int tok = 4 * kb + j;
-        // parts past nparts and rows past the tile read zeros (out of range)
-        float v[kMaxParts];
-#pragma unroll
-        for (int q = 0; q < kMaxParts; ++q) {
-          const uint32_t off = tok < rows && q < nparts
-                                   ? (uint32_t)(q * blk_floats + wid * wave_floats +
-                                                (i * tm + tok) * 16 + r) * 4u
-                                   : ARows::kPadOffset;
-          v[q] = __builtin_bit_cast(float,
-                                    __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, kBufCoherent));
-        }
-        float sum = v[0];
-#pragma unroll
-        for (int q = 1; q < kMaxParts; ++q)
-          if (q < nparts) sum += v[q];
-        acc[i][j] = sum;
-      }
-  }
-  return true;
-}
-
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
-
-// Block-cooperative: which expert and which 16-row tile of its segment is
-// segment tile `slot`?  Tiles are numbered expert by expert.  Returns false
-// when slot is past the last tile.  Requires blockDim.x = 256, E <= 1024.
-__device__ bool locate_tile(const int32_t *__restrict__ off, int E, int slot, int *e_out,
-                            int *mt_out) {
-  __shared__ int s_scan[4];
-  __shared__ int s_res[2];
-  const int tid = threadIdx.x;
-  // five independent loads with clamped (in-bounds) indices, then the counts
-  int o[5];
-#pragma unroll
-  for (int i = 0; i < 5; ++i) o[i] = off[min(4 * tid + i, E)];
-  int c[4], sum = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = 4 * tid + i;
-    c[i] = e < E ? (o[i + 1] - o[i] + kTileM - 1) / kTileM : 0;
-    sum += c[i];
-  }
-  int total;
-  int run = block_excl_scan(sum, s_scan, &total);
-  if (tid == 0) s_res[0] = -1;
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (slot >= run && slot < run + c[i]) {
-      s_res[0] = 4 * tid + i;
-      s_res[1] = slot - run;
-    }
-    run += c[i];
-  }
-  __syncthreads();
-  *e_out = s_res[0];
-  *mt_out = s_res[1];
-  return s_res[0] >= 0;
-}
 
 // PHASE 1: PAIR = gate and up tiles per wave, SwiGLU epilogue.
 // PHASE 2: one matrix, plain epilogue.  GM: quantization group size (GroupMode).
@@ -194,12 +56,8 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
   __shared__ float red[3 * 2 * 4 * kWave];
   __shared__ u32x4 s_act[kActLdsVec];
 
-  const int sblocks = p.shared_items * p.sparts;
-  // partial-sum floats per block (routed and shared blocks alike)
-  const int blk_floats = 4 * kMats * NT * p.tm * 16;
-  if ((int)blockIdx.x >= sblocks) {
-    const int rb = blockIdx.x - sblocks;
-    const int item = rb / p.rparts, kpart = rb - item * p.rparts;
+  if ((int)blockIdx.x >= p.shared_items) {
+    const int item = blockIdx.x - p.shared_items;
     const int ntiles = Nrows / (64 * NT);
     const int slot = item / ntiles, nt = item % ntiles;
     int e, mt;
@@ -228,7 +86,6 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
     f32x4 acc[kMats * NT];
 #pragma unroll
     for (int t = 0; t < kMats * NT; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    const int g0 = kpart * G / p.rparts, g1 = (kpart + 1) * G / p.rparts;
     const int KB = K * 2;                 // bytes per activation row
     if (rows * KB <= kActLdsBytes) {      // block-uniform
       // Stage the tile's token rows in LDS once for the four waves: the
@@ -263,7 +120,7 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
 #pragma unroll
       for (int j = 0; j < kStagePieces; ++j) stg[j] = bload16(rs, voff[j], 0);
       const ALds<kActLdsVec> al(s_act, min(r, rows - 1), stride, kb);
-      w4_tiles<kMats * NT, S, GM, STREAM>(al, qrow, srow, g0, g1, acc, [&] {
+      w4_tiles<kMats * NT, S, GM, STREAM>(al, qrow, srow, 0, G, acc, [&] {
 #pragma unroll
         for (int j = 0; j < kStagePieces; ++j) {
           const int i = j * 256 + tid;
@@ -285,13 +142,8 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
       const ARows arow = p.perm_src
                              ? ARows(p.a_routed, p.T, K, tok, live, kb)
                              : ARows(p.a_routed + (size_t)seg0 * K, rows, K, tok, live, kb);
-      w4_tiles<kMats * NT, S, GM, STREAM>(arow, qrow, srow, g0, g1, acc);
+      w4_tiles<kMats * NT, S, GM, STREAM>(arow, qrow, srow, 0, G, acc);
     }
-    if (p.rparts > 1 &&
-        !split_sum<kMats * NT>(acc, true, rows, p.tm,
-                               p.part + (size_t)(sblocks + item * p.rparts) * blk_floats,
-                               blk_floats, kpart, p.rparts, p.ticket + p.shared_items + item))
-      return;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -309,7 +161,7 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
   const int Ks = kPair ? p.H : p.Fs;
   const int Ns = kPair ? p.Fs : p.H;
   const int Gs = Ks / kGroup;
-  const int sitem = blockIdx.x / p.sparts, spart = blockIdx.x - sitem * p.sparts;
+  const int sitem = blockIdx.x;
   const int sntiles = Ns / 16;
   const int mt = sitem / sntiles, nt = sitem % sntiles;
   const int tok0 = mt * kTileM;
@@ -320,9 +172,7 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
   f32x4 acc[kMats];
 #pragma unroll
   for (int t = 0; t < kMats; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  // this block's part of K, split again over its 4 waves
-  const int lo = spart * Gs / p.sparts, hi = (spart + 1) * Gs / p.sparts;
-  const int g0 = lo + wid * (hi - lo) / 4, g1 = lo + (wid + 1) * (hi - lo) / 4;
+  const int g0 = wid * Gs / 4, g1 = (wid + 1) * Gs / 4;
   if (p.shared_w8) {     // block-uniform: 8-bit codes, 16-row tile nt
     const size_t tile = (size_t)nt * 16;
     const uint8_t *qrow[kMats];
@@ -341,11 +191,6 @@ __global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs p) {
     f16_tiles<kMats>(arow, wrow, kb, g0, g1, acc);
   }
   ksplit_reduce<kMats>(acc, red);
-  if (p.sparts > 1 &&
-      !split_sum<kMats>(acc, wid == 0, rows, p.tm,
-                        p.part + (size_t)sitem * p.sparts * blk_floats, blk_floats, spart,
-                        p.sparts, p.ticket + sitem))
-    return;
   if (wid != 0) return;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -505,7 +350,8 @@ static DecodePlan decode_plan(const moe_layer &L, int32_t T) {
   d.shared2 = Fs ? (int)(mtiles_shared * (H / 16)) : 0;
   d.rparts1 = d.sparts1 = d.rparts2 = d.sparts2 = 1;
   d.tm = T < kTileM ? (T > 0 ? T : 1) : kTileM;
-  if (d.prefill || T > kSplitMaxT) return d;
+  // (a split launch is a streamed one: only those have a split instance)
+  if (d.prefill || T > kSplitMaxT || !d.stream) return d;
   // Routed items that can be live: with T <= 16 every segment is one tile, so
   // at most min(E, N) tiles (the grid's last items exit on locating
   // themselves), and split blocks index their partial sums among those.
@@ -564,7 +410,7 @@ hipError_t launch_ffn(const moe_layer &L, const uint16_t *x, const uint16_t *x_p
   a.ticket = tickets;
 
   // phase 1: token rows from x_perm, or from x through perm_src
-  hipError_t err;
+  hipError_t err = hipSuccess;
   if (d.prefill) {
     err = launch_ffn_prefill_phase(L, 1, x_perm ? x_perm : x, x_perm ? nullptr : perm_src,
                                    offsets, T, h, st);
@@ -590,13 +436,15 @@ hipError_t launch_ffn(const moe_layer &L, const uint16_t *x, const uint16_t *x_p
   a.sparts = d.sparts1;
   int blocks = a.routed_items * a.rparts + a.shared_items * a.sparts;
   if (blocks > 0) {
-    if (d.wide && d.stream)
+    if (a.rparts > 1 || a.sparts > 1)   // split launches are streamed ones
+      err = launch_ffn_split(1, d.wide ? 2 : 1, L.group_size, blocks, a, st);
+    else if (d.wide && d.stream)
       launch_decode<1, 2, 1, true>(L.group_size, blocks, a, st);
     else if (d.wide)
       launch_decode<1, 2, 1, false>(L.group_size, blocks, a, st);
     else
       launch_decode<1, 1, 2, true>(L.group_size, blocks, a, st);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (err != hipSuccess || (err = hipGetLastError()) != hipSuccess) return err;
   }
 
   // phase 2
@@ -620,7 +468,9 @@ hipError_t launch_ffn(const moe_layer &L, const uint16_t *x, const uint16_t *x_p
   a.sparts = d.sparts2;
   blocks = a.routed_items * a.rparts + a.shared_items * a.sparts;
   if (blocks > 0) {
-    if (d.wide2 && d.stream)
+    if (a.rparts > 1 || a.sparts > 1)
+      err = launch_ffn_split(2, d.wide2 ? 4 : 2, L.group_size, blocks, a, st);
+    else if (d.wide2 && d.stream)
       launch_decode<2, 4, 1, true>(L.group_size, blocks, a, st);
     else if (d.wide2)
       launch_decode<2, 4, 1, false>(L.group_size, blocks, a, st);
@@ -628,7 +478,7 @@ hipError_t launch_ffn(const moe_layer &L, const uint16_t *x, const uint16_t *x_p
       launch_decode<2, 2, 2, true>(L.group_size, blocks, a, st);
     else
       launch_decode<2, 2, 2, false>(L.group_size, blocks, a, st);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (err != hipSuccess || (err = hipGetLastError()) != hipSuccess) return err;
   }
   return hipSuccess;
 }
