@@ -162,6 +162,12 @@ __device__ __forceinline__ uint64_t route_key(float v, int e) {
 __device__ __forceinline__ int route_key_expert(uint64_t key) {
   return 0xFFFF - (int)(key & 0xFFFFu);
 }
+// The logit of a key: the inverse of the high word's order map (exact, but
+// for -0, which comes back as +0, and NaN, which comes back as a NaN).
+__device__ __forceinline__ float route_key_value(uint64_t key) {
+  const uint32_t m = (uint32_t)(key >> 32);
+  return __uint_as_float((m & 0x80000000u) ? (m & 0x7fffffffu) : ~m);
+}
 // Cross-lane reductions on DPP row operations (no LDS round trips): within
 // each row of 16 lanes, exchange with lane^1, lane^2, the mirrored lane of the
 // half row and of the row; afterwards every lane of a row holds the row's

@@ -221,8 +221,13 @@ __global__ __launch_bounds__(kStackWaves *kWave) void combine_route_kernel(Combi
           __hip_atomic_store(&p.idx[(size_t)t * k + j], e, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
           p.w[(size_t)t * k + j] = pr;
+          s_idx[j] = e;
         });
+    // one token: this is the last block of all, and the permutation is the
+    // order of its k choices (no second ticket, no reload of the choices)
+    if (T == 1) one_token_permutation(s_idx, k, E, p.offsets, p.perm_src, p.inv_pos);
   }
+  if (T == 1) return;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0)

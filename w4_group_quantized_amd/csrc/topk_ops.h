@@ -18,7 +18,8 @@ namespace moe {
 // masked) so that all NPER reads are in flight together.  Each lane sorts
 // its NPER (logit, expert) keys once; every round is one wave-wide maximum
 // over the lanes' current heads, and the winning lane shifts its list.
-// Lane j < k hands the j-th choice to store(j, expert, probability).
+// Lane j < k hands the j-th choice to store(j, expert, probability); its
+// logit comes back out of the winning key (no second read of the logits).
 template <int NPER, class GetE, class Store>
 __device__ __forceinline__ void wave_softmax_topk(GetE get_expert, int E, int k, Store store) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -52,7 +53,7 @@ __device__ __forceinline__ void wave_softmax_topk(GetE get_expert, int E, int k,
   // winner is the largest head key: its value-order word alone decides
   // unless several heads share it (equal logits, NaN or empty heads), and
   // then the full 64-bit comparison does.
-  int mine = 0;
+  uint64_t mine = 0;
   for (int j = 0; j < k; ++j) {
     const uint32_t hi = (uint32_t)(key[0] >> 32);
     const uint32_t mhi = wave_max_u32(hi);
@@ -64,16 +65,36 @@ __device__ __forceinline__ void wave_softmax_topk(GetE get_expert, int E, int k,
     } else {
       best = wave_max_u64(key[0]);
     }
-    if (lane == j) mine = route_key_expert(best);
+    if (lane == j) mine = best;
     if (key[0] == best) {   // the owner lane: its head won, shift its list
 #pragma unroll
       for (int i = 0; i + 1 < NPER; ++i) key[i] = key[i + 1];
       key[NPER - 1] = 0ull;
     }
   }
-  if (lane < k) {          // the k weights in parallel
-    const float ve = get_expert(mine);
-    store(lane, mine, expf(ve - m) / s);
+  if (lane < k)            // the k weights in parallel
+    store(lane, route_key_expert(mine), expf(route_key_value(mine) - m) / s);
+}
+
+// The permutation of one token's k choices (distinct experts, in s_idx[0..k),
+// k <= 64): their order by expert.  One wave; the same offsets, perm_src and
+// inv_pos as build_permutation gives for these k entries.
+__device__ __forceinline__ void one_token_permutation(const int *s_idx, int k, int E,
+                                                      int32_t *__restrict__ offsets,
+                                                      int32_t *__restrict__ perm_src,
+                                                      int32_t *__restrict__ inv_pos) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int mine = lane < k ? s_idx[lane] : E;
+  int rank = 0;
+  for (int i = 0; i < k; ++i) rank += __builtin_amdgcn_readlane(mine, i) < mine ? 1 : 0;
+  if (lane < k) {
+    perm_src[rank] = lane;
+    inv_pos[lane] = rank;
+  }
+  for (int e = lane; e <= E; e += kWave) {   // offsets[e] = choices below expert e
+    int c = 0;
+    for (int i = 0; i < k; ++i) c += __builtin_amdgcn_readlane(mine, i) < e ? 1 : 0;
+    offsets[e] = c;
   }
 }
 
