@@ -173,13 +173,14 @@ def test_decode_stack_graph_replay_bitwise():
                   lambda: step(other_acts, other_buf), replays=3)
 
 
-def test_decode_stack_call_graph_replay_bitwise():
+@pytest.mark.parametrize("T", [16, 1])
+def test_decode_stack_call_graph_replay_bitwise(T):
     """moe_decode_stack_forward over the 42 layers (the fused combine + next
     router launches) captured into one graph: every layer's output and the
-    last layer's routing after each replay equal eager execution."""
+    last layer's routing after each replay equal eager execution (at one
+    token: the K-split gate/up launch and the one-token permutation)."""
     from w4_group_quantized_amd import W4MoEStack
-    cfg = get_config("decode_stack")
-    T = cfg.tokens
+    cfg = get_config("decode_stack", tokens=T)
     stack = W4MoEStack([device_layer(cfg, li) for li in range(cfg.layers)])
     x = to_dev(G.activations(cfg, batch=72))
     buf = stack.alloc(T)
