@@ -379,15 +379,22 @@ size_t ffn_split_floats(const moe_layer &L, int32_t T) {
   // for T tokens serves every smaller batch.  It depends on neither the group
   // size nor the shared expert's format, so one workspace serves every layer
   // of a stack whose layers agree in experts, widths and top-k.
+  // A phase whose items stay under two kSplitMinBytes blocks even at the
+  // largest (64-wide groups, fp16 shared expert) never splits.
+  const int64_t H = L.hidden, F = L.ffn, Fs = L.shared_ffn;
+  auto can_split = [](int64_t K, int64_t Ks, int nt, int kmats) {
+    const int64_t rb = 64 * nt * kmats * (K / 2 + K / 32), sb = 16 * kmats * Ks * 2;
+    return rb >= 2 * kSplitMinBytes || sb >= 2 * kSplitMinBytes;
+  };
   size_t m = 0;
   for (int32_t t = 1; t <= T && t <= kSplitMaxT; ++t) {
     if (ffn_prefill_mode(L, t)) continue;
     const int64_t N = (int64_t)t * L.top_k;
     const bool wide = N >= kWideMinAvgRows * L.num_experts;     // as decode_plan
-    const bool wide2 = (wide || L.ffn <= 1024) && L.hidden % 256 == 0;
+    const bool wide2 = (wide || F <= 1024) && H % 256 == 0;
     const int nt1 = wide ? 2 : 1, nt2 = wide2 ? 4 : 2;
-    const size_t f1 = split_floats(3, 2 * nt1, t);
-    const size_t f2 = split_floats(nt2 == 4 ? 4 : 3, nt2, t);
+    const size_t f1 = can_split(H, H, nt1, 2) ? split_floats(3, 2 * nt1, t) : 0;
+    const size_t f2 = can_split(F, Fs, nt2, 1) ? split_floats(nt2 == 4 ? 4 : 3, nt2, t) : 0;
     m = f1 > m ? f1 : m;
     m = f2 > m ? f2 : m;
   }
