@@ -79,11 +79,9 @@ __device__ bool split_sum(f32x4 (&acc)[NTL], bool has_acc, int rows, int tm, flo
   return true;
 }
 
-// The same work items with their K range split over p.rparts (routed) and
-// p.sparts (shared) blocks, code loads streamed.  A kernel of its own, so that
-// the whole-item kernel above keeps its code: folding a split into it, even
-// one switched off at compile time, changed its schedule and cost 2% of the
-// fine-grained layers' FFN time.
+// The whole-item kernel's work items (ffn.hip) with their K range split over
+// p.rparts (routed) and p.sparts (shared) blocks, code loads streamed; item
+// b's blocks are consecutive, shared items first.
 template <int PHASE, int NT, int S, int GM>
 __global__ __launch_bounds__(256) void ffn_split_kernel(FfnArgs p) {
   constexpr bool STREAM = true;
