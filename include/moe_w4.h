@@ -325,9 +325,9 @@ moe_status moe_decode_stack_forward(const moe_layer *const *layers, int32_t n_la
  * 16 MiB on every GPU the library is loaded on (held until the process
  * ends): a call whose moe_workspace_size(layer, T) exceeds 16 MiB returns
  * MOE_EWORKSPACE and launches nothing (decode batches fit: the 288-expert
- * hidden-4096 ffn-1536 top-8 layer with its shared expert up to 581 tokens,
- * the 16-expert hidden-12288 ffn-65536 top-4 layer up to 31; the 8192-token
- * prefill layer needs 260 MiB and does not).  The call allocates and frees nothing.  The first call on
+ * hidden-4096 ffn-1536 top-8 layer with its shared expert up to 525 tokens,
+ * the 16-expert hidden-12288 ffn-65536 top-4 layer up to 28; the 8192-token
+ * prefill layer needs 262 MiB and does not).  The call allocates and frees nothing.  The first call on
  * a GPU looks up that GPU's copy of the array and zero-fills its counter
  * block on `stream`; `stream` must belong to the calling thread's current
  * device.  Every call on one GPU uses that GPU's one array: calls that

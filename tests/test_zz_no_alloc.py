@@ -93,7 +93,7 @@ def test_noalloc_matches_layer_forward_full_decode_shape():
 
 def test_noalloc_refuses_what_does_not_fit():
     """Checked on the host before any launch: the 8192-token prefill layer
-    needs a 260 MiB workspace; null pointers are refused first."""
+    needs a 262 MiB workspace; null pointers are refused first."""
     FAKE = 1 << 20
     cfg = get_config("prefill")
     L = N.make_layer(num_experts=cfg.num_experts, hidden=cfg.hidden, ffn=cfg.ffn,
