@@ -119,18 +119,22 @@ def test_full_size_layer(name, n_sample):
     print(f"[{name}] tokens checked {len(toks)}/{T}  max err {err:.3e} (bound {bound:.3e})")
 
 
-@pytest.mark.parametrize("name,T,w8", [("decode_fine", 1, False), ("decode_fine", 1, True),
-                                       ("decode_fine", 2, False), ("decode_fine", 3, False),
-                                       ("decode_fine512", 1, False), ("decode_fine512", 2, False),
-                                       ("decode_fine512", 4, False), ("decode_coarse", 1, False)])
-def test_full_size_small_batches(name, T, w8):
+@pytest.mark.parametrize("name,T,w8,gs", [
+    ("decode_fine", 1, False, 128), ("decode_fine", 1, False, 64), ("decode_fine", 1, False, 256),
+    ("decode_fine", 1, True, 128), ("decode_fine", 2, False, 128), ("decode_fine", 3, False, 128),
+    ("decode_fine512", 1, False, 128), ("decode_fine512", 2, False, 128),
+    ("decode_fine512", 4, False, 128), ("decode_coarse", 1, False, 128),
+    ("decode_coarse", 1, False, 256)])
+def test_full_size_small_batches(name, T, w8, gs):
     """Batches of a few tokens.  Where whole items would leave some CUs
     streaming two of them while others idle, the decode FFN splits each
     item's in_features over several blocks and adds their fp32 partial sums
-    in a fixed order: the gate/up launch at one token on the 288-expert layer,
-    the down launch at one token on the coarse layer; the other cases run
-    whole.  Every token against the oracle, after the permutation check."""
-    cfg = get_config(name, tokens=T)
+    in a fixed order: the gate/up launch at one token on the 288-expert layer
+    (quantization groups of 128, 64 and 256 columns), the down launch at one
+    token on the coarse layer (groups of 128 and 256); the other cases run
+    whole (the 8-bit shared expert is never split).  Every token against the
+    oracle, after the permutation check."""
+    cfg = get_config(name, tokens=T, group_size=gs)
     layer, mats, wr, b, shared = device_layer(cfg, w8=w8)
     x = G.activations(cfg, batch=20 + T)
     buf = layer.alloc(T)

@@ -252,10 +252,10 @@ bool ffn_prefill_mode(const moe_layer &L, int32_t T) {
 // token (interleaved A/B): the 42-layer step 2.21 -> 1.92 ms (gate/up 3
 // routed x 2 shared parts, its launch 26.4 -> 21-22 us), the coarse layer
 // 0.885 -> 0.847 ms (down in 2 parts).  Left whole by the rule, and slower
-// when split: the balanced down launch of the 288-expert layer, the
-// 512-expert layer's launches (fewer items than CUs) and the gate/up launch
-// with the 8-bit shared expert (2-5% slower in 2 routed parts), which sets
-// kSplitCostBytes.
+// when split: the balanced down launch of the 288-expert layer and the
+// 512-expert layer's launches (fewer items than CUs); the gate/up launch
+// with the 8-bit shared expert (2-5% slower in 2 routed parts, which set
+// kSplitCostBytes) is never split.
 constexpr int kCus = 256;
 constexpr int kSplitMaxT = 4;
 constexpr int64_t kSplitMinBytes = 48 << 10;
@@ -350,8 +350,11 @@ static DecodePlan decode_plan(const moe_layer &L, int32_t T) {
   d.shared2 = Fs ? (int)(mtiles_shared * (H / 16)) : 0;
   d.rparts1 = d.sparts1 = d.rparts2 = d.sparts2 = 1;
   d.tm = T < kTileM ? (T > 0 ? T : 1) : kTileM;
-  // (a split launch is a streamed one: only those have a split instance)
-  if (d.prefill || T > kSplitMaxT || !d.stream) return d;
+  // (a split launch is a streamed one: only those have a split instance; the
+  // 8-bit shared expert is never split: at one token on the 288-expert layer
+  // the split the rule would pick measured 2-5% slower, and the split kernel
+  // has no 8-bit path)
+  if (d.prefill || T > kSplitMaxT || !d.stream || (Fs > 0 && L.shared_bits == 8)) return d;
   // Routed items that can be live: with T <= 16 every segment is one tile, so
   // at most min(E, N) tiles (the grid's last items exit on locating
   // themselves), and split blocks index their partial sums among those.

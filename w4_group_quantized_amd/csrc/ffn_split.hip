@@ -208,7 +208,8 @@ __global__ __launch_bounds__(256) void ffn_split_kernel(FfnArgs p) {
     return;
   }
 
-  // shared expert: fp16 weights, 16 weight rows per block, K split over waves
+  // shared expert: fp16 weights (layers with the 8-bit shared expert are
+  // never split), 16 weight rows per block, K split over waves
   const int Ks = kPair ? p.H : p.Fs;
   const int Ns = kPair ? p.Fs : p.H;
   const int Gs = Ks / kGroup;
@@ -226,18 +227,7 @@ __global__ __launch_bounds__(256) void ffn_split_kernel(FfnArgs p) {
   // this block's part of K, split again over its 4 waves
   const int lo = spart * Gs / sparts, hi = (spart + 1) * Gs / sparts;
   const int g0 = lo + wid * (hi - lo) / 4, g1 = lo + (wid + 1) * (hi - lo) / 4;
-  if (p.shared_w8) {     // block-uniform: 8-bit codes, 16-row tile nt
-    const size_t tile = (size_t)nt * 16;
-    const uint8_t *qrow[kMats];
-    const f16 *srow[kMats];
-    qrow[0] = p.wq0 + tile * Ks + kb * 512 + r * 16;
-    srow[0] = p.ws0 + tile * Gs + r;
-    if (kPair) {
-      qrow[kMats - 1] = p.wq1 + tile * Ks + kb * 512 + r * 16;
-      srow[kMats - 1] = p.ws1 + tile * Gs + r;
-    }
-    w8_tiles<kMats, STREAM>(arow, qrow, srow, g0, g1, acc);
-  } else {
+  {
     const f16 *wrow[kMats];
     wrow[0] = p.w0 + (size_t)nrow * Ks;
     if (kPair) wrow[kMats - 1] = p.w1 + (size_t)nrow * Ks;
