@@ -183,9 +183,17 @@ __device__ __forceinline__ void prefill_gemm(f16 *sA, rsrc_t a_rs, rsrc_t b_rs0,
       af[i] = *reinterpret_cast<const f16x8 *>(as + i * 32 * kPK + o.a_rd[w]);
   };
   // Software pipeline over the 4 k16 sub-steps: the region of sub-step w
-  // holds the LDS operand reads and the weight unpack of sub-step w + 1 and
-  // the MFMAs of sub-step w (scheduling fences keep the regions apart, so
-  // the reads and the unpack overlap the matrix-core work).
+  // holds the LDS operand reads and the weight unpack of sub-step w + 1 (for
+  // w = 3: the unpack of the next step's sub-step 0, whose codes are already
+  // in registers) and the MFMAs of sub-step w.  Scheduling fences keep the
+  // regions apart, and inside a region scheduling groups issue the LDS reads
+  // first and then one MFMA after every 4 VALU instructions, so the unpack
+  // runs while the matrix core works (the counters showed half of the VALU
+  // cycles without a concurrent MFMA; this order and the early unpack of the
+  // next step took 1.3% off the prefill FFN).
+  // bf0: the unpacked weights of the next step's first sub-step, made during
+  // this step's last sub-step (its codes are in registers D steps ahead)
+  f16x8 bf0[2];
   auto body = [&](int step, int u) {
     lds_barrier();      // stage step % 2 is complete; stage (step+1) % 2 is free
     const f16 *as = sA + (step & 1) * kPStage;
@@ -193,19 +201,29 @@ __device__ __forceinline__ void prefill_gemm(f16 *sA, rsrc_t a_rs, rsrc_t b_rs0,
     read_a(as, 0, af[0]);
     load_a(min(step + 1, nsteps - 1));
     load_b(min(step + D, nsteps - 1), (u + D) % NS);
-    unpack_b(u, 0, bf[0]);
+    bf[0][0] = bf0[0];
+    bf[0][1] = bf0[1];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       if (w + 1 < 4) {
         read_a(as, w + 1, af[(w + 1) & 1]);
         unpack_b(u, w + 1, bf[(w + 1) & 1]);
+      } else {
+        unpack_b((u + 1) % NS, 0, bf0);
       }
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = mfma_32x32x16(bf[w & 1][j], af[w & 1][i], acc[i][j]);
+      // scheduling groups (mask 0x100: LDS reads, 0x008: MFMA, 0x002: VALU)
+      if (w + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, MI, 0);
+#pragma unroll
+      for (int g = 0; g < 2 * MI; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     if (step + 1 < nsteps) store_a(step + 1);
@@ -214,6 +232,7 @@ __device__ __forceinline__ void prefill_gemm(f16 *sA, rsrc_t a_rs, rsrc_t b_rs0,
   load_a(0);
 #pragma unroll
   for (int u = 0; u < D; ++u) load_b(min(u, nsteps - 1), u);
+  unpack_b(0, 0, bf0);
   store_a(0);
   for (int s0 = 0;; s0 += NS) {
     bool done = false;
