@@ -151,14 +151,14 @@ def test_stack_without_shared_expert():
 
 
 @pytest.mark.parametrize("E,k,T", [(288, 8, 16), (288, 8, 32), (1024, 32, 4), (40, 1, 11),
-                                   (1024, 32, 1), (40, 1, 1), (288, 8, 1)])
+                                   (1024, 32, 1), (40, 1, 1), (288, 8, 1), (16, 16, 1)])
 def test_stack_expert_tiles(E, k, T):
     """Expert tiles sized to give every CU one block: 288 experts at 16
     tokens (18 per block, 16 tiles, two per XCD) and at 32 (36 per block, 8
     tiles, more than one expert per wave), 1024 experts at top-32 (16 per
     block, 64 tiles), and top-1 over 40 experts; at one token (the token's
     own block sorts its choices into the permutation) top-32 of 1024, top-1
-    of 40 and top-8 of 288."""
+    of 40, top-8 of 288 and every expert (top-16 of 16)."""
     cfg = get_config("decode_fine", num_experts=E, hidden=256, ffn=128, top_k=k, shared_ffn=128)
     check_stack(cfg, 3, T, batch=7 + T)
 
