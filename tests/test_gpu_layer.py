@@ -313,3 +313,32 @@ def test_largest_ffn_size():
     torch.cuda.synchronize()
     ref = check_selection(ref, buf, 3, x, wr, b, experts, cfg, None)
     tol_check(out, ref["out"], "F = 262144")
+
+
+@pytest.mark.parametrize("T,gs", [(1, 128), (2, 128), (4, 128), (3, 64), (4, 256)])
+def test_split_ffn_on_a_wide_layer(T, gs):
+    """Batches of up to 4 tokens on a layer of hidden 16384: each gate/up item
+    (64 rows of gate and of up, about 1 MB of codes) and each shared-expert
+    item (1 MB of fp16) is split in K over up to 8 blocks, the down items stay
+    whole.  At one token the token row (32 KB) is staged in LDS; from two
+    tokens on the split blocks read their rows from memory.  Expert weights
+    are drawn as codes."""
+    cfg = get_config("decode_fine", num_experts=4, hidden=16384, ffn=256, top_k=2,
+                     shared_ffn=256, group_size=gs)
+    mats, experts = coded_experts(cfg)
+    wr, b = G.router(cfg)
+    shared = G.shared_expert(cfg)
+    x = G.activations(cfg, tokens=T, batch=T)
+    ref = oracle_layer(x, wr, b, experts, cfg, shared)
+    layer = make_gpu_layer(cfg, mats, wr, b, shared)
+    buf = layer.alloc(T)
+    first = None
+    for call in range(3):          # the tickets reset: later calls repeat the first bitwise
+        out = _np(layer.forward(to_dev(x), buf))
+        torch.cuda.synchronize()
+        if first is None:
+            first = out
+            ref = check_selection(ref, buf, T, x, wr, b, experts, cfg, shared)
+            tol_check(out, ref["out"], f"H = 16384, T = {T}, group {gs}")
+        else:
+            assert out.tobytes() == first.tobytes(), f"call {call}"
