@@ -321,8 +321,9 @@ def test_split_ffn_on_a_wide_layer(T, gs):
     (64 rows of gate and of up, about 1 MB of codes) and each shared-expert
     item (1 MB of fp16) is split in K over up to 8 blocks, the down items stay
     whole.  At one token the token row (32 KB) is staged in LDS; from two
-    tokens on the split blocks read their rows from memory.  Expert weights
-    are drawn as codes."""
+    tokens on the split blocks read their rows from memory.  With the
+    permuted rows materialised (x_perm) the layer gives the same bits.
+    Expert weights are drawn as codes."""
     cfg = get_config("decode_fine", num_experts=4, hidden=16384, ffn=256, top_k=2,
                      shared_ffn=256, group_size=gs)
     mats, experts = coded_experts(cfg)
@@ -342,3 +343,6 @@ def test_split_ffn_on_a_wide_layer(T, gs):
             tol_check(out, ref["out"], f"H = 16384, T = {T}, group {gs}")
         else:
             assert out.tobytes() == first.tobytes(), f"call {call}"
+    out = _np(layer.forward(to_dev(x), buf, gather=True))
+    torch.cuda.synchronize()
+    assert out.tobytes() == first.tobytes(), "rows from x_perm"
