@@ -100,7 +100,8 @@ def parse():
 # valid only for the kernel sources they were taken with.
 FFN_SOURCES = ("w4_group_quantized_amd/csrc/ffn.hip", "w4_group_quantized_amd/csrc/ffn_split.hip",
                "w4_group_quantized_amd/csrc/ffn_decode.h", "w4_group_quantized_amd/csrc/ffn_prefill.hip",
-               "w4_group_quantized_amd/csrc/tiles.h", "w4_group_quantized_amd/csrc/common.h")
+               "w4_group_quantized_amd/csrc/tiles.h", "w4_group_quantized_amd/csrc/common.h",
+               "w4_group_quantized_amd/csrc/split_plan.h")
 FFN_KERNELS = ("ffn_decode_kernel", "ffn_prefill_kernel")
 
 

@@ -6,6 +6,7 @@
 #include "common.h"
 #include "kernels.h"
 #include "tiles.h"
+#include "split_plan.h"
 
 namespace moe {
 
@@ -76,8 +77,6 @@ __device__ bool locate_tile(const int32_t *__restrict__ off, int E, int slot, in
   *mt_out = s_res[1];
   return s_res[0] >= 0;
 }
-
-constexpr int kMaxParts = 8;   // K parts per item at most
 
 // Launch the K-split decode kernel of one phase (1: gate/up, 2: down) with NT
 // 16-row tiles per wave (phase 1: 1 or 2; phase 2: 2 or 4) over `blocks`
