@@ -22,8 +22,8 @@ import oracle as O
 from workloads import get_config
 from workloads import gen as G
 
-from gpu_util import (gpu, require_gpu, to_dev, tol_check, quantized_experts, make_gpu_layer,
-                      on_gpu_selection, shared_w8)
+from gpu_util import (gpu, require_gpu, to_dev, tol_check, quantized_experts, coded_experts,
+                      make_gpu_layer, on_gpu_selection, shared_w8)
 
 pytestmark = gpu
 
@@ -110,15 +110,24 @@ def test_stack_group_size_64_and_8bit_shared_expert():
     check_stack(get_config("decode_fine", **FINE), 3, 16, w8=True, batch=5)
 
 
-def test_stack_mixed_group_sizes_and_shared_formats():
+WIDE = dict(num_experts=4, hidden=8192, ffn=256, top_k=2, shared_ffn=256)
+
+
+@pytest.mark.parametrize("T,dims", [(10, "fine"), (1, "wide"), (3, "wide")])
+def test_stack_mixed_group_sizes_and_shared_formats(T, dims):
     """Layers of one stack may differ in group size and in the shared
-    expert's format (only the shapes must agree)."""
+    expert's format (only the shapes must agree).  On the hidden-8192 layers
+    at 1 and 3 tokens the layers with the fp16 shared expert split their
+    gate/up items in K over blocks and the one with the 8-bit shared expert
+    does not, all in one workspace, between fused combine + router launches
+    (expert weights drawn as codes)."""
     from w4_group_quantized_amd import W4MoEStack
-    T = 10
-    cfgs = [get_config("decode_fine", group_size=gs, **FINE) for gs in (128, 64, 256)]
+    wide = dims == "wide"
+    cfgs = [get_config("decode_fine", group_size=gs, **(WIDE if wide else FINE))
+            for gs in (128, 64, 256)]
     layers, refs = [], []
     for li, cfg in enumerate(cfgs):
-        mats, experts = quantized_experts(cfg, layer=li)
+        mats, experts = (coded_experts if wide else quantized_experts)(cfg, layer=li)
         wr, b = G.router(cfg, li)
         shared = G.shared_expert(cfg, li)
         if li == 1:
