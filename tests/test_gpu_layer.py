@@ -275,26 +275,28 @@ def test_layer_with_8bit_shared_expert(T):
     tol_check(out, ref["out"], "layer out")
 
 
-def test_largest_hidden_size():
+@pytest.mark.parametrize("T", [5, 2])
+def test_largest_hidden_size(T):
     """hidden = 65536, the largest the ABI accepts: the one-launch router with
     its maximum of 16 K parts, gate/up rows of 128 KB streamed from memory
     (too large to stage in LDS), 4096 down-projection row tiles, and the
     combine over rows wider than one block (without the norm, and with it,
-    the two-pass kernel for rows over 8192 columns).  Expert weights are
-    drawn as codes (the quantizer is pinned elsewhere)."""
+    the two-pass kernel for rows over 8192 columns); at 2 tokens the gate/up
+    and shared items split their 512 quantization groups over 8 blocks.
+    Expert weights are drawn as codes (the quantizer is pinned elsewhere)."""
     cfg = get_config("decode_fine", num_experts=3, hidden=65536, ffn=128, top_k=2,
                      shared_ffn=128)
     mats, experts = coded_experts(cfg)
     wr, b = G.router(cfg)
     shared = G.shared_expert(cfg)
-    x = G.activations(cfg, tokens=5, batch=1)
+    x = G.activations(cfg, tokens=T, batch=1)
     ref = O.moe_layer(x, wr, b, experts, cfg.top_k, shared=shared)
     layer = make_gpu_layer(cfg, mats, wr, b, shared)
-    buf = layer.alloc(5)
+    buf = layer.alloc(T)
     for rmsnorm in (False, True):
         out = _np(layer.forward(to_dev(x), buf, rmsnorm=rmsnorm, eps=cfg.rms_eps))
         torch.cuda.synchronize()
-        r = check_selection(ref, buf, 5, x, wr, b, experts, cfg, shared)
+        r = check_selection(ref, buf, T, x, wr, b, experts, cfg, shared)
         want = O.rmsnorm(r["out"], cfg.rms_eps) if rmsnorm else r["out"]
         tol_check(out, want, f"H = 65536, norm {rmsnorm}")
 
